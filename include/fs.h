@@ -1,0 +1,254 @@
+/*
+ * fs.h — C ABI of the fact-store KV-injection library (AMD Instinct MI355X, gfx950).
+ *
+ * The library implements the serving-time hot path of KV injection as the
+ * InferScale pages describe it ("InferScale: GPU-Native KV Injection for
+ * Personalized LLM Serving", Li & Pandey, arXiv 2607.27090):
+ *
+ *   precompute each fact's KV, keep it on the GPU next to a semantic
+ *   embedding, retrieve the relevant facts at serving time and inject their
+ *   KV straight into the paged KV cache
+ *       (astralor.com feed item, "Full text" = the paper's abstract);
+ *   keys are stored before RoPE; at serving time the retrieved facts form one
+ *   contiguous segment and every stored key is rotated to its new position
+ *   (Chunked RoPE); the composed K/V is scatter-copied into the paged cache
+ *       (gist.science technical summary, "Phase En-ligne" / "Fase Online");
+ *   the store may live in host DRAM when the GPU is too small
+ *       (gist.science summary, "Résultats" / "Resultados", scalability item).
+ *
+ * Conventions for every entry point
+ *   - Plain pointers and sizes only.  "device" pointers are HIP device
+ *     memory of the current device; "host" pointers are ordinary host memory
+ *     read during the call and not kept.
+ *   - The caller owns every buffer it passes (embeddings, K/V arenas, caches,
+ *     ids, block tables, queries) and keeps the store's buffers alive until
+ *     fs_destroy_store.  The library owns only what it allocates itself:
+ *     metadata copies, the RoPE frequency table, an error word and scratch.
+ *   - Stream arguments are hipStream_t values passed as void* (NULL = the
+ *     legacy default stream).  Every call except create/destroy/poll only
+ *     enqueues work and returns; results are ready when the stream reaches
+ *     that point.
+ *   - A store must not be used from two streams at the same time (shared
+ *     scratch); this is not detected.
+ *   - Errors: a call returns a status.  Host-checkable errors return before
+ *     anything is enqueued and nothing is written.  Conditions only the GPU
+ *     can see set bits in the store's device error word (fs_poll_errors) and
+ *     the offending request writes nothing.  Nothing is thrown across the
+ *     ABI.  fs_last_error_message() gives the detail of the last failure on
+ *     the calling thread.
+ *
+ * Data layout (bf16 = 16-bit brain float; all bf16 buffers 16-byte aligned)
+ *   fact f has fact_len[f] tokens; facts are stored back to back in fact
+ *   order, so fact f occupies arena rows [sum_{g<f} fact_len[g], ... + fact_len[f]).
+ *   user u owns facts [user_fact_begin[u], user_fact_begin[u+1]).
+ *   K/V arena of one layer:   bf16 [num_tokens][num_kv_heads][head_dim]
+ *                             (keys un-rotated, values raw)
+ *   embeddings:               fp32 [num_facts][embed_dim], row-major
+ *   paged cache of one layer: bf16 [num_blocks][block_size][num_kv_heads][head_dim]
+ *   block table:              int32 [batch][max_blocks]; absolute position p of
+ *                             request b lives in block block_table[b][p / block_size],
+ *                             slot p % block_size.
+ */
+#ifndef FS_H_
+#define FS_H_
+
+#include <stdint.h>
+
+/* the library is built with hidden visibility; only these entry points are exported */
+#if defined(__GNUC__) || defined(__clang__)
+#define FS_API __attribute__((visibility("default")))
+#else
+#define FS_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fs_store fs_store;      /* opaque, library-owned */
+typedef int32_t fs_status;
+
+/* ---- status codes ---------------------------------------------------- */
+#define FS_OK              0
+#define FS_E_ARG           1   /* null/misaligned pointer, bad shape or size   */
+#define FS_E_RANGE         2   /* layer, batch or k outside the store's limits */
+#define FS_E_BLOCKTABLE    3   /* block table arguments unusable (host check)  */
+#define FS_E_NOMEM         4   /* device allocation failed                     */
+#define FS_E_HIP           5   /* a HIP runtime call failed                    */
+#define FS_E_DEVICE        6   /* fs_poll_errors: device error bits were set   */
+#define FS_E_UNSUPPORTED   7   /* valid request this build does not implement  */
+
+/* ---- device error bits (fs_poll_errors) ------------------------------ */
+#define FS_ERR_USER        0x01u  /* user index outside [0, num_users)            */
+#define FS_ERR_FACT_ID     0x02u  /* id not a fact of the request's user, or a -1
+                                     pad followed by a real id                     */
+#define FS_ERR_START_POS   0x04u  /* start_pos < 0, or start_pos + L > INT32_MAX   */
+#define FS_ERR_BLOCK_SHORT 0x08u  /* block table has fewer than
+                                     ceil((start_pos + L) / block_size) entries   */
+#define FS_ERR_BLOCK_ID    0x10u  /* a used block id outside [0, num_blocks)       */
+#define FS_ERR_STAGING     0x20u  /* pinned store: inject ids differ from the ids
+                                     the staging slot was fetched for              */
+
+#define FS_ALL_LAYERS      (-1)
+#define FS_MAX_LAYERS      128
+#define FS_MAX_K           1024
+
+#define FS_KV_DEVICE       0      /* K/V arenas in device memory              */
+#define FS_KV_PINNED_HOST  1      /* K/V arenas in page-locked host memory    */
+
+typedef struct fs_store_desc {
+    int32_t num_layers;      /* 1 .. FS_MAX_LAYERS                               */
+    int32_t num_kv_heads;    /* >= 1                                             */
+    int32_t head_dim;        /* 64, 128 or 256 (rotate-half pairs i, i+head_dim/2) */
+    int32_t embed_dim;       /* multiple of 4, 4 .. 4096                         */
+    double  rope_theta;      /* RoPE base, > 1 (w_i = theta^(-2i/head_dim))      */
+    int32_t block_size;      /* paged-cache block size, power of two, 1 .. 1024  */
+    int32_t kv_location;     /* FS_KV_DEVICE or FS_KV_PINNED_HOST                */
+    int32_t num_users;       /* >= 1                                             */
+    int32_t max_batch;       /* largest batch any call will pass, >= 1           */
+    int32_t max_k;           /* largest k any call will pass, 1 .. FS_MAX_K      */
+    int32_t staging_layers;  /* pinned stores: layers the device staging ring
+                                holds (1 .. num_layers); ignored otherwise       */
+    int64_t num_facts;       /* >= 1                                             */
+    int64_t num_tokens;      /* == sum of fact_len                               */
+} fs_store_desc;
+
+/*
+ * fs_create_store — register a fact store (InferScale abstract: each fact's KV
+ * is precomputed and stored alongside a semantic embedding on the GPU;
+ * "Stockage Pré-RoPE": keys intercepted before RoPE plus raw values).
+ *
+ *   desc             host; shapes and limits (see fs_store_desc)
+ *   user_fact_begin  host int64 [num_users + 1]; 0, non-decreasing, ends at num_facts
+ *   fact_len         host int32 [num_facts]; every length >= 1
+ *   emb              device fp32 [num_facts][embed_dim], 16-byte aligned;
+ *                    rows are expected L2-normalised (not checked)
+ *   k_pre, v         host arrays of num_layers pointers to the per-layer K and V
+ *                    arenas, bf16 [num_tokens][num_kv_heads][head_dim], 16-byte
+ *                    aligned; device memory for FS_KV_DEVICE, page-locked host
+ *                    memory (hipHostMalloc / pinned) for FS_KV_PINNED_HOST
+ *   stream           stream used for the metadata uploads (synchronised before return)
+ *   out              receives the handle; untouched on failure
+ *
+ * The store keeps the emb/k_pre/v pointers (not the data).  Allocates: fact
+ * offsets and lengths, user offsets, the fp64 frequency table, the error word,
+ * score scratch [max_batch][largest user], and for pinned stores the staging
+ * ring [staging_layers][max_batch][max_k * longest fact][heads][head_dim] x2.
+ * Errors: FS_E_ARG (bad desc/pointer/alignment/metadata), FS_E_UNSUPPORTED
+ * (head_dim or embed_dim not built), FS_E_NOMEM, FS_E_HIP.
+ */
+FS_API fs_status fs_create_store(const fs_store_desc* desc,
+                          const int64_t* user_fact_begin,
+                          const int32_t* fact_len,
+                          const float* emb,
+                          const void* const* k_pre,
+                          const void* const* v,
+                          void* stream,
+                          fs_store** out);
+
+/* fs_destroy_store — free everything the library allocated for the store
+ * (waits for the device).  NULL is accepted and ignored. */
+FS_API fs_status fs_destroy_store(fs_store* store);
+
+/*
+ * fs_retrieve_topk — GPU-resident semantic retrieval with budget k
+ * (gist.science summary, "Problématique": k retrieved facts;
+ * "Contributions Clés": retrieval index and KV store both on the GPU).
+ *
+ * For each request b: s_i = <emb[i], query[b]> over the facts i of user[b],
+ * each fp32*fp32 product exact and summed in fp64; selects the
+ * k' = min(k, N_user) best facts ordered by (score descending, fact id
+ * ascending).
+ *
+ *   batch       1 .. max_batch
+ *   user        device int32 [batch]
+ *   query       device fp32 [batch][embed_dim], 16-byte aligned
+ *   k           0 .. max_k
+ *   ids         device int32 [batch][k]: global fact ids in rank order, -1 past k'
+ *   scores      device fp64 [batch][k] or NULL: the scores, -inf past k'
+ *   num_tokens  device int32 [batch] or NULL: L_b = sum of the selected facts' lengths
+ *
+ * A bad user index sets FS_ERR_USER; that request gets ids -1, scores -inf
+ * and num_tokens 0.  Errors: FS_E_ARG, FS_E_RANGE, FS_E_HIP.
+ */
+FS_API fs_status fs_retrieve_topk(const fs_store* store, int32_t batch,
+                           const int32_t* user, const float* query, int32_t k,
+                           int32_t* ids, double* scores, int32_t* num_tokens,
+                           void* stream);
+
+/*
+ * fs_inject — Chunked RoPE + scatter-copy into the paged KV cache
+ * (gist.science summary, "Phase En-ligne": "Rotation Dynamique" and
+ * "Injection"; Theorem 6 as described there: the re-rotation is exact).
+ *
+ * For each request b the facts ids[b][0..] (up to the first -1) are laid end
+ * to end from position start_pos[b]: token t of the segment has position
+ * p = start_pos[b] + t.  For every written layer l and head h:
+ *   K cache (block_table[b][p / bs], slot p % bs, h) =
+ *       bf16_rne( R(p) * k_pre[l][row(t)][h] )     rotate-half RoPE,
+ *       R(p) rotating (x_i, x_{i+D/2}) by angle p * theta^(-2i/D), evaluated in
+ *       fp64 and rounded once to bf16 (round to nearest, ties to even)
+ *   V cache (same address) = v[l][row(t)][h]            (bytes, unchanged)
+ * Every other cache byte is left untouched.
+ *
+ *   layer        0 .. num_layers-1, or FS_ALL_LAYERS
+ *   batch        1 .. max_batch
+ *   user         device int32 [batch]; ids must belong to the request's user
+ *   ids          device int32 [batch][k] (e.g. fs_retrieve_topk's output)
+ *   k            0 .. max_k (0: nothing is enqueued)
+ *   block_table  device int32 [batch][max_blocks]
+ *   start_pos    device int32 [batch]
+ *   k_cache, v_cache  host arrays of num_layers device pointers, each
+ *                bf16 [num_blocks][block_size][num_kv_heads][head_dim],
+ *                16-byte aligned; entries of layers not written may be NULL
+ *   num_blocks   physical blocks per layer cache, >= 1
+ * Pinned stores read the staging slot layer % staging_layers filled by
+ * fs_fetch_async with the same ids (else FS_ERR_STAGING).
+ * Block ids used by one call must be distinct across its requests (caller's
+ * contract, not checked).  Device-checked: FS_ERR_USER, FS_ERR_FACT_ID,
+ * FS_ERR_START_POS, FS_ERR_BLOCK_SHORT, FS_ERR_BLOCK_ID, FS_ERR_STAGING — the
+ * request then writes nothing.  Errors: FS_E_ARG, FS_E_RANGE, FS_E_BLOCKTABLE,
+ * FS_E_HIP.
+ */
+FS_API fs_status fs_inject(const fs_store* store, int32_t layer, int32_t batch,
+                    const int32_t* user, const int32_t* ids, int32_t k,
+                    const int32_t* block_table, int32_t max_blocks,
+                    const int32_t* start_pos,
+                    void* const* k_cache, void* const* v_cache,
+                    int32_t num_blocks, void* stream);
+
+/*
+ * fs_fetch_async — host-DRAM offload (gist.science summary, "Résultats":
+ * the KV store can be offloaded to host DRAM at a small TTFT cost).
+ * Pinned stores only.  Gathers the selected facts' K and V rows of layers
+ * [layer_begin, layer_end) from the page-locked host arenas, over the host
+ * link, into the device staging ring (slot = layer % staging_layers), in
+ * composed segment order; fs_inject then reads the slot.  Enqueued on
+ * `stream` (typically a side stream): the caller orders the later fs_inject
+ * after it (e.g. with an event).  layer_end - layer_begin <= staging_layers.
+ * Device-checked: FS_ERR_USER, FS_ERR_FACT_ID (that request stages nothing).
+ * Errors: FS_E_ARG, FS_E_RANGE, FS_E_UNSUPPORTED (device store), FS_E_HIP.
+ */
+FS_API fs_status fs_fetch_async(const fs_store* store, int32_t batch,
+                         const int32_t* user, const int32_t* ids, int32_t k,
+                         int32_t layer_begin, int32_t layer_end, void* stream);
+
+/*
+ * fs_poll_errors — synchronise `stream`, return the device error bits
+ * accumulated since the last poll in *flags, and clear them.  Returns
+ * FS_E_DEVICE when any bit was set, FS_OK otherwise (FS_E_ARG, FS_E_HIP).
+ */
+FS_API fs_status fs_poll_errors(const fs_store* store, void* stream, uint32_t* flags);
+
+/* fs_strerror — static text for a status code. */
+FS_API const char* fs_strerror(fs_status status);
+
+/* fs_last_error_message — detail of the last failing call on this thread
+ * (static per thread; empty string if none). */
+FS_API const char* fs_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FS_H_ */

@@ -1,0 +1,94 @@
+// Internal declarations shared by the host runtime and the kernel files of the
+// fact-store KV-injection library.  Not part of the ABI (include/fs.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "fs.h"
+
+namespace fsi {
+
+// Largest segment-token count a block's prologue handles for one request in
+// LDS: offsets [k+1] int32 + first rows [k] int64.
+constexpr int kMaxK = FS_MAX_K;
+
+// Top-k keeps a request's keys in LDS when the user has at most this many
+// facts (48 KiB of uint64 keys); larger users are re-read from global memory.
+constexpr int kTopkLdsKeys = 6144;
+
+}  // namespace fsi
+
+struct fs_store {
+    fs_store_desc desc;
+    int device = 0;
+    int32_t max_fact_len = 0;     // longest fact, tokens
+    int32_t max_user_facts = 0;   // largest user, facts
+    int32_t log2_block = 0;
+
+    // library-owned device memory
+    int64_t* d_fact_begin = nullptr;   // [F+1] first arena row of each fact
+    int32_t* d_fact_len = nullptr;     // [F]
+    int64_t* d_user_begin = nullptr;   // [U+1]
+    double* d_inv_freq = nullptr;      // [head_dim/2] theta^(-2i/D)
+    uint32_t* d_err = nullptr;         // device error word
+    double* d_scores = nullptr;        // [max_batch][max_user_facts] score scratch
+    const void** d_src_k = nullptr;    // [L] device-visible arena pointers
+    const void** d_src_v = nullptr;
+
+    // pinned stores: staging ring
+    int32_t stage_tokens = 0;          // max_k * max_fact_len
+    void* d_stage_k = nullptr;         // [staging_layers][max_batch][stage_tokens][H][D] bf16
+    void* d_stage_v = nullptr;
+    int32_t* d_stage_ids = nullptr;    // [staging_layers][max_batch][max_k]
+    int32_t* d_stage_meta = nullptr;   // [staging_layers][4]: k, batch, layer of the last fetch
+
+    // caller-owned, referenced
+    const float* emb = nullptr;
+    std::vector<const void*> src_k, src_v;   // device-visible addresses
+};
+
+// ---- kernel launchers (one translation unit each) -------------------------
+
+struct RetrieveLaunch {
+    const fs_store* st;
+    int32_t batch;
+    const int32_t* user;
+    const float* query;
+    int32_t k;
+    int32_t* ids;
+    double* scores;
+    int32_t* num_tokens;
+    hipStream_t stream;
+};
+hipError_t fsi_launch_retrieve(const RetrieveLaunch& a);
+
+struct InjectLaunch {
+    const fs_store* st;
+    int32_t layer_begin, layer_end;   // [begin, end)
+    int32_t batch;
+    const int32_t* user;
+    const int32_t* ids;
+    int32_t k;
+    const int32_t* block_table;
+    int32_t max_blocks;
+    const int32_t* start_pos;
+    void* const* k_cache;             // host array [num_layers]
+    void* const* v_cache;
+    int32_t num_blocks;
+    hipStream_t stream;
+};
+hipError_t fsi_launch_inject(const InjectLaunch& a);
+
+struct FetchLaunch {
+    const fs_store* st;
+    int32_t layer_begin, layer_end;
+    int32_t batch;
+    const int32_t* user;
+    const int32_t* ids;
+    int32_t k;
+    hipStream_t stream;
+};
+hipError_t fsi_launch_fetch(const FetchLaunch& a);

@@ -1,0 +1,365 @@
+// Host runtime of the fact-store KV-injection library: argument validation,
+// store creation/destruction, launch dispatch and error reporting.
+//
+// Every host-checkable condition is tested before the first HIP call of an
+// entry point, so a rejected call enqueues nothing and writes nothing.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "fs_internal.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+fs_status fail(fs_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+fs_status hip_fail(hipError_t e, const char* what) {
+    return fail(FS_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int64_t x) {
+    int r = 0;
+    while ((int64_t(1) << r) < x) ++r;
+    return r;
+}
+
+void free_store(fs_store* s) {
+    if (!s) return;
+    void* bufs[] = {s->d_fact_begin, s->d_fact_len, s->d_user_begin, s->d_inv_freq, s->d_err,
+                    s->d_scores, (void*)s->d_src_k, (void*)s->d_src_v, s->d_stage_k,
+                    s->d_stage_v, s->d_stage_ids, s->d_stage_meta};
+    for (void* p : bufs)
+        if (p) (void)hipFree(p);
+    delete s;
+}
+
+template <class T>
+hipError_t dev_alloc(T** p, size_t count) {
+    return hipMalloc(reinterpret_cast<void**>(p), count * sizeof(T) > 0 ? count * sizeof(T) : 1);
+}
+
+fs_status check_desc(const fs_store_desc* d) {
+    if (d->num_layers < 1 || d->num_layers > FS_MAX_LAYERS)
+        return fail(FS_E_ARG, "num_layers %d outside [1, %d]", d->num_layers, FS_MAX_LAYERS);
+    if (d->num_kv_heads < 1) return fail(FS_E_ARG, "num_kv_heads must be >= 1");
+    if (d->head_dim < 16 || d->head_dim % 16 != 0)
+        return fail(FS_E_ARG, "head_dim %d must be a positive multiple of 16", d->head_dim);
+    if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256)
+        return fail(FS_E_UNSUPPORTED, "head_dim %d: built for 64, 128, 256", d->head_dim);
+    if (d->embed_dim < 4 || d->embed_dim % 4 != 0)
+        return fail(FS_E_ARG, "embed_dim %d must be a positive multiple of 4", d->embed_dim);
+    if (d->embed_dim > 4096) return fail(FS_E_UNSUPPORTED, "embed_dim %d > 4096", d->embed_dim);
+    if (!(d->rope_theta > 1.0) || !std::isfinite(d->rope_theta))
+        return fail(FS_E_ARG, "rope_theta must be finite and > 1");
+    if (!pow2(d->block_size) || d->block_size > 1024)
+        return fail(FS_E_ARG, "block_size %d must be a power of two <= 1024", d->block_size);
+    if (d->kv_location != FS_KV_DEVICE && d->kv_location != FS_KV_PINNED_HOST)
+        return fail(FS_E_ARG, "kv_location %d unknown", d->kv_location);
+    if (d->num_users < 1) return fail(FS_E_ARG, "num_users must be >= 1");
+    if (d->max_batch < 1 || d->max_batch > 65535)
+        return fail(FS_E_ARG, "max_batch %d outside [1, 65535]", d->max_batch);
+    if (d->max_k < 1 || d->max_k > FS_MAX_K)
+        return fail(FS_E_ARG, "max_k %d outside [1, %d]", d->max_k, FS_MAX_K);
+    if (d->kv_location == FS_KV_PINNED_HOST &&
+        (d->staging_layers < 1 || d->staging_layers > d->num_layers))
+        return fail(FS_E_ARG, "staging_layers %d outside [1, num_layers]", d->staging_layers);
+    if (d->num_facts < 1) return fail(FS_E_ARG, "num_facts must be >= 1");
+    if (d->num_tokens < 1) return fail(FS_E_ARG, "num_tokens must be >= 1");
+    return FS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fs_last_error_message(void) { return g_msg; }
+
+const char* fs_strerror(fs_status s) {
+    switch (s) {
+        case FS_OK: return "ok";
+        case FS_E_ARG: return "invalid argument";
+        case FS_E_RANGE: return "argument out of the store's range";
+        case FS_E_BLOCKTABLE: return "unusable block table arguments";
+        case FS_E_NOMEM: return "device allocation failed";
+        case FS_E_HIP: return "HIP runtime error";
+        case FS_E_DEVICE: return "device-side error bits set";
+        case FS_E_UNSUPPORTED: return "unsupported configuration";
+        default: return "unknown status";
+    }
+}
+
+fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_begin,
+                          const int32_t* fact_len, const float* emb, const void* const* k_pre,
+                          const void* const* v, void* stream, fs_store** out) {
+    g_msg[0] = 0;
+    if (!desc || !user_fact_begin || !fact_len || !emb || !k_pre || !v || !out)
+        return fail(FS_E_ARG, "null pointer argument");
+    if (fs_status st = check_desc(desc)) return st;
+    const fs_store_desc& d = *desc;
+    if (!aligned(emb, 16)) return fail(FS_E_ARG, "emb not 16-byte aligned");
+    for (int l = 0; l < d.num_layers; ++l) {
+        if (!k_pre[l] || !v[l]) return fail(FS_E_ARG, "layer %d arena pointer is null", l);
+        if (!aligned(k_pre[l], 16) || !aligned(v[l], 16))
+            return fail(FS_E_ARG, "layer %d arena not 16-byte aligned", l);
+    }
+    if (user_fact_begin[0] != 0) return fail(FS_E_ARG, "user_fact_begin[0] must be 0");
+    int64_t max_user = 0;
+    for (int u = 0; u < d.num_users; ++u) {
+        int64_t n = user_fact_begin[u + 1] - user_fact_begin[u];
+        if (n < 0) return fail(FS_E_ARG, "user_fact_begin decreases at user %d", u);
+        if (n > max_user) max_user = n;
+    }
+    if (user_fact_begin[d.num_users] != d.num_facts)
+        return fail(FS_E_ARG, "user_fact_begin[num_users] != num_facts");
+    if (max_user > INT32_MAX) return fail(FS_E_UNSUPPORTED, "a user has more than 2^31-1 facts");
+    int64_t total = 0;
+    int32_t max_len = 0;
+    for (int64_t f = 0; f < d.num_facts; ++f) {
+        if (fact_len[f] < 1) return fail(FS_E_ARG, "fact_len[%lld] < 1", (long long)f);
+        total += fact_len[f];
+        if (fact_len[f] > max_len) max_len = fact_len[f];
+    }
+    if (total != d.num_tokens) return fail(FS_E_ARG, "sum(fact_len) != num_tokens");
+    if (int64_t(max_len) * d.max_k > INT32_MAX)
+        return fail(FS_E_UNSUPPORTED, "max_k * longest fact exceeds 2^31-1 tokens");
+
+    // ---- host checks done; from here on HIP calls ---------------------------
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    fs_store* st = new (std::nothrow) fs_store();
+    if (!st) return fail(FS_E_NOMEM, "host allocation failed");
+    st->desc = d;
+    st->max_fact_len = max_len;
+    st->max_user_facts = static_cast<int32_t>(max_user);
+    st->log2_block = ilog2(d.block_size);
+    st->emb = emb;
+    hipError_t e = hipGetDevice(&st->device);
+    if (e != hipSuccess) { free_store(st); return hip_fail(e, "hipGetDevice"); }
+
+    // pointer kinds: a device store must hold device memory, a pinned store
+    // page-locked host memory, and every kernel gets a device-visible address
+    auto kind_ok = [&](const void* p, bool want_host, const void** dev, const char* what,
+                       int l) -> fs_status {
+        hipPointerAttribute_t at;
+        hipError_t pe = hipPointerGetAttributes(&at, p);
+        if (pe != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(FS_E_ARG, "%s (layer %d): not HIP-registered memory", what, l);
+        }
+        if (want_host) {
+            if (at.type != hipMemoryTypeHost)
+                return fail(FS_E_ARG, "%s (layer %d): not page-locked host memory", what, l);
+            void* dp = nullptr;
+            hipError_t ge = hipHostGetDevicePointer(&dp, const_cast<void*>(p), 0);
+            if (ge != hipSuccess || !dp)
+                return fail(FS_E_ARG, "%s (layer %d): no device mapping", what, l);
+            *dev = dp;
+        } else {
+            if (at.type != hipMemoryTypeDevice)
+                return fail(FS_E_ARG, "%s (layer %d): not device memory", what, l);
+            *dev = p;
+        }
+        return FS_OK;
+    };
+    const bool pinned = d.kv_location == FS_KV_PINNED_HOST;
+    {
+        const void* dummy;
+        if (fs_status ks = kind_ok(emb, false, &dummy, "emb", -1)) { free_store(st); return ks; }
+    }
+    st->src_k.resize(d.num_layers);
+    st->src_v.resize(d.num_layers);
+    for (int l = 0; l < d.num_layers; ++l) {
+        if (fs_status ks = kind_ok(k_pre[l], pinned, &st->src_k[l], "k_pre", l)) { free_store(st); return ks; }
+        if (fs_status ks = kind_ok(v[l], pinned, &st->src_v[l], "v", l)) { free_store(st); return ks; }
+    }
+
+    std::vector<int64_t> fb(d.num_facts + 1, 0);
+    for (int64_t f = 0; f < d.num_facts; ++f) fb[f + 1] = fb[f] + fact_len[f];
+    std::vector<double> inv(d.head_dim / 2);
+    for (int i = 0; i < d.head_dim / 2; ++i)
+        inv[i] = std::pow(d.rope_theta, -2.0 * double(i) / double(d.head_dim));
+
+    const int H = d.num_kv_heads, D = d.head_dim;
+    struct { void** p; size_t bytes; const char* what; } allocs[] = {
+        {(void**)&st->d_fact_begin, sizeof(int64_t) * (d.num_facts + 1), "fact offsets"},
+        {(void**)&st->d_fact_len, sizeof(int32_t) * d.num_facts, "fact lengths"},
+        {(void**)&st->d_user_begin, sizeof(int64_t) * (d.num_users + 1), "user offsets"},
+        {(void**)&st->d_inv_freq, sizeof(double) * (D / 2), "frequency table"},
+        {(void**)&st->d_err, sizeof(uint32_t), "error word"},
+        {(void**)&st->d_scores, sizeof(double) * size_t(d.max_batch) * size_t(max_user > 0 ? max_user : 1), "score scratch"},
+        {(void**)&st->d_src_k, sizeof(void*) * d.num_layers, "arena table"},
+        {(void**)&st->d_src_v, sizeof(void*) * d.num_layers, "arena table"},
+    };
+    for (auto& a : allocs) {
+        e = hipMalloc(a.p, a.bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            free_store(st);
+            return fail(FS_E_NOMEM, "hipMalloc(%s, %zu bytes): %s", a.what, a.bytes, hipGetErrorString(e));
+        }
+    }
+    if (pinned) {
+        st->stage_tokens = max_len * d.max_k;
+        size_t rows = size_t(d.staging_layers) * d.max_batch * size_t(st->stage_tokens);
+        size_t bytes = rows * H * D * 2;
+        struct { void** p; size_t bytes; } sa[] = {
+            {&st->d_stage_k, bytes}, {&st->d_stage_v, bytes},
+            {(void**)&st->d_stage_ids, sizeof(int32_t) * size_t(d.staging_layers) * d.max_batch * d.max_k},
+            {(void**)&st->d_stage_meta, sizeof(int32_t) * 4 * size_t(d.staging_layers)}};
+        for (auto& a : sa) {
+            e = hipMalloc(a.p, a.bytes);
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                free_store(st);
+                return fail(FS_E_NOMEM, "hipMalloc(staging, %zu bytes): %s", a.bytes, hipGetErrorString(e));
+            }
+        }
+    }
+
+    std::vector<int32_t> meta_init(4 * size_t(pinned ? d.staging_layers : 0), -1);
+    uint32_t zero = 0;
+    struct { void* dst; const void* src; size_t bytes; } cps[] = {
+        {st->d_fact_begin, fb.data(), sizeof(int64_t) * fb.size()},
+        {st->d_fact_len, fact_len, sizeof(int32_t) * d.num_facts},
+        {st->d_user_begin, user_fact_begin, sizeof(int64_t) * (d.num_users + 1)},
+        {st->d_inv_freq, inv.data(), sizeof(double) * inv.size()},
+        {st->d_err, &zero, sizeof(uint32_t)},
+        {(void*)st->d_src_k, st->src_k.data(), sizeof(void*) * d.num_layers},
+        {(void*)st->d_src_v, st->src_v.data(), sizeof(void*) * d.num_layers},
+        {st->d_stage_meta, meta_init.data(), sizeof(int32_t) * meta_init.size()},
+    };
+    for (auto& c : cps) {
+        if (!c.bytes) continue;
+        e = hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) { free_store(st); return hip_fail(e, "hipMemcpyAsync(metadata)"); }
+    }
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) { free_store(st); return hip_fail(e, "hipStreamSynchronize"); }
+    *out = st;
+    return FS_OK;
+}
+
+fs_status fs_destroy_store(fs_store* store) {
+    g_msg[0] = 0;
+    if (!store) return FS_OK;
+    hipError_t e = hipDeviceSynchronize();
+    free_store(store);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+    return FS_OK;
+}
+
+fs_status fs_retrieve_topk(const fs_store* store, int32_t batch, const int32_t* user,
+                           const float* query, int32_t k, int32_t* ids, double* scores,
+                           int32_t* num_tokens, void* stream) {
+    g_msg[0] = 0;
+    if (!store) return fail(FS_E_ARG, "null store");
+    const fs_store_desc& d = store->desc;
+    if (batch < 1 || batch > d.max_batch)
+        return fail(FS_E_RANGE, "batch %d outside [1, %d]", batch, d.max_batch);
+    if (k < 0 || k > d.max_k) return fail(FS_E_RANGE, "k %d outside [0, %d]", k, d.max_k);
+    if (!user || !query) return fail(FS_E_ARG, "null user or query");
+    if (!aligned(query, 16)) return fail(FS_E_ARG, "query not 16-byte aligned");
+    if (!aligned(user, 4)) return fail(FS_E_ARG, "user not 4-byte aligned");
+    if (k > 0 && !ids) return fail(FS_E_ARG, "null ids");
+    if (ids && !aligned(ids, 4)) return fail(FS_E_ARG, "ids not 4-byte aligned");
+    if (scores && !aligned(scores, 8)) return fail(FS_E_ARG, "scores not 8-byte aligned");
+    if (num_tokens && !aligned(num_tokens, 4)) return fail(FS_E_ARG, "num_tokens not 4-byte aligned");
+    if (k == 0 && !num_tokens) return FS_OK;
+    RetrieveLaunch a{store, batch, user, query, k, ids, scores, num_tokens,
+                     reinterpret_cast<hipStream_t>(stream)};
+    hipError_t e = fsi_launch_retrieve(a);
+    if (e != hipSuccess) return hip_fail(e, "retrieve launch");
+    return FS_OK;
+}
+
+fs_status fs_inject(const fs_store* store, int32_t layer, int32_t batch, const int32_t* user,
+                    const int32_t* ids, int32_t k, const int32_t* block_table, int32_t max_blocks,
+                    const int32_t* start_pos, void* const* k_cache, void* const* v_cache,
+                    int32_t num_blocks, void* stream) {
+    g_msg[0] = 0;
+    if (!store) return fail(FS_E_ARG, "null store");
+    const fs_store_desc& d = store->desc;
+    if (layer != FS_ALL_LAYERS && (layer < 0 || layer >= d.num_layers))
+        return fail(FS_E_RANGE, "layer %d outside [0, %d)", layer, d.num_layers);
+    if (batch < 1 || batch > d.max_batch)
+        return fail(FS_E_RANGE, "batch %d outside [1, %d]", batch, d.max_batch);
+    if (k < 0 || k > d.max_k) return fail(FS_E_RANGE, "k %d outside [0, %d]", k, d.max_k);
+    if (!user || !ids || !block_table || !start_pos || !k_cache || !v_cache)
+        return fail(FS_E_ARG, "null pointer argument");
+    if (!aligned(user, 4) || !aligned(ids, 4) || !aligned(block_table, 4) || !aligned(start_pos, 4))
+        return fail(FS_E_ARG, "int32 argument not 4-byte aligned");
+    if (max_blocks < 1) return fail(FS_E_BLOCKTABLE, "max_blocks %d < 1", max_blocks);
+    if (num_blocks < 1) return fail(FS_E_BLOCKTABLE, "num_blocks %d < 1", num_blocks);
+    int lb = layer == FS_ALL_LAYERS ? 0 : layer;
+    int le = layer == FS_ALL_LAYERS ? d.num_layers : layer + 1;
+    for (int l = lb; l < le; ++l) {
+        if (!k_cache[l] || !v_cache[l]) return fail(FS_E_ARG, "layer %d cache pointer is null", l);
+        if (!aligned(k_cache[l], 16) || !aligned(v_cache[l], 16))
+            return fail(FS_E_ARG, "layer %d cache not 16-byte aligned", l);
+    }
+    if (k == 0) return FS_OK;
+    InjectLaunch a{store, lb, le, batch, user, ids, k, block_table, max_blocks, start_pos,
+                   k_cache, v_cache, num_blocks, reinterpret_cast<hipStream_t>(stream)};
+    hipError_t e = fsi_launch_inject(a);
+    if (e != hipSuccess) return hip_fail(e, "inject launch");
+    return FS_OK;
+}
+
+fs_status fs_fetch_async(const fs_store* store, int32_t batch, const int32_t* user,
+                         const int32_t* ids, int32_t k, int32_t layer_begin, int32_t layer_end,
+                         void* stream) {
+    g_msg[0] = 0;
+    if (!store) return fail(FS_E_ARG, "null store");
+    const fs_store_desc& d = store->desc;
+    if (d.kv_location != FS_KV_PINNED_HOST)
+        return fail(FS_E_UNSUPPORTED, "fs_fetch_async needs a pinned-host store");
+    if (batch < 1 || batch > d.max_batch)
+        return fail(FS_E_RANGE, "batch %d outside [1, %d]", batch, d.max_batch);
+    if (k < 0 || k > d.max_k) return fail(FS_E_RANGE, "k %d outside [0, %d]", k, d.max_k);
+    if (layer_begin < 0 || layer_end > d.num_layers || layer_begin >= layer_end)
+        return fail(FS_E_RANGE, "layer range [%d, %d) invalid", layer_begin, layer_end);
+    if (layer_end - layer_begin > d.staging_layers)
+        return fail(FS_E_RANGE, "layer range wider than staging_layers %d", d.staging_layers);
+    if (!user || !ids) return fail(FS_E_ARG, "null pointer argument");
+    if (!aligned(user, 4) || !aligned(ids, 4)) return fail(FS_E_ARG, "int32 argument not 4-byte aligned");
+    if (k == 0) return FS_OK;
+    FetchLaunch a{store, layer_begin, layer_end, batch, user, ids, k,
+                  reinterpret_cast<hipStream_t>(stream)};
+    hipError_t e = fsi_launch_fetch(a);
+    if (e != hipSuccess) return hip_fail(e, "fetch launch");
+    return FS_OK;
+}
+
+fs_status fs_poll_errors(const fs_store* store, void* stream, uint32_t* flags) {
+    g_msg[0] = 0;
+    if (!store || !flags) return fail(FS_E_ARG, "null pointer argument");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    uint32_t v = 0, zero = 0;
+    e = hipMemcpy(&v, store->d_err, sizeof(v), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy(error word)");
+    e = hipMemcpy(store->d_err, &zero, sizeof(zero), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy(clear error word)");
+    *flags = v;
+    if (v) return fail(FS_E_DEVICE, "device error bits 0x%x", v);
+    return FS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,341 @@
+// GPU-resident retrieval: embedding scores and top-k selection.
+//
+// InferScale keeps the retrieval index and the KV store on the GPU and picks
+// the k most relevant facts per request (gist.science summary,
+// "Contributions Clés" and "Problématique").  Here the similarity is the
+// inner product of fp32 embeddings: each fp32*fp32 product is exact in fp64
+// and the sum is accumulated in fp64, so two facts with identical embedding
+// rows get bit-identical scores and the tie is settled by the lower fact id.
+//
+// score kernel   grid (row tiles, batch), 256 threads = 4 waves, 2 rows per
+//                wave; each lane owns a fixed set of columns (float4 c, c+64,
+//                ...), accumulates them in order, then a fixed butterfly
+//                reduces the wave.  The reduction order depends only on the
+//                column, never on the row, which is what makes equal rows tie.
+// top-k kernel   one 1024-thread block per request.  Scores map to
+//                order-preserving 64-bit keys; an MSB-first radix select
+//                (8-bit digits, LDS histogram) finds the k-th key, stopping as
+//                soon as the boundary bucket is taken whole; ties on the full
+//                key keep the lowest indices (block-wide ordered scan); the
+//                k' winners are bitonic-sorted in LDS by (key desc, id asc).
+//                The same block sums the winners' lengths (the segment length).
+
+#include <hip/hip_runtime.h>
+
+#include "fs_internal.h"
+
+namespace {
+
+constexpr int kScoreWaves = 4;
+constexpr int kScoreRowsPerWave = 2;
+constexpr int kScoreRowsPerBlock = kScoreWaves * kScoreRowsPerWave;
+constexpr int kTopkThreads = 1024;
+
+__device__ __forceinline__ uint64_t order_key(double x) {
+    uint64_t u = (x == 0.0) ? 0ull : static_cast<uint64_t>(__double_as_longlong(x));
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ double key_value(uint64_t key) {
+    uint64_t u = (key >> 63) ? (key & 0x7FFFFFFFFFFFFFFFull) : ~key;
+    return __longlong_as_double(static_cast<long long>(u));
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+struct ScoreArgs {
+    const float4* emb;        // [F][E/4]
+    int32_t e4;               // E/4
+    const int64_t* user_begin;
+    int32_t num_users;
+    const int32_t* user;
+    const float4* query;      // [B][E/4]
+    double* scores;           // [B][stride]
+    int32_t stride;
+};
+
+__global__ __launch_bounds__(256) void fs_score_kernel(ScoreArgs a) {
+    extern __shared__ float4 q_lds[];
+    const int b = blockIdx.y;
+    const int u = a.user[b];
+    if (u < 0 || u >= a.num_users) return;
+    const int64_t base = a.user_begin[u];
+    const int32_t n = static_cast<int32_t>(a.user_begin[u + 1] - base);
+    const int32_t row0 = blockIdx.x * kScoreRowsPerBlock;
+    if (row0 >= n) return;
+    for (int c = threadIdx.x; c < a.e4; c += blockDim.x) q_lds[c] = a.query[int64_t(b) * a.e4 + c];
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int32_t r0 = row0 + wave * kScoreRowsPerWave;
+    const bool v0 = r0 < n, v1 = r0 + 1 < n;
+    const float4* e0 = a.emb + (base + r0) * a.e4;
+    const float4* e1 = e0 + a.e4;
+    double acc0 = 0.0, acc1 = 0.0;
+#pragma unroll 4
+    for (int c = lane; c < a.e4; c += 64) {
+        const float4 q = q_lds[c];
+        if (v0) {
+            const float4 e = e0[c];
+            acc0 = fma(double(e.x), double(q.x), acc0);
+            acc0 = fma(double(e.y), double(q.y), acc0);
+            acc0 = fma(double(e.z), double(q.z), acc0);
+            acc0 = fma(double(e.w), double(q.w), acc0);
+        }
+        if (v1) {
+            const float4 e = e1[c];
+            acc1 = fma(double(e.x), double(q.x), acc1);
+            acc1 = fma(double(e.y), double(q.y), acc1);
+            acc1 = fma(double(e.z), double(q.z), acc1);
+            acc1 = fma(double(e.w), double(q.w), acc1);
+        }
+    }
+    acc0 = wave_sum(acc0);
+    acc1 = wave_sum(acc1);
+    if (lane == 0) {
+        double* out = a.scores + int64_t(b) * a.stride;
+        if (v0) out[r0] = acc0;
+        if (v1) out[r0 + 1] = acc1;
+    }
+}
+
+struct TopkArgs {
+    const double* scores;     // [B][stride]
+    int32_t stride;
+    const int64_t* user_begin;
+    int32_t num_users;
+    const int32_t* user;
+    const int32_t* fact_len;
+    int32_t k;
+    int32_t* ids;             // [B][k] or null when k == 0
+    double* out_scores;       // [B][k] or null
+    int32_t* num_tokens;      // [B] or null
+    uint32_t* err;
+};
+
+__global__ __launch_bounds__(kTopkThreads) void fs_topk_kernel(TopkArgs a) {
+    __shared__ int hist[256];
+    __shared__ uint64_t cand_key[fsi::kMaxK];
+    __shared__ int32_t cand_idx[fsi::kMaxK];
+    __shared__ int wave_cnt[kTopkThreads / 64];
+    __shared__ uint64_t s_prefix, s_mask;
+    __shared__ int s_rem, s_done, s_ncand, s_tokens;
+    extern __shared__ uint64_t keys_lds[];
+
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int k = a.k;
+    const int u = a.user[b];
+    const bool bad_user = (u < 0 || u >= a.num_users);
+    const int64_t base = bad_user ? 0 : a.user_begin[u];
+    const int32_t n = bad_user ? 0 : static_cast<int32_t>(a.user_begin[u + 1] - base);
+    const int kk = n < k ? n : k;
+
+    if (bad_user && tid == 0) atomicOr(a.err, FS_ERR_USER);
+    if (kk == 0) {
+        for (int j = tid; j < k; j += blockDim.x) {
+            a.ids[int64_t(b) * k + j] = -1;
+            if (a.out_scores) a.out_scores[int64_t(b) * k + j] = -__builtin_huge_val();
+        }
+        if (a.num_tokens && tid == 0) a.num_tokens[b] = 0;
+        return;
+    }
+
+    const double* sc = a.scores + int64_t(b) * a.stride;
+    const bool in_lds = n <= fsi::kTopkLdsKeys;
+    if (in_lds)
+        for (int i = tid; i < n; i += blockDim.x) keys_lds[i] = order_key(sc[i]);
+    auto key_at = [&](int i) -> uint64_t { return in_lds ? keys_lds[i] : order_key(sc[i]); };
+
+    if (tid == 0) {
+        s_prefix = 0;
+        s_mask = 0;
+        s_rem = kk;
+        s_done = 0;
+        s_ncand = 0;
+        s_tokens = 0;
+    }
+    __syncthreads();
+
+    // ---- MSB-first radix select of the kk-th largest key ------------------
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0;
+        __syncthreads();
+        const uint64_t prefix = s_prefix, mask = s_mask;
+        for (int i = tid; i < n; i += blockDim.x) {
+            const uint64_t key = key_at(i);
+            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xFF], 1);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // lane l holds digits 255-4l .. 252-4l (descending)
+            int c[4];
+            int sum = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                c[j] = hist[255 - 4 * lane - j];
+                sum += c[j];
+            }
+            int incl = sum;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                int y = __shfl_up(incl, off, 64);
+                if (lane >= off) incl += y;
+            }
+            const int excl = incl - sum;
+            const int rem = s_rem;
+            if (excl < rem && rem <= incl) {
+                int cum = excl;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (cum + c[j] >= rem) {
+                        const uint64_t digit = uint64_t(255 - 4 * lane - j);
+                        const int left = rem - cum;       // still needed from this digit
+                        s_prefix = prefix | (digit << shift);
+                        s_mask = mask | (0xFFull << shift);
+                        s_rem = left;
+                        s_done = (c[j] == left);
+                        break;
+                    }
+                    cum += c[j];
+                }
+            }
+        }
+        __syncthreads();
+        if (s_done) break;
+    }
+
+    // ---- collect the winners ---------------------------------------------
+    const uint64_t prefix = s_prefix, mask = s_mask;
+    const bool done = s_done != 0;
+    const int rem = s_rem;
+    for (int i = tid; i < n; i += blockDim.x) {
+        const uint64_t key = key_at(i);
+        const uint64_t m = key & mask;
+        if (m > prefix || (done && m == prefix)) {
+            const int slot = atomicAdd(&s_ncand, 1);
+            cand_key[slot] = key;
+            cand_idx[slot] = i;
+        }
+    }
+    __syncthreads();
+    if (!done) {
+        // equal full keys: keep the `rem` lowest indices, in index order
+        const int first_slot = kk - rem;
+        int taken = 0;
+        for (int c0 = 0; c0 < n && taken < rem; c0 += blockDim.x) {
+            const int i = c0 + tid;
+            const bool eq = i < n && key_at(i) == prefix;
+            const uint64_t bal = __ballot(eq);
+            if (lane == 0) wave_cnt[wave] = __popcll(bal);
+            __syncthreads();
+            int before = 0, total = 0;
+            for (int w = 0; w < kTopkThreads / 64; ++w) {
+                if (w < wave) before += wave_cnt[w];
+                total += wave_cnt[w];
+            }
+            const int rank = taken + before + __popcll(bal & ((1ull << lane) - 1ull));
+            if (eq && rank < rem) {
+                cand_key[first_slot + rank] = prefix;
+                cand_idx[first_slot + rank] = i;
+            }
+            taken += total;
+            __syncthreads();
+        }
+    }
+
+    // ---- bitonic sort of the kk winners: key desc, index asc ---------------
+    int P = 1;
+    while (P < kk) P <<= 1;
+    for (int i = kk + tid; i < P; i += blockDim.x) {
+        cand_key[i] = 0;
+        cand_idx[i] = 0x7FFFFFFF;
+    }
+    __syncthreads();
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < P; i += blockDim.x) {
+                const int j = i ^ stride;
+                if (j > i) {
+                    const uint64_t ki = cand_key[i], kj = cand_key[j];
+                    const int32_t ii = cand_idx[i], ij = cand_idx[j];
+                    const bool j_first = (kj > ki) || (kj == ki && ij < ii);
+                    const bool i_first = (ki > kj) || (ki == kj && ii < ij);
+                    const bool ascending = (i & size) == 0;
+                    if (ascending ? j_first : i_first) {
+                        cand_key[i] = kj;
+                        cand_key[j] = ki;
+                        cand_idx[i] = ij;
+                        cand_idx[j] = ii;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---- outputs -----------------------------------------------------------
+    int my_tokens = 0;
+    for (int j = tid; j < k; j += blockDim.x) {
+        int32_t id = -1;
+        double s = -__builtin_huge_val();
+        if (j < kk) {
+            id = static_cast<int32_t>(base + cand_idx[j]);
+            s = key_value(cand_key[j]);
+            my_tokens += a.fact_len[id];
+        }
+        a.ids[int64_t(b) * k + j] = id;
+        if (a.out_scores) a.out_scores[int64_t(b) * k + j] = s;
+    }
+    if (a.num_tokens) {
+        if (my_tokens) atomicAdd(&s_tokens, my_tokens);
+        __syncthreads();
+        if (tid == 0) a.num_tokens[b] = s_tokens;
+    }
+}
+
+}  // namespace
+
+hipError_t fsi_launch_retrieve(const RetrieveLaunch& r) {
+    const fs_store* st = r.st;
+    const fs_store_desc& d = st->desc;
+    if (r.k > 0 && st->max_user_facts > 0) {
+        ScoreArgs sa;
+        sa.emb = reinterpret_cast<const float4*>(st->emb);
+        sa.e4 = d.embed_dim / 4;
+        sa.user_begin = st->d_user_begin;
+        sa.num_users = d.num_users;
+        sa.user = r.user;
+        sa.query = reinterpret_cast<const float4*>(r.query);
+        sa.scores = st->d_scores;
+        sa.stride = st->max_user_facts;
+        dim3 grid((st->max_user_facts + kScoreRowsPerBlock - 1) / kScoreRowsPerBlock, r.batch);
+        size_t lds = sizeof(float4) * sa.e4;
+        fs_score_kernel<<<grid, 256, lds, r.stream>>>(sa);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    TopkArgs ta;
+    ta.scores = st->d_scores;
+    ta.stride = st->max_user_facts;
+    ta.user_begin = st->d_user_begin;
+    ta.num_users = d.num_users;
+    ta.user = r.user;
+    ta.fact_len = st->d_fact_len;
+    ta.k = r.k;
+    ta.ids = r.ids;
+    ta.out_scores = r.scores;
+    ta.num_tokens = r.num_tokens;
+    ta.err = st->d_err;
+    const int lds_keys = st->max_user_facts < fsi::kTopkLdsKeys ? st->max_user_facts : fsi::kTopkLdsKeys;
+    size_t lds = sizeof(uint64_t) * size_t(lds_keys);
+    fs_topk_kernel<<<dim3(r.batch), kTopkThreads, lds, r.stream>>>(ta);
+    return hipGetLastError();
+}

@@ -1,0 +1,271 @@
+"""Python binding of libfs.so (ctypes): argument marshalling only.
+
+Every function here has the name of the C entry point it calls (include/fs.h)
+and does nothing but check that the tensors it is handed are what the C side
+expects (dtype, device, contiguity, shape — a wrong buffer would otherwise
+become a GPU memory fault), turn them into pointers, call the library and turn
+a failing status into FsError.  All computation happens in the library's HIP
+kernels; there is no fallback.  torch is used for device memory and streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch  # loads torch's HIP runtime first, so libfs.so binds to the same one
+
+from .build import LIB_PATH
+
+# ---- constants mirrored from include/fs.h (tests check they agree) ---------
+FS_OK = 0
+FS_E_ARG = 1
+FS_E_RANGE = 2
+FS_E_BLOCKTABLE = 3
+FS_E_NOMEM = 4
+FS_E_HIP = 5
+FS_E_DEVICE = 6
+FS_E_UNSUPPORTED = 7
+
+FS_ERR_USER = 0x01
+FS_ERR_FACT_ID = 0x02
+FS_ERR_START_POS = 0x04
+FS_ERR_BLOCK_SHORT = 0x08
+FS_ERR_BLOCK_ID = 0x10
+FS_ERR_STAGING = 0x20
+
+FS_ALL_LAYERS = -1
+FS_MAX_LAYERS = 128
+FS_MAX_K = 1024
+FS_KV_DEVICE = 0
+FS_KV_PINNED_HOST = 1
+
+EXPORTS = ("fs_create_store", "fs_destroy_store", "fs_retrieve_topk", "fs_inject",
+           "fs_fetch_async", "fs_poll_errors", "fs_strerror", "fs_last_error_message")
+
+
+class fs_store_desc(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("embed_dim", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double),
+        ("block_size", ctypes.c_int32),
+        ("kv_location", ctypes.c_int32),
+        ("num_users", ctypes.c_int32),
+        ("max_batch", ctypes.c_int32),
+        ("max_k", ctypes.c_int32),
+        ("staging_layers", ctypes.c_int32),
+        ("num_facts", ctypes.c_int64),
+        ("num_tokens", ctypes.c_int64),
+    ]
+
+
+class FsError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({fs_strerror(status)}): {detail}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built: run `python -m kv_cache_injection_amd.build` "
+            "(or __graft_entry__.build()); there is no non-HIP fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    sig = {
+        "fs_create_store": (i32, [ctypes.POINTER(fs_store_desc), P, P, P, P, P, P,
+                                  ctypes.POINTER(P)]),
+        "fs_destroy_store": (i32, [P]),
+        "fs_retrieve_topk": (i32, [P, i32, P, P, i32, P, P, P, P]),
+        "fs_inject": (i32, [P, i32, i32, P, P, i32, P, i32, P, P, P, i32, P]),
+        "fs_fetch_async": (i32, [P, i32, P, P, i32, i32, i32, P]),
+        "fs_poll_errors": (i32, [P, P, ctypes.POINTER(ctypes.c_uint32)]),
+        "fs_strerror": (ctypes.c_char_p, [i32]),
+        "fs_last_error_message": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def fs_strerror(status: int) -> str:
+    return _lib.fs_strerror(int(status)).decode()
+
+
+def fs_last_error_message() -> str:
+    return _lib.fs_last_error_message().decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != FS_OK:
+        raise FsError(status, where, fs_last_error_message())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t: Optional[torch.Tensor], dtype, *, shape=None, name="tensor", device=True):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Store:
+    """Handle returned by fs_create_store.  Keeps references to the caller's
+    buffers the library points into, so they outlive the store."""
+
+    def __init__(self, handle: ctypes.c_void_p, desc: fs_store_desc, refs):
+        self.handle = handle
+        self.desc = desc
+        self._refs = refs
+
+    def close(self) -> None:
+        if self.handle:
+            fs_destroy_store(self)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _handle(store) -> ctypes.c_void_p:
+    return store.handle if isinstance(store, Store) else store
+
+
+def fs_create_store(desc: fs_store_desc, user_fact_begin, fact_len, emb: torch.Tensor,
+                    k_pre: Sequence[torch.Tensor], v: Sequence[torch.Tensor],
+                    stream=None) -> Store:
+    import numpy as np
+    ufb = np.ascontiguousarray(user_fact_begin, dtype=np.int64)
+    fl = np.ascontiguousarray(fact_len, dtype=np.int32)
+    if ufb.shape != (desc.num_users + 1,) or fl.shape != (desc.num_facts,):
+        raise ValueError("user_fact_begin / fact_len do not match desc")
+    _ptr(emb, torch.float32, shape=(desc.num_facts, desc.embed_dim), name="emb")
+    if len(k_pre) != desc.num_layers or len(v) != desc.num_layers:
+        raise ValueError("k_pre / v need one arena per layer")
+    row = (desc.num_tokens, desc.num_kv_heads, desc.head_dim)
+    pinned = desc.kv_location == FS_KV_PINNED_HOST
+    for name, lst in (("k_pre", k_pre), ("v", v)):
+        for t in lst:
+            _ptr(t, torch.bfloat16, shape=row, name=name, device=not pinned)
+            if pinned and t.device.type != "cpu":
+                raise ValueError(f"{name}: a pinned store takes host tensors")
+    karr = (ctypes.c_void_p * desc.num_layers)(*[t.data_ptr() for t in k_pre])
+    varr = (ctypes.c_void_p * desc.num_layers)(*[t.data_ptr() for t in v])
+    out = ctypes.c_void_p()
+    st = _lib.fs_create_store(ctypes.byref(desc), ufb.ctypes.data_as(ctypes.c_void_p),
+                              fl.ctypes.data_as(ctypes.c_void_p), ctypes.c_void_p(emb.data_ptr()),
+                              karr, varr, _stream(stream), ctypes.byref(out))
+    _check(st, "fs_create_store")
+    return Store(out, desc, (emb, list(k_pre), list(v)))
+
+
+def fs_destroy_store(store) -> None:
+    h = _handle(store)
+    st = _lib.fs_destroy_store(h)
+    if isinstance(store, Store):
+        store.handle = None
+        store._refs = None
+    _check(st, "fs_destroy_store")
+
+
+def fs_retrieve_topk(store, batch: int, user: torch.Tensor, query: torch.Tensor, k: int,
+                     ids: Optional[torch.Tensor], scores: Optional[torch.Tensor] = None,
+                     num_tokens: Optional[torch.Tensor] = None, stream=None) -> None:
+    d = store.desc if isinstance(store, Store) else None
+    E = d.embed_dim if d is not None else query.shape[-1]
+    st = _lib.fs_retrieve_topk(
+        _handle(store), int(batch),
+        _ptr(user, torch.int32, shape=(batch,), name="user"),
+        _ptr(query, torch.float32, shape=(batch, E), name="query"), int(k),
+        _ptr(ids, torch.int32, shape=(batch, k), name="ids"),
+        _ptr(scores, torch.float64, shape=(batch, k), name="scores"),
+        _ptr(num_tokens, torch.int32, shape=(batch,), name="num_tokens"),
+        _stream(stream))
+    _check(st, "fs_retrieve_topk")
+
+
+def fs_inject(store, layer: int, batch: int, user: torch.Tensor, ids: torch.Tensor, k: int,
+              block_table: torch.Tensor, max_blocks: int, start_pos: torch.Tensor,
+              k_cache: Sequence[Optional[torch.Tensor]], v_cache: Sequence[Optional[torch.Tensor]],
+              num_blocks: int, stream=None) -> None:
+    d = store.desc if isinstance(store, Store) else None
+    if d is not None:
+        if len(k_cache) != d.num_layers or len(v_cache) != d.num_layers:
+            raise ValueError("k_cache / v_cache need one entry per layer (None allowed)")
+        cshape = (num_blocks, d.block_size, d.num_kv_heads, d.head_dim)
+        lay = range(d.num_layers) if layer == FS_ALL_LAYERS else [layer]
+        for l in lay:
+            if 0 <= l < d.num_layers:
+                _ptr(k_cache[l], torch.bfloat16, shape=cshape, name=f"k_cache[{l}]")
+                _ptr(v_cache[l], torch.bfloat16, shape=cshape, name=f"v_cache[{l}]")
+    n = len(k_cache)
+    karr = (ctypes.c_void_p * n)(*[0 if t is None else t.data_ptr() for t in k_cache])
+    varr = (ctypes.c_void_p * n)(*[0 if t is None else t.data_ptr() for t in v_cache])
+    st = _lib.fs_inject(
+        _handle(store), int(layer), int(batch),
+        _ptr(user, torch.int32, shape=(batch,), name="user"),
+        _ptr(ids, torch.int32, shape=(batch, k), name="ids"), int(k),
+        _ptr(block_table, torch.int32, shape=(batch, max_blocks), name="block_table"),
+        int(max_blocks),
+        _ptr(start_pos, torch.int32, shape=(batch,), name="start_pos"),
+        karr, varr, int(num_blocks), _stream(stream))
+    _check(st, "fs_inject")
+
+
+def fs_fetch_async(store, batch: int, user: torch.Tensor, ids: torch.Tensor, k: int,
+                   layer_begin: int, layer_end: int, stream=None) -> None:
+    st = _lib.fs_fetch_async(
+        _handle(store), int(batch),
+        _ptr(user, torch.int32, shape=(batch,), name="user"),
+        _ptr(ids, torch.int32, shape=(batch, k), name="ids"), int(k),
+        int(layer_begin), int(layer_end), _stream(stream))
+    _check(st, "fs_fetch_async")
+
+
+def fs_poll_errors(store, stream=None) -> int:
+    """Synchronise, return and clear the device error bits (0 = none)."""
+    flags = ctypes.c_uint32(0)
+    st = _lib.fs_poll_errors(_handle(store), _stream(stream), ctypes.byref(flags))
+    if st not in (FS_OK, FS_E_DEVICE):
+        _check(st, "fs_poll_errors")
+    return int(flags.value)
+
+
+def make_desc(**kw) -> fs_store_desc:
+    d = fs_store_desc()
+    d.staging_layers = 0
+    d.kv_location = FS_KV_DEVICE
+    d.block_size = 16
+    for k, v in kw.items():
+        if not hasattr(d, k):
+            raise AttributeError(k)
+        setattr(d, k, v)
+    return d

@@ -1,0 +1,368 @@
+"""GPU parity: the HIP library against the CPU oracle on seeded synthetic
+workloads, through the C ABI.
+
+Bar (checked element by element):
+  * top-k ids, num_tokens (segment length), placement and V bytes: bit-exact
+    (ids: when the oracle certifies the answer, i.e. every deciding score gap
+    exceeds the fp64 accumulation bound; otherwise validity of the tie);
+  * K: within 1 bf16 ulp of the oracle's once-rounded fp64 rotation;
+  * scores: within E * 2^-53 of the exactly rounded inner product;
+  * every cache byte outside the composed segments keeps the sentinel.
+
+Workloads: tiny (whole cache compared), Llama-3.1-8B shape at full size
+(every written row of all 32 layers), Qwen2.5-7B shape k in {5,10,20,50},
+the 100-user concurrent batch (full users and batch, 2 of 32 layers resident:
+the full store is 393 GB, more than one GPU holds), the 20,000-fact Mistral
+shape with 32 requests, its pinned-host variant, and edge cases.
+"""
+
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _parity import (bf16_ulp_distance, check_injection, check_retrieval, check_sentinel,
+                     gpu_retrieve, say, written_mask)
+from kv_cache_injection_amd import fs, synth
+from kv_cache_injection_amd.workload import build_store, make_desc, request_tensors
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _cleanup():
+    yield
+    gc.collect()
+    if torch.cuda.is_available():
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def _run(wl, layers, *, per_layer=False, ids_override=None, num_blocks=None):
+    """Create the store, retrieve, inject (all layers in one call, or one call
+    per layer), poll errors.  Returns (ds, req, ids, scores, ntok, kc, vc)."""
+    s = wl.shape
+    say(f"{s.name}: building store, layers={list(layers)[:4]}... T={wl.num_tokens}")
+    ds = build_store(wl, layers)
+    req = request_tensors(wl)
+    B, k = s.batch, wl.k
+    say(f"{s.name}: retrieve B={B} k={k}")
+    ids, scores, ntok = gpu_retrieve(ds, req, k, B)
+    kc, vc = synth.make_caches(wl, layers, "cuda", num_blocks)
+    nb = kc[0].shape[0]
+    inj_ids = ids if ids_override is None else ids_override
+    say(f"{s.name}: inject ({'per layer' if per_layer else 'all layers'})")
+    if per_layer:
+        for l in range(len(layers)):
+            fs.fs_inject(ds.store, l, B, req["user"], inj_ids, k, req["block_table"],
+                         wl.block_table.shape[1], req["start_pos"], kc, vc, nb)
+    else:
+        fs.fs_inject(ds.store, fs.FS_ALL_LAYERS, B, req["user"], inj_ids, k, req["block_table"],
+                     wl.block_table.shape[1], req["start_pos"], kc, vc, nb)
+    flags = fs.fs_poll_errors(ds.store)
+    assert flags == 0, f"device error bits 0x{flags:x}"
+    return ds, req, ids, scores, ntok, kc, vc
+
+
+def _host(t):
+    return t.cpu().numpy()
+
+
+# --------------------------------------------------------------------------- tiny
+
+def test_tiny_whole_cache():
+    wl = synth.make_workload("tiny")
+    ds, req, ids, scores, ntok, kc, vc = _run(wl, [0])
+    o = check_retrieval(wl, _host(ids), _host(scores), _host(ntok), [0], wl.k)
+    # the whole cache against the oracle's own injection into a sentinel cache
+    s = wl.shape
+    k_pre = [synth.bf16_bits(ds.k_pre[0])]
+    v_pre = [synth.bf16_bits(ds.v[0])]
+    ek = np.full(kc[0].shape, synth.SENTINEL_BITS, np.uint16)
+    ev = np.full(vc[0].shape, synth.SENTINEL_BITS, np.uint16)
+    L = oracle.inject_request(k_pre, v_pre, [ek], [ev], o[0], wl.fact_len, wl.fact_token_begin,
+                              int(wl.start_pos[0]), wl.block_table[0], s.block_size,
+                              s.rope_theta, [0])
+    assert L == 80
+    gk, gv = synth.bf16_bits(kc[0]), synth.bf16_bits(vc[0])
+    assert np.array_equal(gv, ev)
+    d = bf16_ulp_distance(gk, ek)
+    say(f"tiny: K elements off by 1 ulp: {int((d == 1).sum())} of {d.size}")
+    assert int(d.max()) <= 1
+    ds.close()
+
+
+# ------------------------------------------------------------ retrieval edge cases
+
+def _small_store(emb, ufb, fact_len, layers=1, H=2, D=128, bs=16, max_k=8, max_batch=4):
+    T = int(np.sum(fact_len))
+    k_pre = [torch.randn((T, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+    v = [torch.randn((T, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+    desc = fs.make_desc(num_layers=layers, num_kv_heads=H, head_dim=D, embed_dim=emb.shape[1],
+                        rope_theta=1e6, block_size=bs, num_users=len(ufb) - 1,
+                        max_batch=max_batch, max_k=max_k, num_facts=emb.shape[0], num_tokens=T)
+    e = torch.from_numpy(emb).cuda()
+    return fs.fs_create_store(desc, ufb, fact_len, e, k_pre, v), k_pre, v
+
+
+def test_retrieval_ties_padding_and_empty_user():
+    rng = np.random.default_rng(5)
+    E = 64
+    emb = rng.standard_normal((30, E)).astype(np.float32)
+    emb /= np.linalg.norm(emb, axis=1, keepdims=True)
+    emb[12] = emb[17]          # exact duplicates: must tie by lower id
+    emb[25] = emb[17]
+    ufb = np.array([0, 20, 20, 30], np.int64)     # user 1 has no facts
+    fl = rng.integers(1, 9, 30).astype(np.int32)
+    st, _, _ = _small_store(emb, ufb, fl, max_k=8)
+    q = np.stack([emb[17], emb[3], emb[27], emb[25]]).astype(np.float32)
+    users = np.array([0, 1, 2, 2], np.int32)
+    user_t = torch.from_numpy(users).cuda()
+    q_t = torch.from_numpy(q).cuda()
+    for k in (0, 1, 3, 8):
+        ids = torch.full((4, k), -7, dtype=torch.int32, device="cuda")
+        sc = torch.zeros((4, k), dtype=torch.float64, device="cuda")
+        nt = torch.full((4,), -7, dtype=torch.int32, device="cuda")
+        say(f"edge retrieval k={k}")
+        fs.fs_retrieve_topk(st, 4, user_t, q_t, k, ids, sc, nt)
+        assert fs.fs_poll_errors(st) == 0
+        g, gs, gn = _host(ids), _host(sc), _host(nt)
+        for b in range(4):
+            u = users[b]
+            o_ids, o_sc = oracle.retrieve(emb, ufb, u, q[b], k)
+            assert np.array_equal(g[b].astype(np.int64), o_ids), (k, b, g[b], o_ids)
+            kk = min(k, ufb[u + 1] - ufb[u])
+            assert np.all(np.abs(gs[b][:kk] - o_sc[:kk]) <= 1e-15)
+            assert np.all(np.isneginf(gs[b][kk:]))
+            assert gn[b] == oracle.compose(o_ids, fl)[1]
+    # user 0's query is row 17: its duplicate row 12 ties with it and wins
+    # on the lower id (row 25, the third copy, belongs to user 2)
+    ids = torch.empty((4, 3), dtype=torch.int32, device="cuda")
+    fs.fs_retrieve_topk(st, 4, user_t, q_t, 3, ids, None, None)
+    assert list(_host(ids)[0][:2]) == [12, 17]
+    st.close()
+
+
+def test_retrieval_bad_user_sets_error():
+    rng = np.random.default_rng(6)
+    emb = rng.standard_normal((10, 16)).astype(np.float32)
+    st, _, _ = _small_store(emb, np.array([0, 10], np.int64), np.full(10, 4, np.int32))
+    ids = torch.full((2, 3), -7, dtype=torch.int32, device="cuda")
+    nt = torch.full((2,), -7, dtype=torch.int32, device="cuda")
+    fs.fs_retrieve_topk(st, 2, torch.tensor([0, 3], dtype=torch.int32, device="cuda"),
+                        torch.from_numpy(emb[:2].copy()).cuda(), 3, ids, None, nt)
+    assert fs.fs_poll_errors(st) == fs.FS_ERR_USER
+    g = _host(ids)
+    assert np.all(g[1] == -1) and _host(nt)[1] == 0
+    assert np.all(g[0] >= 0)
+    assert fs.fs_poll_errors(st) == 0      # cleared
+    st.close()
+
+
+def test_host_checked_errors_enqueue_nothing():
+    rng = np.random.default_rng(7)
+    emb = rng.standard_normal((10, 16)).astype(np.float32)
+    st, _, _ = _small_store(emb, np.array([0, 10], np.int64), np.full(10, 4, np.int32),
+                            max_k=4, max_batch=2)
+    u = torch.zeros(2, dtype=torch.int32, device="cuda")
+    q = torch.from_numpy(emb[:2].copy()).cuda()
+    ids = torch.zeros((2, 5), dtype=torch.int32, device="cuda")
+    with pytest.raises(fs.FsError) as e:
+        fs.fs_retrieve_topk(st, 2, u, q, 5, ids)
+    assert e.value.status == fs.FS_E_RANGE
+    with pytest.raises(fs.FsError) as e:
+        fs.fs_retrieve_topk(st, 3, torch.zeros(3, dtype=torch.int32, device="cuda"),
+                            torch.zeros((3, 16), device="cuda"), 2,
+                            torch.zeros((3, 2), dtype=torch.int32, device="cuda"))
+    assert e.value.status == fs.FS_E_RANGE
+    kc = [torch.zeros((4, 16, 2, 128), dtype=torch.bfloat16, device="cuda")]
+    bt = torch.zeros((2, 4), dtype=torch.int32, device="cuda")
+    sp = torch.zeros(2, dtype=torch.int32, device="cuda")
+    with pytest.raises(fs.FsError) as e:
+        fs.fs_inject(st, 1, 2, u, ids[:, :2].contiguous(), 2, bt, 4, sp, kc, kc, 4)
+    assert e.value.status == fs.FS_E_RANGE
+    with pytest.raises(fs.FsError) as e:
+        fs.fs_fetch_async(st, 2, u, ids[:, :2].contiguous(), 2, 0, 1)
+    assert e.value.status == fs.FS_E_UNSUPPORTED
+    assert fs.fs_poll_errors(st) == 0
+    st.close()
+
+
+# --------------------------------------------------------- device-checked faults
+
+@pytest.mark.parametrize("fault", ["block_short", "block_id", "start_pos", "fact_id",
+                                   "pad_then_id", "user"])
+def test_device_checked_fault_writes_nothing(fault):
+    wl = synth.make_workload("tiny", seed=91)
+    s = wl.shape
+    B = 2
+    ds = build_store(wl, [0], max_batch=B)
+    rng = np.random.default_rng(3)
+    ids = np.stack([rng.choice(s.num_facts, wl.k, replace=False) for _ in range(B)]).astype(np.int32)
+    table = np.stack([rng.permutation(s.pool_blocks)[:8] for _ in range(B)]).astype(np.int32)
+    table[1] = np.setdiff1d(np.arange(s.pool_blocks), table[0])[:8]   # disjoint from request 0
+    sp = np.array([37, 5], np.int32)
+    users = np.zeros(B, np.int32)
+    mb = 8
+    expect = {"block_short": fs.FS_ERR_BLOCK_SHORT, "block_id": fs.FS_ERR_BLOCK_ID,
+              "start_pos": fs.FS_ERR_START_POS, "fact_id": fs.FS_ERR_FACT_ID,
+              "pad_then_id": fs.FS_ERR_FACT_ID, "user": fs.FS_ERR_USER}[fault]
+    if fault == "block_short":
+        sp[1] = 50                        # 50 + 80 tokens need 9 blocks, table has 8
+    elif fault == "block_id":
+        table[1, 3] = s.pool_blocks       # one past the end
+    elif fault == "start_pos":
+        sp[1] = -1
+    elif fault == "fact_id":
+        ids[1, 2] = s.num_facts
+    elif fault == "pad_then_id":
+        ids[1, 1] = -1
+    elif fault == "user":
+        users[1] = 1
+    kc, vc = synth.make_caches(wl, [0], "cuda")
+    say(f"fault {fault}")
+    fs.fs_inject(ds.store, fs.FS_ALL_LAYERS, B, torch.from_numpy(users).cuda(),
+                 torch.from_numpy(ids).cuda(), wl.k, torch.from_numpy(table).cuda(), mb,
+                 torch.from_numpy(sp).cuda(), kc, vc, s.pool_blocks)
+    assert fs.fs_poll_errors(ds.store) == expect
+    # request 0 is fine and written; request 1 wrote nothing
+    w0 = {0: ids[0].astype(np.int64)}
+    wl0 = synth.make_workload("tiny", seed=91)
+    wl0.start_pos = sp
+    wl0.block_table = table
+    wl0.users = users
+    check_injection(wl0, ds, kc, vc, w0, [0])
+    check_sentinel(kc, vc, written_mask(wl0, w0, s.pool_blocks), [0])
+    ds.close()
+
+
+# ------------------------------------------------------ other shapes and layouts
+
+@pytest.mark.parametrize("D, H, bs", [(64, 4, 16), (256, 2, 8), (128, 3, 1), (128, 8, 32)])
+def test_head_dims_and_block_sizes(D, H, bs):
+    import dataclasses
+    base = synth.CONFIGS["tiny"]
+    shape = dataclasses.replace(base, name=f"d{D}", num_kv_heads=H, head_dim=D, block_size=bs,
+                                num_layers=3, len_lo=3, len_hi=40, facts_per_user=120,
+                                table="free", start_lo=0, start_hi=300,
+                                pool_blocks=(300 + 5 * 40) // bs + 64, k=5, rope_theta=1e6)
+    wl = synth.make_workload(shape, seed=D + H + bs)
+    ds, req, ids, scores, ntok, kc, vc = _run(wl, [0, 1, 2])
+    o = check_retrieval(wl, _host(ids), _host(scores), _host(ntok), [0], wl.k)
+    check_injection(wl, ds, kc, vc, o, [0, 1, 2])
+    check_sentinel(kc, vc, written_mask(wl, o, kc[0].shape[0]), [0, 1, 2])
+    ds.close()
+    # one call per layer writes exactly what the all-layer call wrote
+    ds2, _, _, _, _, kc2, vc2 = _run(wl, [0, 1, 2], per_layer=True)
+    for l in range(3):
+        assert torch.equal(kc[l].view(torch.int16), kc2[l].view(torch.int16))
+        assert torch.equal(vc[l].view(torch.int16), vc2[l].view(torch.int16))
+    ds2.close()
+
+
+def test_multi_user_batch_small():
+    wl = synth.make_workload("concurrent", num_users=12, facts_per_user=150, batch=12)
+    ds, req, ids, scores, ntok, kc, vc = _run(wl, [0, 5])
+    o = check_retrieval(wl, _host(ids), _host(scores), _host(ntok), range(12), wl.k)
+    check_injection(wl, ds, kc, vc, o, [0, 1])
+    check_sentinel(kc, vc, written_mask(wl, o, kc[0].shape[0]), [0, 1])
+    ds.close()
+
+
+# --------------------------------------------------------------- full-size shapes
+
+def test_llama_full_size_all_rows():
+    wl = synth.make_workload("llama")
+    ds, req, ids, scores, ntok, kc, vc = _run(wl, range(32))
+    o = check_retrieval(wl, _host(ids), _host(scores), _host(ntok), [0], wl.k)
+    stats = {}
+    say("llama: oracle over all 32 layers")
+    check_injection(wl, ds, kc, vc, o, range(32), stats)
+    say(f"llama: K elements {stats['elements']}, off by 1 ulp {stats['ulp1']}")
+    check_sentinel(kc, vc, written_mask(wl, o, kc[0].shape[0]), [0, 31])
+    ds.close()
+
+
+@pytest.mark.parametrize("k", [5, 10, 20, 50])
+def test_qwen_k_sweep(k):
+    wl = synth.make_workload("qwen", k=k)
+    ds, req, ids, scores, ntok, kc, vc = _run(wl, range(28), per_layer=(k == 50))
+    o = check_retrieval(wl, _host(ids), _host(scores), _host(ntok), [0], k)
+    check_injection(wl, ds, kc, vc, o, [0, 13, 27])
+    check_sentinel(kc, vc, written_mask(wl, o, kc[0].shape[0]), [0, 27])
+    ds.close()
+
+
+def test_concurrent_batch_layer_chunk():
+    # 100 users x 1,000 facts, 100 requests: the full 32-layer store is 393 GB,
+    # so two of its layers are resident (every request keeps its real shape)
+    wl = synth.make_workload("concurrent")
+    ds, req, ids, scores, ntok, kc, vc = _run(wl, [0, 31])
+    say("concurrent: oracle retrieval for 100 requests")
+    o = check_retrieval(wl, _host(ids), _host(scores), _host(ntok), range(100), wl.k)
+    sample = {b: o[b] for b in (0, 1, 37, 63, 99)}
+    check_injection(wl, ds, kc, vc, sample, [0, 1])
+    check_sentinel(kc, vc, written_mask(wl, o, kc[0].shape[0]), [0, 1])
+    ds.close()
+
+
+def test_large_store_batch32():
+    wl = synth.make_workload("large")
+    ds, req, ids, scores, ntok, kc, vc = _run(wl, range(32))
+    say("large: oracle retrieval for 4 sampled requests")
+    o = check_retrieval(wl, _host(ids), _host(scores), _host(ntok), [0, 9, 21, 31], wl.k)
+    check_injection(wl, ds, kc, vc, o, [0, 17, 31])
+    # all 32 requests' segments for the sentinel check: the GPU ids are
+    # certified equal to the oracle's on the sampled requests; the others'
+    # slots come from the oracle's own retrieval
+    say("large: oracle retrieval for all 32 requests (sentinel mask)")
+    all_o = {b: oracle.retrieve(wl.emb, wl.user_fact_begin, 0, wl.queries[b], wl.k)[0]
+             for b in range(32)}
+    check_sentinel(kc, vc, written_mask(wl, all_o, kc[0].shape[0]), [0, 31])
+    ds.close()
+
+
+def test_pinned_host_store_fetch_then_inject():
+    # Mistral shape with the K/V arenas in page-locked host memory (4 of 32
+    # layers resident: 9.8 GB pinned), fetched over the host link on a side
+    # stream into a 2-layer staging ring, then rotated and scattered
+    wl = synth.make_workload("large")
+    s = wl.shape
+    layers = [0, 1, 2, 3]
+    say("pinned: building pinned store")
+    ds = build_store(wl, layers, pinned=True, staging_layers=2)
+    req = request_tensors(wl)
+    B, k = s.batch, wl.k
+    ids, scores, ntok = gpu_retrieve(ds, req, k, B)
+    kc, vc = synth.make_caches(wl, layers, "cuda")
+    nb = kc[0].shape[0]
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    for lb in (0, 2):
+        ev = torch.cuda.Event()
+        side.wait_stream(main)
+        say(f"pinned: fetch layers [{lb}, {lb + 2})")
+        fs.fs_fetch_async(ds.store, B, req["user"], ids, k, lb, lb + 2, stream=side)
+        ev.record(side)
+        main.wait_event(ev)
+        for l in (lb, lb + 1):
+            fs.fs_inject(ds.store, l, B, req["user"], ids, k, req["block_table"],
+                         wl.block_table.shape[1], req["start_pos"], kc, vc, nb)
+    assert fs.fs_poll_errors(ds.store) == 0
+    o = check_retrieval(wl, _host(ids), _host(scores), _host(ntok), [0, 31], k)
+    check_injection(wl, ds, kc, vc, o, [0, 1, 2, 3])
+    # the ring now holds layers 2 and 3: layer 0 is no longer staged, and
+    # layer 2 was staged for other ids — both injections are refused and
+    # write nothing
+    before_k = kc[0].clone()
+    fs.fs_inject(ds.store, 0, B, req["user"], ids, k, req["block_table"],
+                 wl.block_table.shape[1], req["start_pos"], kc, vc, nb)
+    assert fs.fs_poll_errors(ds.store) == fs.FS_ERR_STAGING
+    other = torch.roll(ids, 1, dims=1).contiguous()
+    fs.fs_inject(ds.store, 2, B, req["user"], other, k, req["block_table"],
+                 wl.block_table.shape[1], req["start_pos"], kc, vc, nb)
+    assert fs.fs_poll_errors(ds.store) == fs.FS_ERR_STAGING
+    assert torch.equal(before_k.view(torch.int16), kc[0].view(torch.int16))
+    ds.close()
