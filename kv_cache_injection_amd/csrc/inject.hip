@@ -131,7 +131,9 @@ __device__ uint32_t plan_request(const int32_t* user, const int32_t* ids, int k,
                 first_pad = min(first_pad, j);
             } else {
                 last_real = j;
-                if (id < ub0 || id >= ub1) {
+                if (bad_user) {
+                    // reported once as FS_ERR_USER; ids cannot be judged
+                } else if (id < ub0 || id >= ub1) {
                     bits |= FS_ERR_FACT_ID;
                 } else {
                     len = fact_len[id];

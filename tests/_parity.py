@@ -57,7 +57,11 @@ def check_retrieval(wl: synth.Workload, ids_gpu: np.ndarray, scores_gpu: np.ndar
         u = int(wl.users[b])
         a, e = int(wl.user_fact_begin[u]), int(wl.user_fact_begin[u + 1])
         s_all = oracle.score(wl.emb[a:e], wl.queries[b])
-        o_ids, o_sc = oracle.retrieve(wl.emb, wl.user_fact_begin, u, wl.queries[b], k)
+        local = oracle.select_topk(s_all, k)
+        o_ids = np.full(k, -1, np.int64)
+        o_sc = np.full(k, -np.inf)
+        o_ids[: len(local)] = np.asarray(local, np.int64) + a
+        o_sc[: len(local)] = s_all[local]
         out[b] = o_ids
         g_ids = ids_gpu[b].astype(np.int64)
         kk = min(k, e - a)
@@ -124,14 +128,32 @@ def written_mask(wl: synth.Workload, ids_by_req: Dict[int, np.ndarray], num_bloc
     return m
 
 
-def check_sentinel(kc: list, vc: list, mask: np.ndarray, layer_idx: Sequence[int]) -> None:
-    """Every slot outside ``mask`` still holds the sentinel, in every byte."""
-    keep = torch.from_numpy(~mask).cuda()
+def table_mask(wl: synth.Workload, requests: Sequence[int], num_blocks: int):
+    """Boolean [num_blocks, block_size]: every slot of every block that the
+    listed requests' block tables reference."""
+    s = wl.shape
+    m = np.zeros((num_blocks, s.block_size), bool)
+    for b in requests:
+        t = wl.block_table[b]
+        m[t[(t >= 0) & (t < num_blocks)]] = True
+    return m
+
+
+def check_sentinel(kc: list, vc: list, mask: np.ndarray, layer_idx: Sequence[int],
+                   skip: Optional[np.ndarray] = None) -> None:
+    """Every slot outside ``mask`` still holds the sentinel, in every byte, and
+    every slot inside it was written.  Slots in ``skip`` are not examined
+    (blocks of requests whose segments were not computed by the oracle)."""
+    sent = np.int16(np.uint16(synth.SENTINEL_BITS).view(np.int16)).item()
+    if skip is None:
+        skip = np.zeros_like(mask)
+    keep = torch.from_numpy(~mask & ~skip).cuda()
+    wrote = torch.from_numpy(mask & ~skip).cuda()
     for li in layer_idx:
         for name, c in (("K", kc[li]), ("V", vc[li])):
             untouched = c.view(torch.int16)[keep]
-            bad = int((untouched != np.int16(np.uint16(synth.SENTINEL_BITS).view(np.int16)).item()).sum())
+            bad = int((untouched != sent).sum())
             assert bad == 0, f"layer {li} {name}: {bad} elements changed outside the segment"
-            written = c.view(torch.int16)[~keep]
-            still = int((written == np.int16(np.uint16(synth.SENTINEL_BITS).view(np.int16)).item()).sum())
+            written = c.view(torch.int16)[wrote]
+            still = int((written == sent).sum())
             assert still == 0, f"layer {li} {name}: {still} elements of the segment not written"
