@@ -1,0 +1,223 @@
+"""Throughput of the KV-injection hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config llama] [--k 50]
+
+One step = one pass of the whole hot path over one batch of requests:
+fs_retrieve_topk (embedding scores + top-k + segment length) followed by one
+all-layer fs_inject (gather -> Chunked RoPE -> paged scatter into every layer's
+cache).  Inputs are resident in HBM before the timed region; every step uses
+a different (query, start position, block table) set, cycling through
+--sets pre-drawn sets, so the selected facts change from step to step.
+
+Prints ONE JSON line:
+  value       whole-step algorithmic HBM bytes / step time (GB/s)
+  roofline    the inject kernel: its algorithmic bytes per launch over its
+              average launch time, measured with HIP events on the launch
+              stream over the timed region, against 8 TB/s
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload
+
+Algorithmic bytes: inject = 8 * L * layers * heads * head_dim (K and V, bf16,
+read once and written once) per request of segment length L; retrieval =
+4 * N_user * embed_dim (one fp32 scan of the user's embeddings) per request.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=300)
+    p.add_argument("--warmup", type=int, default=30)
+    p.add_argument("--config", default="llama",
+                   choices=["tiny", "llama", "qwen", "concurrent", "large"])
+    p.add_argument("--k", type=int, default=None)
+    p.add_argument("--layers", type=int, default=None,
+                   help="resident layers (default: all; the concurrent store needs fewer)")
+    p.add_argument("--sets", type=int, default=50)
+    p.add_argument("--cpu-requests", type=int, default=2,
+                   help="requests of the oracle's bounded CPU sample (0 = skip)")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run a plain 1 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from kv_cache_injection_amd import fs, synth
+    from kv_cache_injection_amd.workload import build_store, request_tensors
+
+    torch.cuda.set_device(0)
+    wl = synth.make_workload(args.config, k=args.k)
+    s = wl.shape
+    nl = args.layers or s.num_layers
+    layers = list(range(nl))
+    B, k = s.batch, wl.k
+    print(f"[bench] {s.name}: building store ({nl} layers, {wl.num_tokens} tokens)", file=sys.stderr, flush=True)
+    ds = build_store(wl, layers)
+    kc, vc = synth.make_caches(wl, layers, "cuda")
+    nb = kc[0].shape[0]
+    caches = fs.CacheTable(ds.store, kc, vc, nb)
+    base = request_tensors(wl)
+    sets = []
+    for r in synth.request_sets(wl, args.sets, seed=wl.seed + 1):
+        t = request_tensors(wl, queries=r["queries"], start_pos=r["start_pos"],
+                            block_table=r["block_table"])
+        sets.append(t)
+    mb = wl.block_table.shape[1]
+    user = base["user"]
+    ids = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    total = args.warmup + args.steps
+    ntok = torch.zeros((total, B), dtype=torch.int32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(total)]
+
+    def step(i):
+        r = sets[i % len(sets)]
+        e0, e1, e2 = ev[i]
+        e0.record()
+        fs.fs_retrieve_topk(ds.store, B, user, r["query"], k, ids, None, ntok[i])
+        e1.record()
+        fs.fs_inject(ds.store, fs.FS_ALL_LAYERS, B, user, ids, k, r["block_table"], mb,
+                     r["start_pos"], caches)
+        e2.record()
+
+    print(f"[bench] warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    flags = fs.fs_poll_errors(ds.store)
+    if flags:
+        raise RuntimeError(f"device error bits 0x{flags:x}")
+
+    wall = t1 - t0
+    timed = range(args.warmup, total)
+    L = ntok.cpu().numpy().astype(np.int64)[args.warmup:]          # [steps, B]
+    row_bytes = 2 * s.num_kv_heads * s.head_dim                      # one token, one layer, K or V
+    inject_bytes = 4 * row_bytes * L.sum(axis=1) * nl                # K,V read + write
+    n_user = np.diff(wl.user_fact_begin)[wl.users]
+    scan_bytes = 4 * int(n_user.sum()) * s.embed_dim
+    step_bytes = inject_bytes + scan_bytes
+    inj_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in timed])
+    ret_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in timed])
+    achieved = float(inject_bytes.sum() / (inj_ms.sum() * 1e-3) / 1e9)
+    value = float(step_bytes.sum() / wall / 1e9)
+    ms_per_step = wall / args.steps * 1e3
+
+    if args.copy_probe:
+        a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+        bb = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        bb.copy_(a)
+        c1.record()
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: 1 GiB read + 1 GiB write in {c0.elapsed_time(c1):.3f} ms",
+              file=sys.stderr, flush=True)
+        del a, bb
+
+    cpu = None
+    if args.cpu_requests > 0:
+        cpu = cpu_baseline(wl, ds, layers, args.cpu_requests)
+
+    out = {
+        "metric": "KV-injection GB/s & requests/s at k=50, Llama-8B shape; % of HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "requests_per_s": round(B * args.steps / wall, 1),
+        "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "config": {
+            "workload": f"{s.name}: {nl} layers x {s.num_kv_heads} KV heads x head_dim {s.head_dim}, "
+                        f"theta {s.rope_theta:g}; {s.num_users} user(s) x {s.facts_per_user} facts "
+                        f"of U[{s.len_lo},{s.len_hi}] tokens, {s.embed_dim}-d embeddings; "
+                        f"{B} request(s) per step, k={k}, block_size {s.block_size}",
+            "batch": B, "k": k, "layers": nl, "mean_segment_tokens": round(float(L.mean()), 1),
+            "request_sets": args.sets,
+        },
+        "kernels_ms": {"retrieve_avg": round(float(ret_ms.mean()), 5),
+                       "inject_avg": round(float(inj_ms.mean()), 5)},
+        "roofline": {"bound": "hbm", "kernel": "fs_inject_kernel<128>",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": float(inject_bytes.mean()), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    ds.close()
+
+
+def cpu_baseline(wl, ds, layers, n_req):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    retrieve + compose + rotate + scatter for ``n_req`` requests over every
+    resident layer, single thread.  Same algorithmic-bytes accounting."""
+    import numpy as np
+
+    import oracle
+    from kv_cache_injection_amd import synth
+
+    s = wl.shape
+    print(f"[bench] cpu baseline: copying arenas to host", file=sys.stderr, flush=True)
+    kb = [synth.bf16_bits(t) for t in ds.k_pre]
+    vb = [synth.bf16_bits(t) for t in ds.v]
+    nb = s.pool_blocks
+    shape = (nb, s.block_size, s.num_kv_heads, s.head_dim)
+    kc = [np.full(shape, synth.SENTINEL_BITS, np.uint16) for _ in layers]
+    vc = [np.full(shape, synth.SENTINEL_BITS, np.uint16) for _ in layers]
+    total_bytes = 0
+    t0 = time.perf_counter()
+    sets = synth.request_sets(wl, n_req, seed=wl.seed + 1)   # the bench's first sets
+    for b in range(n_req):
+        r = sets[b]
+        u = int(wl.users[0])
+        ids, _ = oracle.retrieve(wl.emb, wl.user_fact_begin, u, r["queries"][0], wl.k)
+        L = oracle.inject_request(kb, vb, kc, vc, ids, wl.fact_len, wl.fact_token_begin,
+                                  int(r["start_pos"][0]), r["block_table"][0], s.block_size,
+                                  s.rope_theta, layers)
+        n_user = int(wl.user_fact_begin[u + 1] - wl.user_fact_begin[u])
+        total_bytes += 8 * L * len(layers) * s.num_kv_heads * s.head_dim + 4 * n_user * s.embed_dim
+    dt = time.perf_counter() - t0
+    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s",
+            "requests_per_s": round(n_req / dt, 4), "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"{n_req} request(s) of the {s.name} workload, {len(layers)} layers, "
+                      f"k={wl.k}: numpy fp64 oracle, one thread"}
+
+
+if __name__ == "__main__":
+    main()

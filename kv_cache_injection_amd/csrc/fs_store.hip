@@ -43,16 +43,12 @@ int ilog2(int64_t x) {
 void free_store(fs_store* s) {
     if (!s) return;
     void* bufs[] = {s->d_fact_begin, s->d_fact_len, s->d_user_begin, s->d_inv_freq, s->d_err,
-                    s->d_scores, (void*)s->d_src_k, (void*)s->d_src_v, s->d_stage_k,
+                    s->d_scores, (void*)s->d_src_k, (void*)s->d_src_v, s->d_tok_src,
+                    s->d_tok_dst, s->d_req_len, s->d_rope_tab, s->d_req_base, s->d_stage_k,
                     s->d_stage_v, s->d_stage_ids, s->d_stage_meta};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
     delete s;
-}
-
-template <class T>
-hipError_t dev_alloc(T** p, size_t count) {
-    return hipMalloc(reinterpret_cast<void**>(p), count * sizeof(T) > 0 ? count * sizeof(T) : 1);
 }
 
 fs_status check_desc(const fs_store_desc* d) {
@@ -151,6 +147,9 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
     st->emb = emb;
     hipError_t e = hipGetDevice(&st->device);
     if (e != hipSuccess) { free_store(st); return hip_fail(e, "hipGetDevice"); }
+    e = hipDeviceGetAttribute(&st->num_cus, hipDeviceAttributeMultiprocessorCount, st->device);
+    if (e != hipSuccess || st->num_cus < 1) { free_store(st); return hip_fail(e, "hipDeviceGetAttribute(CUs)"); }
+    st->seg_tokens = max_len * d.max_k;
 
     // pointer kinds: a device store must hold device memory, a pinned store
     // page-locked host memory, and every kernel gets a device-visible address
@@ -205,6 +204,11 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
         {(void**)&st->d_scores, sizeof(double) * size_t(d.max_batch) * size_t(max_user > 0 ? max_user : 1), "score scratch"},
         {(void**)&st->d_src_k, sizeof(void*) * d.num_layers, "arena table"},
         {(void**)&st->d_src_v, sizeof(void*) * d.num_layers, "arena table"},
+        {(void**)&st->d_tok_src, sizeof(int64_t) * size_t(d.max_batch) * size_t(st->seg_tokens), "segment plan"},
+        {(void**)&st->d_tok_dst, sizeof(int64_t) * size_t(d.max_batch) * size_t(st->seg_tokens), "segment plan"},
+        {(void**)&st->d_req_len, sizeof(int32_t) * size_t(d.max_batch), "segment plan"},
+        {(void**)&st->d_rope_tab, sizeof(double2) * size_t(st->seg_tokens) * (D / 2), "RoPE table"},
+        {(void**)&st->d_req_base, sizeof(double2) * size_t(d.max_batch) * (D / 2), "RoPE bases"},
     };
     for (auto& a : allocs) {
         e = hipMalloc(a.p, a.bytes);
@@ -215,7 +219,7 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
         }
     }
     if (pinned) {
-        st->stage_tokens = max_len * d.max_k;
+        st->stage_tokens = st->seg_tokens;
         size_t rows = size_t(d.staging_layers) * d.max_batch * size_t(st->stage_tokens);
         size_t bytes = rows * H * D * 2;
         struct { void** p; size_t bytes; } sa[] = {
@@ -249,6 +253,8 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
         e = hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyHostToDevice, s);
         if (e != hipSuccess) { free_store(st); return hip_fail(e, "hipMemcpyAsync(metadata)"); }
     }
+    e = fsi_init_rope_table(st, s);
+    if (e != hipSuccess) { free_store(st); return hip_fail(e, "RoPE table kernel"); }
     e = hipStreamSynchronize(s);
     if (e != hipSuccess) { free_store(st); return hip_fail(e, "hipStreamSynchronize"); }
     *out = st;

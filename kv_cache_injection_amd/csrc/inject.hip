@@ -5,24 +5,36 @@
 // into one contiguous segment, every stored key is rotated to its new
 // serving-time position, and the composed K/V is scatter-copied into the
 // paged KV cache.  Values are copied raw.  The re-rotation is exact under
-// RoPE (Theorem 6 as the pages describe it), so this kernel evaluates the
+// RoPE (Theorem 6 as the pages describe it), so the kernel evaluates the
 // rotation in fp64 and rounds once to bf16.
 //
-// Work decomposition (HBM-bound copy with a small amount of arithmetic; no
-// dense contraction, so no MFMA):
-//   block = one wave (64 threads); grid = (token tiles, request, layer chunk)
-//   team  = head_dim/16 lanes per segment token; lane `tl` of a team owns the
-//           8 rotate-half pairs i = 8*tl .. 8*tl+7 (elements i and i + D/2),
-//           i.e. one 16-byte vector from each half of a head row
-//   a team computes cos/sin of p*w_i for its 8 frequencies ONCE (fp64) and
-//   reuses them for every head of every layer in its chunk.
-//   Per (layer, head): two 16-byte loads of K, two of V, two 16-byte stores
-//   of each — rows are 2*head_dim bytes, read and written whole by the team.
+// One fs_inject call is two launches:
 //
-// Every block first plans its request (prefix sums of the selected facts'
-// lengths, validation of ids, start position and the used block-table
-// entries).  A request that fails any check writes nothing; the first block
-// of the request records the reason in the store's error word.
+//   plan kernel    one block; each wave plans whole requests: prefix sums of
+//                  the selected facts' lengths, validation of ids, start
+//                  position, block-table entries (and staging slots), then a
+//                  token map (arena row and cache slot of every segment token)
+//                  in scratch.  A rejected request gets length 0 and an error
+//                  bit, so nothing of it is written.  Finally the block turns
+//                  the lengths into a prefix of work units over requests.
+//
+//   inject kernel  persistent: exactly 16 one-wave blocks per compute unit.
+//                  The job is cut into units = (request, group of tokens,
+//                  layer, head); wave w takes the w-th equal contiguous share.
+//                  Throughput here is capped per CU, so equal bytes per CU is
+//                  what keeps every CU busy until the end (a grid of blocks
+//                  per token tile leaves some CUs with 1.5x the bytes of
+//                  others).  A team of head_dim/16 lanes owns one token: lane
+//                  tl holds the 8 rotate-half pairs i = 8*tl .. 8*tl+7 (one
+//                  16-byte vector from each half of the head row), computes
+//                  cos/sin of p*w_i once in fp64 and reuses them for every
+//                  (layer, head) unit of that token group.  Units are
+//                  processed two at a time: 8 vector loads in flight per
+//                  lane, then rotation and 8 non-temporal stores (more would
+//                  not fit 128 VGPRs, the limit for 16 waves per CU).
+//
+// HBM-bound copy with a small amount of arithmetic; no dense contraction, so
+// no MFMA.
 
 #include <hip/hip_runtime.h>
 
@@ -30,12 +42,21 @@
 
 namespace {
 
-constexpr int kThreads = 64;   // one wave per block
+constexpr int kThreads = 64;        // one wave per inject / fetch block
+constexpr int kInjectThreads = 1024;   // one inject block (16 waves) per CU: <= 128 VGPRs
+constexpr int kPlanThreads = 1024;
 
-struct InjectArgs {
+#define FS_GLOBAL __attribute__((address_space(1)))
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 ld_stream(const FS_GLOBAL u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st_stream(FS_GLOBAL u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+
+struct PlanArgs {
     const int32_t* user;
     const int32_t* ids;
     int32_t k;
+    int32_t batch;
     const int32_t* block_table;
     int32_t max_blocks;
     const int32_t* start_pos;
@@ -45,39 +66,39 @@ struct InjectArgs {
     const int32_t* fact_len;
     const int64_t* user_begin;
     int32_t num_users;
+    int32_t layer_begin, layer_end, heads;
+    const int32_t* stage_ids;       // non-null for pinned stores
+    const int32_t* stage_meta;
+    int32_t staging_layers, max_batch, max_k;
+    int32_t seg_tokens;
+    int64_t* tok_src;
+    int64_t* tok_dst;
+    int32_t* req_len;
     const double* inv_freq;
+    int32_t half_dim;
+    double2* req_base;              // (cos, sin) of start_pos * w_i per request
+    uint32_t* err;
+};
+
+struct InjectArgs {
+    int32_t batch;
+    const int32_t* start_pos;
+    const int64_t* tok_src;
+    const int64_t* tok_dst;
+    const int32_t* req_len;
+    int32_t seg_tokens;
+    const double* inv_freq;
+    const double2* rope_tab;        // [seg_tokens][D/2] (cos, sin) of t * w_i
+    const double2* req_base;        // [batch][D/2] (cos, sin) of start_pos * w_i
     int32_t heads;
-    int32_t layer_begin, layer_end, layers_per_block;
+    int32_t layer_begin, layer_end;
     const void* const* src_k;       // device table [num_layers] (device store)
     const void* const* src_v;
     const uint16_t* stage_k;        // non-null: read the staging ring instead
     const uint16_t* stage_v;
-    const int32_t* stage_ids;       // [staging_layers][max_batch][max_k]
-    const int32_t* stage_meta;      // [staging_layers][4]: k, batch, layer
-    int32_t staging_layers, stage_tokens, max_batch, max_k;
-    uint32_t* err;
+    int32_t staging_layers, stage_tokens, max_batch;
     void* kc[FS_MAX_LAYERS];
     void* vc[FS_MAX_LAYERS];
-};
-
-struct FetchArgs {
-    const int32_t* user;
-    const int32_t* ids;
-    int32_t k;
-    const int64_t* fact_begin;
-    const int32_t* fact_len;
-    const int64_t* user_begin;
-    int32_t num_users;
-    int32_t heads;
-    int32_t layer_begin, layer_end, layers_per_block;
-    const void* const* src_k;       // device table of device-visible host addresses
-    const void* const* src_v;
-    uint16_t* stage_k;
-    uint16_t* stage_v;
-    int32_t* stage_ids;
-    int32_t* stage_meta;
-    int32_t staging_layers, stage_tokens, max_batch, max_k, batch;
-    uint32_t* err;
 };
 
 __device__ __forceinline__ int wave_or(int v) {
@@ -113,24 +134,27 @@ __device__ uint32_t plan_request(const int32_t* user, const int32_t* ids, int k,
                                  const int64_t* user_begin, int num_users,
                                  const int32_t* fact_len, const int64_t* fact_begin, int b,
                                  int32_t* off, int64_t* row0, int* L_out, int* nf_out) {
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     uint32_t bits = 0;
     const int u = user[b];
     const bool bad_user = (u < 0 || u >= num_users);
     if (bad_user) bits |= FS_ERR_USER;
     const int64_t ub0 = bad_user ? 0 : user_begin[u];
     const int64_t ub1 = bad_user ? 0 : user_begin[u + 1];
+    // Lengths are counted only up to the first -1 pad, so every token t < L
+    // maps into a valid fact of the user even when the request is rejected
+    // (the kernels may read before the verdict is in, never out of bounds).
     int carry = 0, first_pad = k, last_real = -1;
     for (int c0 = 0; c0 < k; c0 += 64) {
         const int j = c0 + lane;
         int len = 0;
         int64_t r0 = 0;
+        const int id = j < k ? ids[int64_t(b) * k + j] : 0;
+        first_pad = wave_min(min(first_pad, (j < k && id < 0) ? j : k));
         if (j < k) {
-            const int id = ids[int64_t(b) * k + j];
-            if (id < 0) {
-                first_pad = min(first_pad, j);
+            if (id < 0 || j > first_pad) {
+                // pad, or an id after a pad (reported below)
             } else {
-                last_real = j;
                 if (bad_user) {
                     // reported once as FS_ERR_USER; ids cannot be judged
                 } else if (id < ub0 || id >= ub1) {
@@ -141,6 +165,7 @@ __device__ uint32_t plan_request(const int32_t* user, const int32_t* ids, int k,
                 }
             }
         }
+        if (j < k && id >= 0) last_real = j;
         const int incl = wave_incl_scan(len, lane);
         if (j < k) {
             off[j] = carry + incl - len;
@@ -148,7 +173,6 @@ __device__ uint32_t plan_request(const int32_t* user, const int32_t* ids, int k,
         }
         carry += __shfl(incl, 63, 64);
     }
-    first_pad = wave_min(first_pad);
     last_real = wave_max(last_real);
     if (last_real > first_pad) bits |= FS_ERR_FACT_ID;
     *L_out = carry;
@@ -201,47 +225,63 @@ __device__ __forceinline__ uint32_t rot_word(uint32_t wa, uint32_t wb, int e, co
     return f64_to_bf16_bits(y0) | (f64_to_bf16_bits(y1) << 16);
 }
 
-__device__ __forceinline__ void rotate16(const uint4& xa, const uint4& xb, const double* c,
-                                         const double* s, uint4& ya, uint4& yb) {
-    ya.x = rot_word(xa.x, xb.x, 0, c, s, &yb.x);
-    ya.y = rot_word(xa.y, xb.y, 1, c, s, &yb.y);
-    ya.z = rot_word(xa.z, xb.z, 2, c, s, &yb.z);
-    ya.w = rot_word(xa.w, xb.w, 3, c, s, &yb.w);
+struct FetchArgs {
+    const int32_t* user;
+    const int32_t* ids;
+    int32_t k;
+    const int64_t* fact_begin;
+    const int32_t* fact_len;
+    const int64_t* user_begin;
+    int32_t num_users;
+    int32_t heads;
+    int32_t layer_begin, layer_end, layers_per_block;
+    const void* const* src_k;       // device table of device-visible host addresses
+    const void* const* src_v;
+    uint16_t* stage_k;
+    uint16_t* stage_v;
+    int32_t* stage_ids;
+    int32_t* stage_meta;
+    int32_t staging_layers, stage_tokens, max_batch, max_k, batch;
+    uint32_t* err;
+};
+
+__device__ __forceinline__ void rot_v(const u32x4& xa, const u32x4& xb, const double* c,
+                                      const double* s, u32x4& ya, u32x4& yb) {
+    uint32_t b0, b1, b2, b3;
+    ya.x = rot_word(xa.x, xb.x, 0, c, s, &b0);
+    ya.y = rot_word(xa.y, xb.y, 1, c, s, &b1);
+    ya.z = rot_word(xa.z, xb.z, 2, c, s, &b2);
+    ya.w = rot_word(xa.w, xb.w, 3, c, s, &b3);
+    yb.x = b0;
+    yb.y = b1;
+    yb.z = b2;
+    yb.w = b3;
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void fs_inject_kernel(InjectArgs a) {
-    constexpr int kTeam = D / 16;            // lanes per token
-    constexpr int kTok = kThreads / kTeam;   // tokens per block
-    constexpr int kHalf = D / 16;            // uint4 per half head row
-    extern __shared__ int64_t plan_lds[];
-    int64_t* row0 = plan_lds;
-    int32_t* off = reinterpret_cast<int32_t*>(plan_lds + a.k);
-
-    const int b = blockIdx.y;
-    const int lane = threadIdx.x;
-    int L = 0, nf = 0;
-    uint32_t bits = plan_request(a.user, a.ids, a.k, a.user_begin, a.num_users, a.fact_len,
-                                 a.fact_begin, b, off, row0, &L, &nf);
+// Validation of one planned request, shared by the plan kernel and the
+// single-request inject path: start position, block-table coverage and
+// entries, and for pinned stores that every staging slot holds these ids.
+__device__ uint32_t check_request(const PlanArgs& a, int b, int L) {
+    const int lane = threadIdx.x & 63;
+    uint32_t bits = 0;
     const int s = a.start_pos[b];
-    if (s < 0 || int64_t(s) + L > int64_t(INT32_MAX)) bits |= FS_ERR_START_POS;
-    const int bs_mask = (1 << a.log2_block) - 1;
-    if (!(bits & FS_ERR_START_POS) && L > 0) {
+    const int32_t* bt = a.block_table + int64_t(b) * a.max_blocks;
+    if (s < 0 || int64_t(s) + L > int64_t(INT32_MAX)) {
+        bits |= FS_ERR_START_POS;
+    } else if (L > 0) {
         const int first = s >> a.log2_block;
         const int last = (s + L - 1) >> a.log2_block;
         if (last >= a.max_blocks) {
             bits |= FS_ERR_BLOCK_SHORT;
         } else {
-            const int32_t* bt = a.block_table + int64_t(b) * a.max_blocks;
             for (int j = first + lane; j <= last; j += 64) {
                 const int e = bt[j];
                 if (e < 0 || e >= a.num_blocks) bits |= FS_ERR_BLOCK_ID;
             }
         }
     }
-    if (a.stage_k) {
-        for (int l = a.layer_begin + blockIdx.z * a.layers_per_block;
-             l < min(a.layer_end, a.layer_begin + (int(blockIdx.z) + 1) * a.layers_per_block); ++l) {
+    if (a.stage_ids) {
+        for (int l = a.layer_begin; l < a.layer_end; ++l) {
             const int slot = l % a.staging_layers;
             const int32_t* meta = a.stage_meta + 4 * slot;
             if (meta[0] != a.k || meta[1] <= b || meta[2] != l) {
@@ -253,74 +293,218 @@ __global__ __launch_bounds__(kThreads) void fs_inject_kernel(InjectArgs a) {
             }
         }
     }
-    bits = wave_or(bits);
-    if (bits) {
-        if (lane == 0 && blockIdx.x == 0 && blockIdx.z == 0) atomicOr(a.err, bits);
-        return;
-    }
-    __syncthreads();   // plan in LDS visible to every lane
+    return bits;
+}
 
+// Batches: one block per request.  Wave 0 plans into LDS, then the whole
+// block writes the token map; a rejected request gets length 0.
+__global__ __launch_bounds__(kPlanThreads) void fs_plan_kernel(PlanArgs a) {
+    extern __shared__ int64_t plan_lds[];
+    __shared__ int s_len, s_nf;
+    int64_t* row0 = plan_lds;
+    int32_t* off = reinterpret_cast<int32_t*>(plan_lds + a.k);
+    const int b = blockIdx.x;
+    if (threadIdx.x < 64) {
+        int L = 0, nf = 0;
+        uint32_t bits = plan_request(a.user, a.ids, a.k, a.user_begin, a.num_users, a.fact_len,
+                                     a.fact_begin, b, off, row0, &L, &nf);
+        bits |= check_request(a, b, L);
+        bits = wave_or(bits);
+        if (threadIdx.x == 0) {
+            if (bits) atomicOr(a.err, bits);
+            s_len = bits ? 0 : L;
+            s_nf = nf;
+            a.req_len[b] = bits ? 0 : L;
+        }
+    }
+    __syncthreads();
+    const int L = s_len, nf = s_nf;
+    const int s = a.start_pos[b];
+    const int32_t* bt = a.block_table + int64_t(b) * a.max_blocks;
+    const int bs_mask = (1 << a.log2_block) - 1;
+    int64_t* src = a.tok_src + int64_t(b) * a.seg_tokens;
+    int64_t* dst = a.tok_dst + int64_t(b) * a.seg_tokens;
+    for (int t = threadIdx.x; t < L; t += blockDim.x) {
+        const int j = find_fact(off, nf, t);
+        src[t] = row0[j] + (t - off[j]);
+        const int p = s + t;
+        dst[t] = (int64_t(bt[p >> a.log2_block]) << a.log2_block) | (p & bs_mask);
+    }
+    if (L > 0 && threadIdx.x < a.half_dim) {
+        double sv, cv;
+        sincos(static_cast<double>(s) * a.inv_freq[threadIdx.x], &sv, &cv);
+        a.req_base[int64_t(b) * a.half_dim + threadIdx.x] = make_double2(cv, sv);
+    }
+}
+
+// (cos, sin) of t * w_i for every segment offset t: the per-token factor of
+// the angle-addition form cos((s+t)w) = cos(sw)cos(tw) - sin(sw)sin(tw)
+__global__ void fs_rope_table_kernel(double2* tab, const double* inv_freq, int half, int64_t n) {
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= n) return;
+    const int64_t t = idx / half;
+    const int i = static_cast<int>(idx - t * half);
+    double sv, cv;
+    sincos(static_cast<double>(t) * inv_freq[i], &sv, &cv);
+    tab[idx] = make_double2(cv, sv);
+}
+
+// One 1024-thread block (16 waves) per compute unit.  The block owns an equal
+// contiguous share of the units; its waves take units one at a time from an
+// LDS counter, so the waves the CU favours do more of the share.
+template <int D, bool kSingle>
+__global__ __launch_bounds__(kInjectThreads) void fs_inject_kernel(InjectArgs a, PlanArgs pa) {
+    constexpr int kTeam = D / 16;            // lanes per token
+    constexpr int kTok = 64 / kTeam;         // tokens per unit
+    constexpr int kHalf = D / 16;            // 16-byte vectors per half head row
+    extern __shared__ int64_t plan_lds[];
+    __shared__ int s_L, s_nf, s_bits;
+    __shared__ unsigned s_next;
+    __shared__ double2 s_base[128];      // kSingle: (cos, sin) of start_pos * w_i
+    const int lane = threadIdx.x & 63;
     const int team = lane / kTeam;
     const int tl = lane % kTeam;
-    const int t = blockIdx.x * kTok + team;
-    if (t >= L) return;
-    const int j = find_fact(off, nf, t);
-    const int64_t row = row0[j] + (t - off[j]);
-    const int p = s + t;
-    const int blk = a.block_table[int64_t(b) * a.max_blocks + (p >> a.log2_block)];
-    const int64_t dst_row = (int64_t(blk) << a.log2_block) | (p & bs_mask);
-
-    double c[8], sn[8];
-    const double pd = static_cast<double>(p);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sincos(pd * a.inv_freq[8 * tl + e], &sn[e], &c[e]);
-
     const int H = a.heads;
+    const int per_group = (a.layer_end - a.layer_begin) * H;
     const int64_t row_elems = int64_t(H) * D;
-    const int l0 = a.layer_begin + blockIdx.z * a.layers_per_block;
-    const int l1 = min(a.layer_end, l0 + a.layers_per_block);
-    for (int l = l0; l < l1; ++l) {
-        const uint4* ks;
-        const uint4* vs;
-        if (a.stage_k) {
-            const int64_t srow = (int64_t(l % a.staging_layers) * a.max_batch + b) * a.stage_tokens + t;
-            ks = reinterpret_cast<const uint4*>(a.stage_k + srow * row_elems);
-            vs = reinterpret_cast<const uint4*>(a.stage_v + srow * row_elems);
-        } else {
-            ks = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.src_k[l]) + row * row_elems);
-            vs = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.src_v[l]) + row * row_elems);
+    int64_t* row0 = plan_lds;
+    int32_t* off = reinterpret_cast<int32_t*>(plan_lds + pa.k);
+
+    if (threadIdx.x < 64) {
+        if (kSingle) {
+            // one request: each block plans it (the same answer everywhere),
+            // so there is no second launch and no scratch round trip
+            int L = 0, nf = 0;
+            uint32_t bits = plan_request(pa.user, pa.ids, pa.k, pa.user_begin, pa.num_users,
+                                         pa.fact_len, pa.fact_begin, 0, off, row0, &L, &nf);
+            bits |= check_request(pa, 0, L);
+            bits = wave_or(bits);
+            if (lane == 0) {
+                s_L = L;
+                s_nf = nf;
+                s_bits = bits;
+                if (bits && blockIdx.x == 0) atomicOr(pa.err, bits);
+            }
+        } else if (lane == 0) {
+            s_bits = 0;
         }
-        uint4* kd = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.kc[l]) + dst_row * row_elems);
-        uint4* vd = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.vc[l]) + dst_row * row_elems);
-        int h = 0;
-        for (; h + 2 <= H; h += 2) {
-            const int o0 = h * (D / 8) + tl, o1 = o0 + D / 8;
-            const uint4 xa0 = ks[o0], xb0 = ks[o0 + kHalf];
-            const uint4 xa1 = ks[o1], xb1 = ks[o1 + kHalf];
-            const uint4 va0 = vs[o0], vb0 = vs[o0 + kHalf];
-            const uint4 va1 = vs[o1], vb1 = vs[o1 + kHalf];
-            uint4 ya0, yb0, ya1, yb1;
-            rotate16(xa0, xb0, c, sn, ya0, yb0);
-            rotate16(xa1, xb1, c, sn, ya1, yb1);
-            kd[o0] = ya0;
-            kd[o0 + kHalf] = yb0;
-            kd[o1] = ya1;
-            kd[o1 + kHalf] = yb1;
-            vd[o0] = va0;
-            vd[o0 + kHalf] = vb0;
-            vd[o1] = va1;
-            vd[o1 + kHalf] = vb1;
+        if (lane == 0) s_next = 0;
+    } else if (kSingle && threadIdx.x - 64 < unsigned(D / 2)) {
+        // the second wave meanwhile prepares the request's angle base
+        const int i = threadIdx.x - 64;
+        double sv, cv;
+        sincos(static_cast<double>(a.start_pos[0]) * a.inv_freq[i], &sv, &cv);
+        s_base[i] = make_double2(cv, sv);
+    }
+    __syncthreads();
+    if (s_bits) return;
+
+    int64_t total = 0;
+    const int L0 = kSingle ? s_L : 0;
+    const int nf0 = kSingle ? s_nf : 0;
+    if (kSingle) {
+        total = int64_t((L0 + kTok - 1) / kTok) * per_group;
+    } else {
+        for (int c0 = 0; c0 < a.batch; c0 += 64) {
+            const int bb = c0 + lane;
+            int64_t units = bb < a.batch ? int64_t((a.req_len[bb] + kTok - 1) / kTok) * per_group : 0;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) units += __shfl_xor(units, o, 64);
+            total += units;
         }
-        for (; h < H; ++h) {
-            const int o0 = h * (D / 8) + tl;
-            const uint4 xa0 = ks[o0], xb0 = ks[o0 + kHalf];
-            const uint4 va0 = vs[o0], vb0 = vs[o0 + kHalf];
-            uint4 ya0, yb0;
-            rotate16(xa0, xb0, c, sn, ya0, yb0);
-            kd[o0] = ya0;
-            kd[o0 + kHalf] = yb0;
-            vd[o0] = va0;
-            vd[o0 + kHalf] = vb0;
+    }
+    const int64_t G = gridDim.x;
+    const int64_t blk_lo = total * int64_t(blockIdx.x) / G;
+    const int64_t blk_n = total * (int64_t(blockIdx.x) + 1) / G - blk_lo;
+    if (blk_n <= 0) return;
+
+    // request of the wave's current unit and that request's unit range
+    auto units_of = [&](int bb) -> int64_t {
+        return int64_t((a.req_len[bb] + kTok - 1) / kTok) * per_group;
+    };
+    int b = 0;
+    int64_t req_lo = 0, req_hi = kSingle ? total : units_of(0);
+    int cur_b = -1, cur_g = -1;
+    bool act = false;
+    int t = 0;
+    int64_t src_row = 0, dst_row = 0;
+    double c[8], sn[8];
+
+    for (;;) {
+        unsigned i = 0;
+        if (lane == 0) i = atomicAdd(&s_next, 1u);
+        i = __shfl(i, 0, 64);
+        if (int64_t(i) >= blk_n) break;
+        const int64_t u = blk_lo + i;
+        if (!kSingle) {
+            while (u >= req_hi) {        // a wave's units only move forward
+                ++b;
+                req_lo = req_hi;
+                req_hi = req_lo + units_of(b);
+            }
+        }
+        const int64_t r = u - req_lo;
+        const int g = static_cast<int>(r / per_group);
+        const int lh = static_cast<int>(r - int64_t(g) * per_group);
+
+        if (b != cur_b || g != cur_g) {
+            cur_b = b;
+            cur_g = g;
+            t = g * kTok + team;
+            if (kSingle) {
+                act = t < L0;
+                if (act) {
+                    const int j = find_fact(off, nf0, t);
+                    src_row = row0[j] + (t - off[j]);
+                    const int p = a.start_pos[0] + t;
+                    const int blk = pa.block_table[p >> pa.log2_block];
+                    dst_row = (int64_t(blk) << pa.log2_block) | (p & ((1 << pa.log2_block) - 1));
+                }
+            } else {
+                act = t < a.req_len[b];
+                if (act) {
+                    src_row = a.tok_src[int64_t(b) * a.seg_tokens + t];
+                    dst_row = a.tok_dst[int64_t(b) * a.seg_tokens + t];
+                }
+            }
+            if (act) {
+                // angle (s + t) * w_i by angle addition from the request's
+                // base (s * w_i) and the tabulated t * w_i, all in fp64
+                const double2* tb = a.rope_tab + int64_t(t) * (D / 2) + 8 * tl;
+                const double2* bb = kSingle ? &s_base[8 * tl] : a.req_base + int64_t(b) * (D / 2) + 8 * tl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const double2 tv = tb[e];
+                    const double2 bv = bb[e];
+                    c[e] = fma(bv.x, tv.x, -(bv.y * tv.y));
+                    sn[e] = fma(bv.y, tv.x, bv.x * tv.y);
+                }
+            }
+        }
+        if (act) {
+            const int l = a.layer_begin + lh / H;
+            const int h = lh - (lh / H) * H;
+            const FS_GLOBAL u32x4* ks;
+            const FS_GLOBAL u32x4* vs;
+            if (a.stage_k) {
+                const int64_t srow = (int64_t(l % a.staging_layers) * a.max_batch + b) * a.stage_tokens + t;
+                ks = (const FS_GLOBAL u32x4*)(a.stage_k + srow * row_elems + h * D);
+                vs = (const FS_GLOBAL u32x4*)(a.stage_v + srow * row_elems + h * D);
+            } else {
+                ks = (const FS_GLOBAL u32x4*)(static_cast<const uint16_t*>(a.src_k[l]) + src_row * row_elems + h * D);
+                vs = (const FS_GLOBAL u32x4*)(static_cast<const uint16_t*>(a.src_v[l]) + src_row * row_elems + h * D);
+            }
+            const u32x4 ka = ld_stream(ks + tl), kb = ld_stream(ks + tl + kHalf);
+            const u32x4 va = ld_stream(vs + tl), vb = ld_stream(vs + tl + kHalf);
+            const int64_t o = dst_row * row_elems + h * D;
+            FS_GLOBAL u32x4* kd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.kc[l]) + o);
+            FS_GLOBAL u32x4* vd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.vc[l]) + o);
+            u32x4 ya, yb;
+            rot_v(ka, kb, c, sn, ya, yb);
+            st_stream(kd + tl, ya);
+            st_stream(kd + tl + kHalf, yb);
+            st_stream(vd + tl, va);
+            st_stream(vd + tl + kHalf, vb);
         }
     }
 }
@@ -403,20 +587,51 @@ template <int D>
 hipError_t launch_inject(const InjectLaunch& r) {
     const fs_store* st = r.st;
     const fs_store_desc& d = st->desc;
+
+    PlanArgs pa{};
+    pa.user = r.user;
+    pa.ids = r.ids;
+    pa.k = r.k;
+    pa.batch = r.batch;
+    pa.block_table = r.block_table;
+    pa.max_blocks = r.max_blocks;
+    pa.start_pos = r.start_pos;
+    pa.num_blocks = r.num_blocks;
+    pa.log2_block = st->log2_block;
+    pa.fact_begin = st->d_fact_begin;
+    pa.fact_len = st->d_fact_len;
+    pa.user_begin = st->d_user_begin;
+    pa.num_users = d.num_users;
+    pa.layer_begin = r.layer_begin;
+    pa.layer_end = r.layer_end;
+    pa.heads = d.num_kv_heads;
+    if (d.kv_location == FS_KV_PINNED_HOST) {
+        pa.stage_ids = st->d_stage_ids;
+        pa.stage_meta = st->d_stage_meta;
+        pa.staging_layers = d.staging_layers;
+    }
+    pa.max_batch = d.max_batch;
+    pa.max_k = d.max_k;
+    pa.seg_tokens = st->seg_tokens;
+    pa.tok_src = st->d_tok_src;
+    pa.tok_dst = st->d_tok_dst;
+    pa.req_len = st->d_req_len;
+    pa.inv_freq = st->d_inv_freq;
+    pa.half_dim = d.head_dim / 2;
+    pa.req_base = st->d_req_base;
+    pa.err = st->d_err;
+    const size_t plan_lds = sizeof(int64_t) * (size_t(r.k) + (size_t(r.k) + 2) / 2);
+
     InjectArgs a{};
-    a.user = r.user;
-    a.ids = r.ids;
-    a.k = r.k;
-    a.block_table = r.block_table;
-    a.max_blocks = r.max_blocks;
+    a.batch = r.batch;
     a.start_pos = r.start_pos;
-    a.num_blocks = r.num_blocks;
-    a.log2_block = st->log2_block;
-    a.fact_begin = st->d_fact_begin;
-    a.fact_len = st->d_fact_len;
-    a.user_begin = st->d_user_begin;
-    a.num_users = d.num_users;
+    a.tok_src = st->d_tok_src;
+    a.tok_dst = st->d_tok_dst;
+    a.req_len = st->d_req_len;
+    a.seg_tokens = st->seg_tokens;
     a.inv_freq = st->d_inv_freq;
+    a.rope_tab = st->d_rope_tab;
+    a.req_base = st->d_req_base;
     a.heads = d.num_kv_heads;
     a.layer_begin = r.layer_begin;
     a.layer_end = r.layer_end;
@@ -425,26 +640,23 @@ hipError_t launch_inject(const InjectLaunch& r) {
     if (d.kv_location == FS_KV_PINNED_HOST) {
         a.stage_k = static_cast<const uint16_t*>(st->d_stage_k);
         a.stage_v = static_cast<const uint16_t*>(st->d_stage_v);
-        a.stage_ids = st->d_stage_ids;
-        a.stage_meta = st->d_stage_meta;
         a.staging_layers = d.staging_layers;
         a.stage_tokens = st->stage_tokens;
     }
     a.max_batch = d.max_batch;
-    a.max_k = d.max_k;
-    a.err = st->d_err;
     for (int l = 0; l < d.num_layers; ++l) {
         a.kc[l] = r.k_cache[l];
         a.vc[l] = r.v_cache[l];
     }
-    constexpr int kTok = kThreads / (D / 16);
-    const int64_t max_tokens = int64_t(r.k) * st->max_fact_len;
-    const int64_t tiles = (max_tokens + kTok - 1) / kTok;
-    const int nl = r.layer_end - r.layer_begin;
-    a.layers_per_block = layers_per_block(nl, tiles * r.batch);
-    dim3 grid(static_cast<unsigned>(tiles), r.batch, (nl + a.layers_per_block - 1) / a.layers_per_block);
-    size_t lds = sizeof(int64_t) * r.k + sizeof(int32_t) * (r.k + 1);
-    fs_inject_kernel<D><<<grid, kThreads, lds, r.stream>>>(a);
+    const dim3 grid(st->num_cus);
+    if (r.batch == 1) {
+        fs_inject_kernel<D, true><<<grid, kInjectThreads, plan_lds, r.stream>>>(a, pa);
+        return hipGetLastError();
+    }
+    fs_plan_kernel<<<dim3(r.batch), kPlanThreads, plan_lds, r.stream>>>(pa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    fs_inject_kernel<D, false><<<grid, kInjectThreads, 0, r.stream>>>(a, pa);
     return hipGetLastError();
 }
 
@@ -495,6 +707,15 @@ hipError_t fsi_launch_inject(const InjectLaunch& r) {
         case 256: return launch_inject<256>(r);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t fsi_init_rope_table(const fs_store* st, hipStream_t stream) {
+    const int half = st->desc.head_dim / 2;
+    const int64_t n = int64_t(st->seg_tokens) * half;
+    if (n == 0) return hipSuccess;
+    fs_rope_table_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), 256, 0, stream>>>(
+        st->d_rope_tab, st->d_inv_freq, half, n);
+    return hipGetLastError();
 }
 
 hipError_t fsi_launch_fetch(const FetchLaunch& r) {

@@ -212,23 +212,42 @@ def fs_retrieve_topk(store, batch: int, user: torch.Tensor, query: torch.Tensor,
     _check(st, "fs_retrieve_topk")
 
 
+class CacheTable:
+    """Marshalled per-layer cache pointers for fs_inject: validated once
+    (dtype, device, contiguity, shape [num_blocks, block_size, heads,
+    head_dim]) so repeated calls pay no per-layer checks.  Entries may be None
+    for layers that are never written."""
+
+    def __init__(self, store, k_cache: Sequence[Optional[torch.Tensor]],
+                 v_cache: Sequence[Optional[torch.Tensor]], num_blocks: int):
+        d = store.desc if isinstance(store, Store) else None
+        n = len(k_cache)
+        if len(v_cache) != n or (d is not None and n != d.num_layers):
+            raise ValueError("k_cache / v_cache need one entry per layer (None allowed)")
+        if d is not None:
+            cshape = (num_blocks, d.block_size, d.num_kv_heads, d.head_dim)
+            for l in range(n):
+                for nm, t in (("k_cache", k_cache[l]), ("v_cache", v_cache[l])):
+                    if t is not None:
+                        _ptr(t, torch.bfloat16, shape=cshape, name=f"{nm}[{l}]")
+        self.num_blocks = int(num_blocks)
+        self.present = [k_cache[l] is not None and v_cache[l] is not None for l in range(n)]
+        self.k = (ctypes.c_void_p * n)(*[0 if t is None else t.data_ptr() for t in k_cache])
+        self.v = (ctypes.c_void_p * n)(*[0 if t is None else t.data_ptr() for t in v_cache])
+        self._refs = (list(k_cache), list(v_cache))
+
+
 def fs_inject(store, layer: int, batch: int, user: torch.Tensor, ids: torch.Tensor, k: int,
               block_table: torch.Tensor, max_blocks: int, start_pos: torch.Tensor,
-              k_cache: Sequence[Optional[torch.Tensor]], v_cache: Sequence[Optional[torch.Tensor]],
-              num_blocks: int, stream=None) -> None:
-    d = store.desc if isinstance(store, Store) else None
-    if d is not None:
-        if len(k_cache) != d.num_layers or len(v_cache) != d.num_layers:
-            raise ValueError("k_cache / v_cache need one entry per layer (None allowed)")
-        cshape = (num_blocks, d.block_size, d.num_kv_heads, d.head_dim)
-        lay = range(d.num_layers) if layer == FS_ALL_LAYERS else [layer]
-        for l in lay:
-            if 0 <= l < d.num_layers:
-                _ptr(k_cache[l], torch.bfloat16, shape=cshape, name=f"k_cache[{l}]")
-                _ptr(v_cache[l], torch.bfloat16, shape=cshape, name=f"v_cache[{l}]")
-    n = len(k_cache)
-    karr = (ctypes.c_void_p * n)(*[0 if t is None else t.data_ptr() for t in k_cache])
-    varr = (ctypes.c_void_p * n)(*[0 if t is None else t.data_ptr() for t in v_cache])
+              k_cache, v_cache=None, num_blocks: Optional[int] = None, stream=None) -> None:
+    """k_cache: a CacheTable (then v_cache/num_blocks come from it), or
+    per-layer lists of tensors plus num_blocks."""
+    table = k_cache if isinstance(k_cache, CacheTable) else CacheTable(store, k_cache, v_cache, num_blocks)
+    if layer == FS_ALL_LAYERS:
+        if not all(table.present):
+            raise ValueError("FS_ALL_LAYERS needs a cache for every layer")
+    elif 0 <= layer < len(table.present) and not table.present[layer]:
+        raise ValueError(f"no cache given for layer {layer}")
     st = _lib.fs_inject(
         _handle(store), int(layer), int(batch),
         _ptr(user, torch.int32, shape=(batch,), name="user"),
@@ -236,7 +255,7 @@ def fs_inject(store, layer: int, batch: int, user: torch.Tensor, ids: torch.Tens
         _ptr(block_table, torch.int32, shape=(batch, max_blocks), name="block_table"),
         int(max_blocks),
         _ptr(start_pos, torch.int32, shape=(batch,), name="start_pos"),
-        karr, varr, int(num_blocks), _stream(stream))
+        table.k, table.v, table.num_blocks, _stream(stream))
     _check(st, "fs_inject")
 
 
