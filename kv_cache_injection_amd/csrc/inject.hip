@@ -43,7 +43,14 @@
 namespace {
 
 constexpr int kThreads = 64;        // one wave per inject / fetch block
-constexpr int kInjectThreads = 1024;   // one inject block (16 waves) per CU: <= 128 VGPRs
+#ifndef FS_INJ_THREADS
+#define FS_INJ_THREADS 1024
+#endif
+#ifndef FS_INJ_UNITS
+#define FS_INJ_UNITS 2
+#endif
+constexpr int kInjectThreads = FS_INJ_THREADS;   // one inject block per CU
+constexpr int kGrab = FS_INJ_UNITS;              // units taken (and in flight) per grab
 constexpr int kPlanThreads = 1024;
 
 #define FS_GLOBAL __attribute__((address_space(1)))
@@ -359,7 +366,7 @@ __global__ __launch_bounds__(kInjectThreads) void fs_inject_kernel(InjectArgs a,
     constexpr int kHalf = D / 16;            // 16-byte vectors per half head row
     extern __shared__ int64_t plan_lds[];
     __shared__ int s_L, s_nf, s_bits;
-    __shared__ unsigned s_next;
+    __shared__ unsigned s_next;          // block queue over the block's share
     __shared__ double2 s_base[128];      // kSingle: (cos, sin) of start_pos * w_i
     const int lane = threadIdx.x & 63;
     const int team = lane / kTeam;
@@ -413,10 +420,10 @@ __global__ __launch_bounds__(kInjectThreads) void fs_inject_kernel(InjectArgs a,
             total += units;
         }
     }
+    // the units are split evenly over the blocks (one block per CU)
     const int64_t G = gridDim.x;
     const int64_t blk_lo = total * int64_t(blockIdx.x) / G;
     const int64_t blk_n = total * (int64_t(blockIdx.x) + 1) / G - blk_lo;
-    if (blk_n <= 0) return;
 
     // request of the wave's current unit and that request's unit range
     auto units_of = [&](int bb) -> int64_t {
@@ -430,12 +437,10 @@ __global__ __launch_bounds__(kInjectThreads) void fs_inject_kernel(InjectArgs a,
     int64_t src_row = 0, dst_row = 0;
     double c[8], sn[8];
 
-    for (;;) {
-        unsigned i = 0;
-        if (lane == 0) i = atomicAdd(&s_next, 1u);
-        i = __shfl(i, 0, 64);
-        if (int64_t(i) >= blk_n) break;
-        const int64_t u = blk_lo + i;
+    // units [u, u_stop): every one is processed; a range crossing a
+    // token-group or request boundary is done in several passes
+    auto run = [&](int64_t u, const int64_t u_stop) {
+      while (u < u_stop) {
         if (!kSingle) {
             while (u >= req_hi) {        // a wave's units only move forward
                 ++b;
@@ -445,7 +450,11 @@ __global__ __launch_bounds__(kInjectThreads) void fs_inject_kernel(InjectArgs a,
         }
         const int64_t r = u - req_lo;
         const int g = static_cast<int>(r / per_group);
-        const int lh = static_cast<int>(r - int64_t(g) * per_group);
+        const int lh0 = static_cast<int>(r - int64_t(g) * per_group);
+        int n = kGrab;
+        if (int64_t(n) > u_stop - u) n = static_cast<int>(u_stop - u);
+        if (n > per_group - lh0) n = per_group - lh0;
+        if (!kSingle && int64_t(n) > req_hi - u) n = static_cast<int>(req_hi - u);
 
         if (b != cur_b || g != cur_g) {
             cur_b = b;
@@ -482,30 +491,57 @@ __global__ __launch_bounds__(kInjectThreads) void fs_inject_kernel(InjectArgs a,
             }
         }
         if (act) {
-            const int l = a.layer_begin + lh / H;
-            const int h = lh - (lh / H) * H;
-            const FS_GLOBAL u32x4* ks;
-            const FS_GLOBAL u32x4* vs;
-            if (a.stage_k) {
-                const int64_t srow = (int64_t(l % a.staging_layers) * a.max_batch + b) * a.stage_tokens + t;
-                ks = (const FS_GLOBAL u32x4*)(a.stage_k + srow * row_elems + h * D);
-                vs = (const FS_GLOBAL u32x4*)(a.stage_v + srow * row_elems + h * D);
-            } else {
-                ks = (const FS_GLOBAL u32x4*)(static_cast<const uint16_t*>(a.src_k[l]) + src_row * row_elems + h * D);
-                vs = (const FS_GLOBAL u32x4*)(static_cast<const uint16_t*>(a.src_v[l]) + src_row * row_elems + h * D);
+            u32x4 ka[kGrab], kb[kGrab], va[kGrab], vb[kGrab];
+#pragma unroll
+            for (int q = 0; q < kGrab; ++q) {
+                if (q < n) {
+                    const int lh = lh0 + q;
+                    const int l = a.layer_begin + lh / H;
+                    const int h = lh - (lh / H) * H;
+                    const FS_GLOBAL u32x4* ks;
+                    const FS_GLOBAL u32x4* vs;
+                    if (a.stage_k) {
+                        const int64_t srow = (int64_t(l % a.staging_layers) * a.max_batch + b) * a.stage_tokens + t;
+                        ks = (const FS_GLOBAL u32x4*)(a.stage_k + srow * row_elems + h * D);
+                        vs = (const FS_GLOBAL u32x4*)(a.stage_v + srow * row_elems + h * D);
+                    } else {
+                        ks = (const FS_GLOBAL u32x4*)(static_cast<const uint16_t*>(a.src_k[l]) + src_row * row_elems + h * D);
+                        vs = (const FS_GLOBAL u32x4*)(static_cast<const uint16_t*>(a.src_v[l]) + src_row * row_elems + h * D);
+                    }
+                    ka[q] = ld_stream(ks + tl);
+                    kb[q] = ld_stream(ks + tl + kHalf);
+                    va[q] = ld_stream(vs + tl);
+                    vb[q] = ld_stream(vs + tl + kHalf);
+                }
             }
-            const u32x4 ka = ld_stream(ks + tl), kb = ld_stream(ks + tl + kHalf);
-            const u32x4 va = ld_stream(vs + tl), vb = ld_stream(vs + tl + kHalf);
-            const int64_t o = dst_row * row_elems + h * D;
-            FS_GLOBAL u32x4* kd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.kc[l]) + o);
-            FS_GLOBAL u32x4* vd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.vc[l]) + o);
-            u32x4 ya, yb;
-            rot_v(ka, kb, c, sn, ya, yb);
-            st_stream(kd + tl, ya);
-            st_stream(kd + tl + kHalf, yb);
-            st_stream(vd + tl, va);
-            st_stream(vd + tl + kHalf, vb);
+#pragma unroll
+            for (int q = 0; q < kGrab; ++q) {
+                if (q < n) {
+                    const int lh = lh0 + q;
+                    const int l = a.layer_begin + lh / H;
+                    const int h = lh - (lh / H) * H;
+                    const int64_t o = dst_row * row_elems + h * D;
+                    FS_GLOBAL u32x4* kd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.kc[l]) + o);
+                    FS_GLOBAL u32x4* vd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.vc[l]) + o);
+                    u32x4 ya, yb;
+                    rot_v(ka[q], kb[q], c, sn, ya, yb);
+                    st_stream(kd + tl, ya);
+                    st_stream(kd + tl + kHalf, yb);
+                    st_stream(vd + tl, va[q]);
+                    st_stream(vd + tl + kHalf, vb[q]);
+                }
+            }
         }
+        u += n;
+      }
+    };
+
+    for (;;) {
+        unsigned i = 0;
+        if (lane == 0) i = atomicAdd(&s_next, unsigned(kGrab));
+        i = __shfl(i, 0, 64);
+        if (int64_t(i) >= blk_n) break;
+        run(blk_lo + i, blk_lo + (int64_t(i) + kGrab < blk_n ? int64_t(i) + kGrab : blk_n));
     }
 }
 

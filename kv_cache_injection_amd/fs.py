@@ -278,6 +278,53 @@ def fs_poll_errors(store, stream=None) -> int:
     return int(flags.value)
 
 
+class Prepared:
+    """A call with its arguments marshalled once (validated like the plain
+    call) for repeated launches on the same buffers: calling it only passes
+    the cached ctypes values to the library (host cost of one foreign call)."""
+
+    def __init__(self, fn, args, where, refs):
+        self._fn = fn
+        self._args = args
+        self._where = where
+        self._refs = refs
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != FS_OK:
+            _check(st, self._where)
+
+
+def prepare_retrieve_topk(store, batch: int, user, query, k: int, ids, scores=None,
+                          num_tokens=None, stream=None) -> Prepared:
+    d = store.desc if isinstance(store, Store) else None
+    E = d.embed_dim if d is not None else query.shape[-1]
+    args = (_handle(store), int(batch),
+            _ptr(user, torch.int32, shape=(batch,), name="user"),
+            _ptr(query, torch.float32, shape=(batch, E), name="query"), int(k),
+            _ptr(ids, torch.int32, shape=(batch, k), name="ids"),
+            _ptr(scores, torch.float64, shape=(batch, k), name="scores"),
+            _ptr(num_tokens, torch.int32, shape=(batch,), name="num_tokens"),
+            _stream(stream))
+    return Prepared(_lib.fs_retrieve_topk, args, "fs_retrieve_topk",
+                    (store, user, query, ids, scores, num_tokens))
+
+
+def prepare_inject(store, layer: int, batch: int, user, ids, k: int, block_table,
+                   max_blocks: int, start_pos, caches: "CacheTable", stream=None) -> Prepared:
+    if not isinstance(caches, CacheTable):
+        raise TypeError("prepare_inject takes a CacheTable")
+    args = (_handle(store), int(layer), int(batch),
+            _ptr(user, torch.int32, shape=(batch,), name="user"),
+            _ptr(ids, torch.int32, shape=(batch, k), name="ids"), int(k),
+            _ptr(block_table, torch.int32, shape=(batch, max_blocks), name="block_table"),
+            int(max_blocks),
+            _ptr(start_pos, torch.int32, shape=(batch,), name="start_pos"),
+            caches.k, caches.v, caches.num_blocks, _stream(stream))
+    return Prepared(_lib.fs_inject, args, "fs_inject",
+                    (store, user, ids, block_table, start_pos, caches))
+
+
 def make_desc(**kw) -> fs_store_desc:
     d = fs_store_desc()
     d.staging_layers = 0
