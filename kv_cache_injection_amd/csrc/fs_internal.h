@@ -35,7 +35,6 @@ struct fs_store {
     int32_t* d_fact_len = nullptr;     // [F]
     int64_t* d_user_begin = nullptr;   // [U+1]
     double* d_inv_freq = nullptr;      // [head_dim/2] theta^(-2i/D)
-    double2* d_rope_tab = nullptr;     // [seg_tokens][head_dim/2] (cos, sin) of t * w_i
     uint32_t* d_err = nullptr;         // device error word
     double* d_scores = nullptr;        // [max_batch][max_user_facts] score scratch
     const void** d_src_k = nullptr;    // [L] device-visible arena pointers
@@ -44,7 +43,6 @@ struct fs_store {
     int64_t* d_tok_src = nullptr;      // [max_batch][seg_tokens] arena row of segment token t
     int64_t* d_tok_dst = nullptr;      // [max_batch][seg_tokens] cache slot (block*bs + slot)
     int32_t* d_req_len = nullptr;      // [max_batch] segment length, 0 if rejected
-    double2* d_req_base = nullptr;     // [max_batch][head_dim/2] (cos, sin) of start_pos * w_i
 
     // pinned stores: staging ring
     int32_t stage_tokens = 0;          // max_k * max_fact_len
@@ -89,8 +87,6 @@ struct InjectLaunch {
     hipStream_t stream;
 };
 hipError_t fsi_launch_inject(const InjectLaunch& a);
-// fills d_rope_tab (store creation)
-hipError_t fsi_init_rope_table(const fs_store* st, hipStream_t stream);
 
 struct FetchLaunch {
     const fs_store* st;

@@ -44,7 +44,7 @@ void free_store(fs_store* s) {
     if (!s) return;
     void* bufs[] = {s->d_fact_begin, s->d_fact_len, s->d_user_begin, s->d_inv_freq, s->d_err,
                     s->d_scores, (void*)s->d_src_k, (void*)s->d_src_v, s->d_tok_src,
-                    s->d_tok_dst, s->d_req_len, s->d_rope_tab, s->d_req_base, s->d_stage_k,
+                    s->d_tok_dst, s->d_req_len, s->d_stage_k,
                     s->d_stage_v, s->d_stage_ids, s->d_stage_meta};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
@@ -207,8 +207,6 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
         {(void**)&st->d_tok_src, sizeof(int64_t) * size_t(d.max_batch) * size_t(st->seg_tokens), "segment plan"},
         {(void**)&st->d_tok_dst, sizeof(int64_t) * size_t(d.max_batch) * size_t(st->seg_tokens), "segment plan"},
         {(void**)&st->d_req_len, sizeof(int32_t) * size_t(d.max_batch), "segment plan"},
-        {(void**)&st->d_rope_tab, sizeof(double2) * size_t(st->seg_tokens) * (D / 2), "RoPE table"},
-        {(void**)&st->d_req_base, sizeof(double2) * size_t(d.max_batch) * (D / 2), "RoPE bases"},
     };
     for (auto& a : allocs) {
         e = hipMalloc(a.p, a.bytes);
@@ -253,8 +251,6 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
         e = hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyHostToDevice, s);
         if (e != hipSuccess) { free_store(st); return hip_fail(e, "hipMemcpyAsync(metadata)"); }
     }
-    e = fsi_init_rope_table(st, s);
-    if (e != hipSuccess) { free_store(st); return hip_fail(e, "RoPE table kernel"); }
     e = hipStreamSynchronize(s);
     if (e != hipSuccess) { free_store(st); return hip_fail(e, "hipStreamSynchronize"); }
     *out = st;

@@ -10,28 +10,25 @@
 //
 // One fs_inject call is two launches:
 //
-//   plan kernel    one block; each wave plans whole requests: prefix sums of
-//                  the selected facts' lengths, validation of ids, start
-//                  position, block-table entries (and staging slots), then a
-//                  token map (arena row and cache slot of every segment token)
-//                  in scratch.  A rejected request gets length 0 and an error
-//                  bit, so nothing of it is written.  Finally the block turns
-//                  the lengths into a prefix of work units over requests.
+//   plan kernel    one block per request: prefix sums of the selected facts'
+//                  lengths, validation of ids, start position, block-table
+//                  entries (and staging slots), then a token map (arena row and
+//                  cache slot of every segment token) in scratch.  A rejected
+//                  request gets length 0 and an error bit, so nothing of it is
+//                  written.
 //
-//   inject kernel  persistent: exactly 16 one-wave blocks per compute unit.
-//                  The job is cut into units = (request, group of tokens,
-//                  layer, head); wave w takes the w-th equal contiguous share.
-//                  Throughput here is capped per CU, so equal bytes per CU is
-//                  what keeps every CU busy until the end (a grid of blocks
-//                  per token tile leaves some CUs with 1.5x the bytes of
-//                  others).  A team of head_dim/16 lanes owns one token: lane
-//                  tl holds the 8 rotate-half pairs i = 8*tl .. 8*tl+7 (one
-//                  16-byte vector from each half of the head row), computes
-//                  cos/sin of p*w_i once in fp64 and reuses them for every
-//                  (layer, head) unit of that token group.  Units are
-//                  processed two at a time: 8 vector loads in flight per
-//                  lane, then rotation and 8 non-temporal stores (more would
-//                  not fit 128 VGPRs, the limit for 16 waves per CU).
+//   inject kernel  one small block per (token group, request, layer).  A team
+//                  of head_dim/16 lanes owns one token: lane tl holds the 8
+//                  rotate-half pairs i = 8*tl .. 8*tl+7 (one 16-byte vector
+//                  from each half of the head row).  The block first evaluates
+//                  cos/sin of p*w_i in fp64 for every (token, frequency) of its
+//                  group into LDS, one sincos per entry, while its first loads
+//                  are in flight; each wave then streams whole heads of the
+//                  group: 4 non-temporal 16-byte loads per lane, rotation of
+//                  K, 4 non-temporal stores.  Thousands of small blocks let the
+//                  dispatcher keep every CU fed to the end of the launch (a
+//                  persistent grid with equal shares per CU finished later:
+//                  the CUs do not drain at the same rate).
 //
 // HBM-bound copy with a small amount of arithmetic; no dense contraction, so
 // no MFMA.
@@ -42,15 +39,9 @@
 
 namespace {
 
-constexpr int kThreads = 64;        // one wave per inject / fetch block
-#ifndef FS_INJ_THREADS
-#define FS_INJ_THREADS 1024
-#endif
-#ifndef FS_INJ_UNITS
-#define FS_INJ_UNITS 2
-#endif
-constexpr int kInjectThreads = FS_INJ_THREADS;   // one inject block per CU
-constexpr int kGrab = FS_INJ_UNITS;              // units taken (and in flight) per grab
+constexpr int kThreads = 64;        // one wave per fetch block
+constexpr int kInjectThreads = 256; // 4 waves per inject block
+constexpr int kInjectOcc = 6;       // waves per SIMD the register budget allows
 constexpr int kPlanThreads = 1024;
 
 #define FS_GLOBAL __attribute__((address_space(1)))
@@ -81,24 +72,18 @@ struct PlanArgs {
     int64_t* tok_src;
     int64_t* tok_dst;
     int32_t* req_len;
-    const double* inv_freq;
-    int32_t half_dim;
-    double2* req_base;              // (cos, sin) of start_pos * w_i per request
     uint32_t* err;
 };
 
 struct InjectArgs {
-    int32_t batch;
     const int32_t* start_pos;
     const int64_t* tok_src;
     const int64_t* tok_dst;
     const int32_t* req_len;
     int32_t seg_tokens;
-    const double* inv_freq;
-    const double2* rope_tab;        // [seg_tokens][D/2] (cos, sin) of t * w_i
-    const double2* req_base;        // [batch][D/2] (cos, sin) of start_pos * w_i
+    const double* inv_freq;         // [D/2] w_i
     int32_t heads;
-    int32_t layer_begin, layer_end;
+    int32_t layer_begin;
     const void* const* src_k;       // device table [num_layers] (device store)
     const void* const* src_v;
     const uint16_t* stage_k;        // non-null: read the staging ring instead
@@ -337,211 +322,87 @@ __global__ __launch_bounds__(kPlanThreads) void fs_plan_kernel(PlanArgs a) {
         const int p = s + t;
         dst[t] = (int64_t(bt[p >> a.log2_block]) << a.log2_block) | (p & bs_mask);
     }
-    if (L > 0 && threadIdx.x < a.half_dim) {
-        double sv, cv;
-        sincos(static_cast<double>(s) * a.inv_freq[threadIdx.x], &sv, &cv);
-        a.req_base[int64_t(b) * a.half_dim + threadIdx.x] = make_double2(cv, sv);
-    }
 }
 
-// (cos, sin) of t * w_i for every segment offset t: the per-token factor of
-// the angle-addition form cos((s+t)w) = cos(sw)cos(tw) - sin(sw)sin(tw)
-__global__ void fs_rope_table_kernel(double2* tab, const double* inv_freq, int half, int64_t n) {
-    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (idx >= n) return;
-    const int64_t t = idx / half;
-    const int i = static_cast<int>(idx - t * half);
-    double sv, cv;
-    sincos(static_cast<double>(t) * inv_freq[i], &sv, &cv);
-    tab[idx] = make_double2(cv, sv);
-}
-
-// One 1024-thread block (16 waves) per compute unit.  The block owns an equal
-// contiguous share of the units; its waves take units one at a time from an
-// LDS counter, so the waves the CU favours do more of the share.
-template <int D, bool kSingle>
-__global__ __launch_bounds__(kInjectThreads) void fs_inject_kernel(InjectArgs a, PlanArgs pa) {
+// One block per (token group g, request b, layer l).  The group's tokens are
+// t = g*kTok + team; blocks past the request's segment exit at once.
+template <int D>
+__global__ __launch_bounds__(kInjectThreads, kInjectOcc) void fs_inject_kernel(InjectArgs a) {
     constexpr int kTeam = D / 16;            // lanes per token
-    constexpr int kTok = 64 / kTeam;         // tokens per unit
+    constexpr int kTok = 64 / kTeam;         // tokens per group
     constexpr int kHalf = D / 16;            // 16-byte vectors per half head row
-    extern __shared__ int64_t plan_lds[];
-    __shared__ int s_L, s_nf, s_bits;
-    __shared__ unsigned s_next;          // block queue over the block's share
-    __shared__ double2 s_base[128];      // kSingle: (cos, sin) of start_pos * w_i
+    constexpr int kCS = kTok * (D / 2);      // (cos, sin) entries of the group
+    constexpr int kWaves = kInjectThreads / 64;
+    __shared__ double2 s_cs[kCS];
+    const int b = blockIdx.y;
+    const int g = blockIdx.x;
+    const int L = a.req_len[b];
+    if (g * kTok >= L) return;               // uniform over the block
+    const int l = a.layer_begin + blockIdx.z;
     const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int team = lane / kTeam;
     const int tl = lane % kTeam;
-    const int H = a.heads;
-    const int per_group = (a.layer_end - a.layer_begin) * H;
-    const int64_t row_elems = int64_t(H) * D;
-    int64_t* row0 = plan_lds;
-    int32_t* off = reinterpret_cast<int32_t*>(plan_lds + pa.k);
-
-    if (threadIdx.x < 64) {
-        if (kSingle) {
-            // one request: each block plans it (the same answer everywhere),
-            // so there is no second launch and no scratch round trip
-            int L = 0, nf = 0;
-            uint32_t bits = plan_request(pa.user, pa.ids, pa.k, pa.user_begin, pa.num_users,
-                                         pa.fact_len, pa.fact_begin, 0, off, row0, &L, &nf);
-            bits |= check_request(pa, 0, L);
-            bits = wave_or(bits);
-            if (lane == 0) {
-                s_L = L;
-                s_nf = nf;
-                s_bits = bits;
-                if (bits && blockIdx.x == 0) atomicOr(pa.err, bits);
-            }
-        } else if (lane == 0) {
-            s_bits = 0;
-        }
-        if (lane == 0) s_next = 0;
-    } else if (kSingle && threadIdx.x - 64 < unsigned(D / 2)) {
-        // the second wave meanwhile prepares the request's angle base
-        const int i = threadIdx.x - 64;
-        double sv, cv;
-        sincos(static_cast<double>(a.start_pos[0]) * a.inv_freq[i], &sv, &cv);
-        s_base[i] = make_double2(cv, sv);
-    }
-    __syncthreads();
-    if (s_bits) return;
-
-    int64_t total = 0;
-    const int L0 = kSingle ? s_L : 0;
-    const int nf0 = kSingle ? s_nf : 0;
-    if (kSingle) {
-        total = int64_t((L0 + kTok - 1) / kTok) * per_group;
-    } else {
-        for (int c0 = 0; c0 < a.batch; c0 += 64) {
-            const int bb = c0 + lane;
-            int64_t units = bb < a.batch ? int64_t((a.req_len[bb] + kTok - 1) / kTok) * per_group : 0;
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) units += __shfl_xor(units, o, 64);
-            total += units;
-        }
-    }
-    // the units are split evenly over the blocks (one block per CU)
-    const int64_t G = gridDim.x;
-    const int64_t blk_lo = total * int64_t(blockIdx.x) / G;
-    const int64_t blk_n = total * (int64_t(blockIdx.x) + 1) / G - blk_lo;
-
-    // request of the wave's current unit and that request's unit range
-    auto units_of = [&](int bb) -> int64_t {
-        return int64_t((a.req_len[bb] + kTok - 1) / kTok) * per_group;
-    };
-    int b = 0;
-    int64_t req_lo = 0, req_hi = kSingle ? total : units_of(0);
-    int cur_b = -1, cur_g = -1;
-    bool act = false;
-    int t = 0;
+    const int t = g * kTok + team;
+    const bool act = t < L;
     int64_t src_row = 0, dst_row = 0;
-    double c[8], sn[8];
+    if (act) {
+        src_row = a.tok_src[int64_t(b) * a.seg_tokens + t];
+        dst_row = a.tok_dst[int64_t(b) * a.seg_tokens + t];
+    }
+    const int H = a.heads;
+    const int64_t row_elems = int64_t(H) * D;
+    const FS_GLOBAL u32x4* kbase;
+    const FS_GLOBAL u32x4* vbase;
+    if (a.stage_k) {
+        const int64_t srow = (int64_t(l % a.staging_layers) * a.max_batch + b) * a.stage_tokens + t;
+        kbase = (const FS_GLOBAL u32x4*)(a.stage_k + srow * row_elems);
+        vbase = (const FS_GLOBAL u32x4*)(a.stage_v + srow * row_elems);
+    } else {
+        kbase = (const FS_GLOBAL u32x4*)(static_cast<const uint16_t*>(a.src_k[l]) + src_row * row_elems);
+        vbase = (const FS_GLOBAL u32x4*)(static_cast<const uint16_t*>(a.src_v[l]) + src_row * row_elems);
+    }
+    FS_GLOBAL u32x4* kd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.kc[l]) + dst_row * row_elems);
+    FS_GLOBAL u32x4* vd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.vc[l]) + dst_row * row_elems);
 
-    // units [u, u_stop): every one is processed; a range crossing a
-    // token-group or request boundary is done in several passes
-    auto run = [&](int64_t u, const int64_t u_stop) {
-      while (u < u_stop) {
-        if (!kSingle) {
-            while (u >= req_hi) {        // a wave's units only move forward
-                ++b;
-                req_lo = req_hi;
-                req_hi = req_lo + units_of(b);
-            }
+    u32x4 ka, kb, va, vb;
+    auto load_head = [&](int h) {
+        if (act && h < H) {
+            const int o = h * (D / 8) + tl;
+            ka = ld_stream(kbase + o);
+            kb = ld_stream(kbase + o + kHalf);
+            va = ld_stream(vbase + o);
+            vb = ld_stream(vbase + o + kHalf);
         }
-        const int64_t r = u - req_lo;
-        const int g = static_cast<int>(r / per_group);
-        const int lh0 = static_cast<int>(r - int64_t(g) * per_group);
-        int n = kGrab;
-        if (int64_t(n) > u_stop - u) n = static_cast<int>(u_stop - u);
-        if (n > per_group - lh0) n = per_group - lh0;
-        if (!kSingle && int64_t(n) > req_hi - u) n = static_cast<int>(req_hi - u);
-
-        if (b != cur_b || g != cur_g) {
-            cur_b = b;
-            cur_g = g;
-            t = g * kTok + team;
-            if (kSingle) {
-                act = t < L0;
-                if (act) {
-                    const int j = find_fact(off, nf0, t);
-                    src_row = row0[j] + (t - off[j]);
-                    const int p = a.start_pos[0] + t;
-                    const int blk = pa.block_table[p >> pa.log2_block];
-                    dst_row = (int64_t(blk) << pa.log2_block) | (p & ((1 << pa.log2_block) - 1));
-                }
-            } else {
-                act = t < a.req_len[b];
-                if (act) {
-                    src_row = a.tok_src[int64_t(b) * a.seg_tokens + t];
-                    dst_row = a.tok_dst[int64_t(b) * a.seg_tokens + t];
-                }
-            }
-            if (act) {
-                // angle (s + t) * w_i by angle addition from the request's
-                // base (s * w_i) and the tabulated t * w_i, all in fp64
-                const double2* tb = a.rope_tab + int64_t(t) * (D / 2) + 8 * tl;
-                const double2* bb = kSingle ? &s_base[8 * tl] : a.req_base + int64_t(b) * (D / 2) + 8 * tl;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const double2 tv = tb[e];
-                    const double2 bv = bb[e];
-                    c[e] = fma(bv.x, tv.x, -(bv.y * tv.y));
-                    sn[e] = fma(bv.y, tv.x, bv.x * tv.y);
-                }
-            }
-        }
-        if (act) {
-            u32x4 ka[kGrab], kb[kGrab], va[kGrab], vb[kGrab];
-#pragma unroll
-            for (int q = 0; q < kGrab; ++q) {
-                if (q < n) {
-                    const int lh = lh0 + q;
-                    const int l = a.layer_begin + lh / H;
-                    const int h = lh - (lh / H) * H;
-                    const FS_GLOBAL u32x4* ks;
-                    const FS_GLOBAL u32x4* vs;
-                    if (a.stage_k) {
-                        const int64_t srow = (int64_t(l % a.staging_layers) * a.max_batch + b) * a.stage_tokens + t;
-                        ks = (const FS_GLOBAL u32x4*)(a.stage_k + srow * row_elems + h * D);
-                        vs = (const FS_GLOBAL u32x4*)(a.stage_v + srow * row_elems + h * D);
-                    } else {
-                        ks = (const FS_GLOBAL u32x4*)(static_cast<const uint16_t*>(a.src_k[l]) + src_row * row_elems + h * D);
-                        vs = (const FS_GLOBAL u32x4*)(static_cast<const uint16_t*>(a.src_v[l]) + src_row * row_elems + h * D);
-                    }
-                    ka[q] = ld_stream(ks + tl);
-                    kb[q] = ld_stream(ks + tl + kHalf);
-                    va[q] = ld_stream(vs + tl);
-                    vb[q] = ld_stream(vs + tl + kHalf);
-                }
-            }
-#pragma unroll
-            for (int q = 0; q < kGrab; ++q) {
-                if (q < n) {
-                    const int lh = lh0 + q;
-                    const int l = a.layer_begin + lh / H;
-                    const int h = lh - (lh / H) * H;
-                    const int64_t o = dst_row * row_elems + h * D;
-                    FS_GLOBAL u32x4* kd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.kc[l]) + o);
-                    FS_GLOBAL u32x4* vd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.vc[l]) + o);
-                    u32x4 ya, yb;
-                    rot_v(ka[q], kb[q], c, sn, ya, yb);
-                    st_stream(kd + tl, ya);
-                    st_stream(kd + tl + kHalf, yb);
-                    st_stream(vd + tl, va[q]);
-                    st_stream(vd + tl + kHalf, vb[q]);
-                }
-            }
-        }
-        u += n;
-      }
     };
-
-    for (;;) {
-        unsigned i = 0;
-        if (lane == 0) i = atomicAdd(&s_next, unsigned(kGrab));
-        i = __shfl(i, 0, 64);
-        if (int64_t(i) >= blk_n) break;
-        run(blk_lo + i, blk_lo + (int64_t(i) + kGrab < blk_n ? int64_t(i) + kGrab : blk_n));
+    load_head(wave);                         // in flight while the table is built
+    const int p0 = a.start_pos[b] + g * kTok;
+    for (int e = threadIdx.x; e < kCS; e += kInjectThreads) {
+        const int tt = e / (D / 2);
+        const int i = e - tt * (D / 2);
+        double sv, cv;
+        sincos(static_cast<double>(p0 + tt) * a.inv_freq[i], &sv, &cv);
+        s_cs[e] = make_double2(cv, sv);
+    }
+    __syncthreads();                         // reached by every thread of the block
+    if (!act) return;
+    double c[8], sn[8];
+    const double2* cs = s_cs + team * (D / 2) + 8 * tl;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const double2 v = cs[e];
+        c[e] = v.x;
+        sn[e] = v.y;
+    }
+    for (int h = wave; h < H; h += kWaves) {
+        if (h != wave) load_head(h);
+        const int o = h * (D / 8) + tl;
+        u32x4 ya, yb;
+        rot_v(ka, kb, c, sn, ya, yb);
+        st_stream(kd + o, ya);
+        st_stream(kd + o + kHalf, yb);
+        st_stream(vd + o, va);
+        st_stream(vd + o + kHalf, vb);
     }
 }
 
@@ -652,25 +513,18 @@ hipError_t launch_inject(const InjectLaunch& r) {
     pa.tok_src = st->d_tok_src;
     pa.tok_dst = st->d_tok_dst;
     pa.req_len = st->d_req_len;
-    pa.inv_freq = st->d_inv_freq;
-    pa.half_dim = d.head_dim / 2;
-    pa.req_base = st->d_req_base;
     pa.err = st->d_err;
     const size_t plan_lds = sizeof(int64_t) * (size_t(r.k) + (size_t(r.k) + 2) / 2);
 
     InjectArgs a{};
-    a.batch = r.batch;
     a.start_pos = r.start_pos;
     a.tok_src = st->d_tok_src;
     a.tok_dst = st->d_tok_dst;
     a.req_len = st->d_req_len;
     a.seg_tokens = st->seg_tokens;
     a.inv_freq = st->d_inv_freq;
-    a.rope_tab = st->d_rope_tab;
-    a.req_base = st->d_req_base;
     a.heads = d.num_kv_heads;
     a.layer_begin = r.layer_begin;
-    a.layer_end = r.layer_end;
     a.src_k = st->d_src_k;
     a.src_v = st->d_src_v;
     if (d.kv_location == FS_KV_PINNED_HOST) {
@@ -684,15 +538,17 @@ hipError_t launch_inject(const InjectLaunch& r) {
         a.kc[l] = r.k_cache[l];
         a.vc[l] = r.v_cache[l];
     }
-    const dim3 grid(st->num_cus);
-    if (r.batch == 1) {
-        fs_inject_kernel<D, true><<<grid, kInjectThreads, plan_lds, r.stream>>>(a, pa);
-        return hipGetLastError();
-    }
     fs_plan_kernel<<<dim3(r.batch), kPlanThreads, plan_lds, r.stream>>>(pa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    fs_inject_kernel<D, false><<<grid, kInjectThreads, 0, r.stream>>>(a, pa);
+    // token groups of the longest possible segment; the blocks past a
+    // request's real length exit at their first instruction
+    constexpr int kTok = 64 / (D / 16);
+    const int64_t groups = (int64_t(r.k) * st->max_fact_len + kTok - 1) / kTok;
+    if (groups == 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(groups), static_cast<unsigned>(r.batch),
+                    static_cast<unsigned>(r.layer_end - r.layer_begin));
+    fs_inject_kernel<D><<<grid, kInjectThreads, 0, r.stream>>>(a);
     return hipGetLastError();
 }
 
@@ -743,15 +599,6 @@ hipError_t fsi_launch_inject(const InjectLaunch& r) {
         case 256: return launch_inject<256>(r);
         default: return hipErrorInvalidValue;
     }
-}
-
-hipError_t fsi_init_rope_table(const fs_store* st, hipStream_t stream) {
-    const int half = st->desc.head_dim / 2;
-    const int64_t n = int64_t(st->seg_tokens) * half;
-    if (n == 0) return hipSuccess;
-    fs_rope_table_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), 256, 0, stream>>>(
-        st->d_rope_tab, st->d_inv_freq, half, n);
-    return hipGetLastError();
 }
 
 hipError_t fsi_launch_fetch(const FetchLaunch& r) {
