@@ -35,6 +35,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "fs_internal.h"
 
 namespace {
@@ -325,31 +327,88 @@ __global__ __launch_bounds__(kPlanThreads) void fs_plan_kernel(PlanArgs a) {
 }
 
 // One block per (token group g, request b, layer l).  The group's tokens are
-// t = g*kTok + team; blocks past the request's segment exit at once.
-template <int D>
-__global__ __launch_bounds__(kInjectThreads, kInjectOcc) void fs_inject_kernel(InjectArgs a) {
+// t = g*kTok + team.
+//
+// kPlanned = false (device stores): the block plans its request itself.  Wave 0
+// reads the ids and prefix-sums the fact lengths into LDS while the other
+// waves fill the cos/sin table.  After the first barrier every lane locates
+// its token's arena row and cache slot and issues its first loads, while wave
+// 0 validates the whole request (so a rejected request writes nothing in any
+// block); the second barrier publishes the verdict before any store.  Reads
+// before the verdict stay in bounds: the plan counts only valid facts of the
+// user, and block-table reads are range-checked.  No launch is spent on
+// planning.
+//
+// kPlanned = true (pinned stores): the plan kernel has validated the request
+// (including every layer's staging slot) and written the token map.
+template <int D, bool kPlanned>
+__global__ __launch_bounds__(kInjectThreads, kInjectOcc) void fs_inject_kernel(InjectArgs a, PlanArgs pa) {
     constexpr int kTeam = D / 16;            // lanes per token
     constexpr int kTok = 64 / kTeam;         // tokens per group
     constexpr int kHalf = D / 16;            // 16-byte vectors per half head row
     constexpr int kCS = kTok * (D / 2);      // (cos, sin) entries of the group
     constexpr int kWaves = kInjectThreads / 64;
     __shared__ double2 s_cs[kCS];
+    __shared__ int s_L, s_nf, s_bits;
+    extern __shared__ int64_t plan_lds[];
+    int64_t* row0 = plan_lds;
+    int32_t* off = reinterpret_cast<int32_t*>(plan_lds + pa.k);
     const int b = blockIdx.y;
     const int g = blockIdx.x;
-    const int L = a.req_len[b];
-    if (g * kTok >= L) return;               // uniform over the block
     const int l = a.layer_begin + blockIdx.z;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int team = lane / kTeam;
     const int tl = lane % kTeam;
     const int t = g * kTok + team;
-    const bool act = t < L;
+    const int64_t p0 = int64_t(a.start_pos[b]) + int64_t(g) * kTok;
+    const bool reporter = !kPlanned && g == 0 && blockIdx.z == 0;
+
+    int L;
     int64_t src_row = 0, dst_row = 0;
-    if (act) {
-        src_row = a.tok_src[int64_t(b) * a.seg_tokens + t];
-        dst_row = a.tok_dst[int64_t(b) * a.seg_tokens + t];
+    if (kPlanned) {
+        L = a.req_len[b];
+        if (g * kTok >= L) return;           // uniform over the block
+        if (t < L) {
+            src_row = a.tok_src[int64_t(b) * a.seg_tokens + t];
+            dst_row = a.tok_dst[int64_t(b) * a.seg_tokens + t];
+        }
+    } else if (wave == 0) {
+        int Lr = 0, nf = 0;
+        const uint32_t bits = plan_request(pa.user, pa.ids, pa.k, pa.user_begin, pa.num_users,
+                                           pa.fact_len, pa.fact_begin, b, off, row0, &Lr, &nf);
+        const uint32_t any = wave_or(bits);
+        if (lane == 0) {
+            s_L = Lr;
+            s_nf = nf;
+            s_bits = any;
+        }
     }
+    const int cs_begin = kPlanned ? 0 : 64;  // threads filling the table
+    if (kPlanned || wave > 0) {
+        for (int e = threadIdx.x - cs_begin; e < kCS; e += kInjectThreads - cs_begin) {
+            const int tt = e / (D / 2);
+            const int i = e - tt * (D / 2);
+            double sv, cv;
+            sincos(static_cast<double>(p0 + tt) * a.inv_freq[i], &sv, &cv);
+            s_cs[e] = make_double2(cv, sv);
+        }
+    }
+    if (!kPlanned) {
+        __syncthreads();                     // plan in LDS
+        L = s_L;
+        if (g * kTok >= L && !reporter) return;   // uniform over the block
+        if (t < L) {
+            const int j = find_fact(off, s_nf, t);
+            src_row = row0[j] + (t - off[j]);
+            const int64_t p = p0 + team;
+            const int64_t bi = p >> pa.log2_block;
+            int blk = 0;
+            if (p >= 0 && bi < pa.max_blocks) blk = pa.block_table[int64_t(b) * pa.max_blocks + bi];
+            dst_row = (int64_t(blk) << pa.log2_block) | (p & ((1 << pa.log2_block) - 1));
+        }
+    }
+    const bool act = t < L;
     const int H = a.heads;
     const int64_t row_elems = int64_t(H) * D;
     const FS_GLOBAL u32x4* kbase;
@@ -362,9 +421,6 @@ __global__ __launch_bounds__(kInjectThreads, kInjectOcc) void fs_inject_kernel(I
         kbase = (const FS_GLOBAL u32x4*)(static_cast<const uint16_t*>(a.src_k[l]) + src_row * row_elems);
         vbase = (const FS_GLOBAL u32x4*)(static_cast<const uint16_t*>(a.src_v[l]) + src_row * row_elems);
     }
-    FS_GLOBAL u32x4* kd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.kc[l]) + dst_row * row_elems);
-    FS_GLOBAL u32x4* vd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.vc[l]) + dst_row * row_elems);
-
     u32x4 ka, kb, va, vb;
     auto load_head = [&](int h) {
         if (act && h < H) {
@@ -375,17 +431,19 @@ __global__ __launch_bounds__(kInjectThreads, kInjectOcc) void fs_inject_kernel(I
             vb = ld_stream(vbase + o + kHalf);
         }
     };
-    load_head(wave);                         // in flight while the table is built
-    const int p0 = a.start_pos[b] + g * kTok;
-    for (int e = threadIdx.x; e < kCS; e += kInjectThreads) {
-        const int tt = e / (D / 2);
-        const int i = e - tt * (D / 2);
-        double sv, cv;
-        sincos(static_cast<double>(p0 + tt) * a.inv_freq[i], &sv, &cv);
-        s_cs[e] = make_double2(cv, sv);
+    load_head(wave);                         // in flight across the barrier
+    if (!kPlanned && wave == 0) {
+        const uint32_t bits = wave_or(check_request(pa, b, L)) | s_bits;
+        if (lane == 0) {
+            s_bits = bits;
+            if (bits && reporter) atomicOr(pa.err, bits);
+        }
     }
-    __syncthreads();                         // reached by every thread of the block
+    __syncthreads();                         // reached by every thread still here
+    if (!kPlanned && s_bits) return;
     if (!act) return;
+    FS_GLOBAL u32x4* kd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.kc[l]) + dst_row * row_elems);
+    FS_GLOBAL u32x4* vd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.vc[l]) + dst_row * row_elems);
     double c[8], sn[8];
     const double2* cs = s_cs + team * (D / 2) + 8 * tl;
 #pragma unroll
@@ -538,17 +596,21 @@ hipError_t launch_inject(const InjectLaunch& r) {
         a.kc[l] = r.k_cache[l];
         a.vc[l] = r.v_cache[l];
     }
-    fs_plan_kernel<<<dim3(r.batch), kPlanThreads, plan_lds, r.stream>>>(pa);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // token groups of the longest possible segment; the blocks past a
-    // request's real length exit at their first instruction
+    // token groups of the longest possible segment (at least one, which
+    // reports the request's errors); the blocks past a request's real length
+    // exit once its length is known
     constexpr int kTok = 64 / (D / 16);
-    const int64_t groups = (int64_t(r.k) * st->max_fact_len + kTok - 1) / kTok;
-    if (groups == 0) return hipSuccess;
+    const int64_t groups = std::max<int64_t>(1, (int64_t(r.k) * st->max_fact_len + kTok - 1) / kTok);
     const dim3 grid(static_cast<unsigned>(groups), static_cast<unsigned>(r.batch),
                     static_cast<unsigned>(r.layer_end - r.layer_begin));
-    fs_inject_kernel<D><<<grid, kInjectThreads, 0, r.stream>>>(a);
+    if (d.kv_location == FS_KV_PINNED_HOST) {
+        fs_plan_kernel<<<dim3(r.batch), kPlanThreads, plan_lds, r.stream>>>(pa);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        fs_inject_kernel<D, true><<<grid, kInjectThreads, 0, r.stream>>>(a, pa);
+    } else {
+        fs_inject_kernel<D, false><<<grid, kInjectThreads, plan_lds, r.stream>>>(a, pa);
+    }
     return hipGetLastError();
 }
 
