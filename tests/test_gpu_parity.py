@@ -192,8 +192,8 @@ def test_host_checked_errors_enqueue_nothing():
 
 # --------------------------------------------------------- device-checked faults
 
-@pytest.mark.parametrize("fault", ["block_short", "block_id", "start_pos", "fact_id",
-                                   "pad_then_id", "user"])
+@pytest.mark.parametrize("fault", ["block_short", "block_id", "start_pos", "pos_overflow",
+                                   "fact_id", "pad_then_id", "user"])
 def test_device_checked_fault_writes_nothing(fault):
     wl = synth.make_workload("tiny", seed=91)
     s = wl.shape
@@ -207,7 +207,8 @@ def test_device_checked_fault_writes_nothing(fault):
     users = np.zeros(B, np.int32)
     mb = 8
     expect = {"block_short": fs.FS_ERR_BLOCK_SHORT, "block_id": fs.FS_ERR_BLOCK_ID,
-              "start_pos": fs.FS_ERR_START_POS, "fact_id": fs.FS_ERR_FACT_ID,
+              "start_pos": fs.FS_ERR_START_POS, "pos_overflow": fs.FS_ERR_START_POS,
+              "fact_id": fs.FS_ERR_FACT_ID,
               "pad_then_id": fs.FS_ERR_FACT_ID, "user": fs.FS_ERR_USER}[fault]
     if fault == "block_short":
         sp[1] = 50                        # 50 + 80 tokens need 9 blocks, table has 8
@@ -215,6 +216,8 @@ def test_device_checked_fault_writes_nothing(fault):
         table[1, 3] = s.pool_blocks       # one past the end
     elif fault == "start_pos":
         sp[1] = -1
+    elif fault == "pos_overflow":
+        sp[1] = 2**31 - 40                # start + 80 tokens passes INT32_MAX
     elif fault == "fact_id":
         ids[1, 2] = s.num_facts
     elif fault == "pad_then_id":
