@@ -12,13 +12,22 @@
 //                ...), accumulates them in order, then a fixed butterfly
 //                reduces the wave.  The reduction order depends only on the
 //                column, never on the row, which is what makes equal rows tie.
-// top-k kernel   one 1024-thread block per request.  Scores map to
-//                order-preserving 64-bit keys; an MSB-first radix select
-//                (8-bit digits, LDS histogram) finds the k-th key, stopping as
-//                soon as the boundary bucket is taken whole; ties on the full
-//                key keep the lowest indices (block-wide ordered scan); the
-//                k' winners are bitonic-sorted in LDS by (key desc, id asc).
-//                The same block sums the winners' lengths (the segment length).
+// top-k kernel   one 1024-thread block per request.  First try: the min and
+//                max of the request's scores define 2048 equal-width value
+//                bins (the bin is a monotone function of the score, so equal
+//                scores share a bin); an LDS histogram and a block suffix scan
+//                find the bin that holds the k-th best score, every score in
+//                that bin or above becomes a candidate, and each candidate's
+//                rank is the number of candidates that beat it on
+//                (score desc, index asc).  That costs a few passes over the
+//                scores whatever k is.  When the threshold bin holds too many
+//                scores (heavy ties, clustered values) or a score is not
+//                finite, the block falls back to an exact MSB-first radix
+//                select on order-preserving 64-bit keys (8-bit digits, LDS
+//                histogram; equal full keys keep the lowest indices through a
+//                block-wide ordered scan) and a bitonic sort of the winners.
+//                The same block sums the winners' lengths (the segment
+//                length).
 
 #include <hip/hip_runtime.h>
 
@@ -30,6 +39,10 @@ constexpr int kScoreWaves = 4;
 constexpr int kScoreRowsPerWave = 2;
 constexpr int kScoreRowsPerBlock = kScoreWaves * kScoreRowsPerWave;
 constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kBins = 2048;          // value bins of the threshold search
+constexpr int kCandMax = 2048;       // largest candidate set ranked directly
+constexpr int kKeep = 4;             // scores per thread kept in registers
 
 __device__ __forceinline__ uint64_t order_key(double x) {
     uint64_t u = (x == 0.0) ? 0ull : static_cast<uint64_t>(__double_as_longlong(x));
@@ -39,6 +52,17 @@ __device__ __forceinline__ uint64_t order_key(double x) {
 __device__ __forceinline__ double key_value(uint64_t key) {
     uint64_t u = (key >> 63) ? (key & 0x7FFFFFFFFFFFFFFFull) : ~key;
     return __longlong_as_double(static_cast<long long>(u));
+}
+
+__device__ __forceinline__ bool better(uint64_t ka, int ia, uint64_t kb, int ib) {
+    return ka > kb || (ka == kb && ia < ib);
+}
+
+// Bin of a score: (x - lo) * scale rounds monotonically, so x <= y implies
+// bin(x) <= bin(y).  One definition serves both passes that need it.
+__device__ __forceinline__ int value_bin(double x, double lo, double scale) {
+    const int bin = static_cast<int>((x - lo) * scale);
+    return bin < kBins - 1 ? bin : kBins - 1;
 }
 
 __device__ __forceinline__ double wave_sum(double v) {
@@ -59,7 +83,6 @@ struct ScoreArgs {
 };
 
 __global__ __launch_bounds__(256) void fs_score_kernel(ScoreArgs a) {
-    extern __shared__ float4 q_lds[];
     const int b = blockIdx.y;
     const int u = a.user[b];
     if (u < 0 || u >= a.num_users) return;
@@ -67,8 +90,9 @@ __global__ __launch_bounds__(256) void fs_score_kernel(ScoreArgs a) {
     const int32_t n = static_cast<int32_t>(a.user_begin[u + 1] - base);
     const int32_t row0 = blockIdx.x * kScoreRowsPerBlock;
     if (row0 >= n) return;
-    for (int c = threadIdx.x; c < a.e4; c += blockDim.x) q_lds[c] = a.query[int64_t(b) * a.e4 + c];
-    __syncthreads();
+    // the query is read straight from global memory (cached after the first
+    // wave touches it), so its loads overlap the embedding loads
+    const float4* qv = a.query + int64_t(b) * a.e4;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -79,7 +103,7 @@ __global__ __launch_bounds__(256) void fs_score_kernel(ScoreArgs a) {
     double acc0 = 0.0, acc1 = 0.0;
 #pragma unroll 4
     for (int c = lane; c < a.e4; c += 64) {
-        const float4 q = q_lds[c];
+        const float4 q = qv[c];
         if (v0) {
             const float4 e = e0[c];
             acc0 = fma(double(e.x), double(q.x), acc0);
@@ -149,6 +173,139 @@ __global__ __launch_bounds__(kTopkThreads) void fs_topk_kernel(TopkArgs a) {
     }
 
     const double* sc = a.scores + int64_t(b) * a.stride;
+
+    bool tokens_known = false;           // the fast path sums the lengths itself
+
+    // ---- first try: threshold bin, then rank the candidates ---------------
+    __shared__ int s_bin[kBins];
+    __shared__ uint64_t s_ck[kCandMax];
+    __shared__ int32_t s_ci[kCandMax];
+    __shared__ int32_t s_cl[kCandMax];   // candidate's fact length
+    __shared__ double s_wlo[kTopkWaves], s_whi[kTopkWaves];
+    __shared__ int s_wbad[kTopkWaves], s_wsum[kTopkWaves];
+    __shared__ int s_t, s_C, s_nc;
+    {
+        // scores i = tid + j*blockDim.x: the first kKeep stay in registers
+        // for the later passes, the rest (large users) are re-read
+        double xv[kKeep];
+        const int tail0 = tid + kKeep * kTopkThreads;
+#pragma unroll
+        for (int j = 0; j < kKeep; ++j) {
+            const int i = tid + j * kTopkThreads;
+            xv[j] = i < n ? sc[i] : 0.0;
+        }
+        double lo = __builtin_huge_val(), hi = -__builtin_huge_val();
+        int bad = 0;
+        auto see = [&](double x) {
+            if (!(fabs(x) < __builtin_huge_val())) bad = 1;     // NaN or infinite
+            lo = fmin(lo, x);
+            hi = fmax(hi, x);
+        };
+#pragma unroll
+        for (int j = 0; j < kKeep; ++j)
+            if (tid + j * kTopkThreads < n) see(xv[j]);
+        for (int i = tail0; i < n; i += kTopkThreads) see(sc[i]);
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            lo = fmin(lo, __shfl_xor(lo, m, 64));
+            hi = fmax(hi, __shfl_xor(hi, m, 64));
+            bad |= __shfl_xor(bad, m, 64);
+        }
+        if (lane == 0) {
+            s_wlo[wave] = lo;
+            s_whi[wave] = hi;
+            s_wbad[wave] = bad;
+        }
+        for (int i = tid; i < kBins; i += blockDim.x) s_bin[i] = 0;
+        if (tid == 0) {
+            s_nc = 0;
+            s_tokens = 0;
+        }
+        __syncthreads();
+        for (int w = 0; w < kTopkWaves; ++w) {
+            lo = fmin(lo, s_wlo[w]);
+            hi = fmax(hi, s_whi[w]);
+            bad |= s_wbad[w];
+        }
+        const double range = hi - lo;
+        const double scale = (kBins - 0.5) / range;
+        if (!bad && range == 0.0) {
+            // every score is equal: the lowest kk indices win, in order
+            for (int j = tid; j < kk; j += blockDim.x) {
+                cand_key[j] = order_key(lo);
+                cand_idx[j] = j;
+            }
+            __syncthreads();
+            goto outputs;
+        }
+        if (!bad && range < __builtin_huge_val() && scale < __builtin_huge_val()) {
+#pragma unroll
+            for (int j = 0; j < kKeep; ++j)
+                if (tid + j * kTopkThreads < n) atomicAdd(&s_bin[value_bin(xv[j], lo, scale)], 1);
+            for (int i = tail0; i < n; i += kTopkThreads) atomicAdd(&s_bin[value_bin(sc[i], lo, scale)], 1);
+            __syncthreads();
+            // suffix counts from the top bin down: thread tid owns the two
+            // bins at descending positions 2*tid and 2*tid + 1
+            const int hb0 = kBins - 1 - 2 * tid, hb1 = hb0 - 1;
+            const int c0 = s_bin[hb0], c1 = s_bin[hb1];
+            const int local = c0 + c1;
+            int incl = local;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(incl, off, 64);
+                if (lane >= off) incl += y;
+            }
+            if (lane == 63) s_wsum[wave] = incl;
+            __syncthreads();
+            int before = incl - local;
+            for (int w = 0; w < wave; ++w) before += s_wsum[w];
+            // the k-th best score lies in the bin where the count of scores
+            // above it first reaches kk
+            if (before < kk && kk <= before + c0) {
+                s_t = hb0;
+                s_C = before + c0;
+            } else if (before + c0 < kk && kk <= before + local) {
+                s_t = hb1;
+                s_C = before + local;
+            }
+            __syncthreads();
+            const int t = s_t, C = s_C;
+            if (C <= kCandMax) {
+                auto gather = [&](double x, int i) {
+                    if (value_bin(x, lo, scale) >= t) {
+                        const int slot = atomicAdd(&s_nc, 1);
+                        s_ck[slot] = order_key(x);
+                        s_ci[slot] = i;
+                        s_cl[slot] = a.fact_len[base + i];
+                    }
+                };
+#pragma unroll
+                for (int j = 0; j < kKeep; ++j)
+                    if (tid + j * kTopkThreads < n) gather(xv[j], tid + j * kTopkThreads);
+                for (int i = tail0; i < n; i += kTopkThreads) gather(sc[i], i);
+                __syncthreads();
+                int my_tokens = 0;
+                for (int j = tid; j < C; j += blockDim.x) {
+                    const uint64_t kj = s_ck[j];
+                    const int ij = s_ci[j];
+                    int r = 0;
+#pragma unroll 8
+                    for (int m = 0; m < C; ++m) r += better(s_ck[m], s_ci[m], kj, ij) ? 1 : 0;
+                    if (r < kk) {
+                        cand_key[r] = kj;
+                        cand_idx[r] = ij;
+                        my_tokens += s_cl[j];
+                    }
+                }
+                if (my_tokens) atomicAdd(&s_tokens, my_tokens);
+                __syncthreads();
+                tokens_known = true;
+                goto outputs;
+            }
+        }
+    }
+
+    {
     const bool in_lds = n <= fsi::kTopkLdsKeys;
     if (in_lds)
         for (int i = tid; i < n; i += blockDim.x) keys_lds[i] = order_key(sc[i]);
@@ -281,6 +438,9 @@ __global__ __launch_bounds__(kTopkThreads) void fs_topk_kernel(TopkArgs a) {
         }
     }
 
+    }
+
+outputs:
     // ---- outputs -----------------------------------------------------------
     int my_tokens = 0;
     for (int j = tid; j < k; j += blockDim.x) {
@@ -289,14 +449,16 @@ __global__ __launch_bounds__(kTopkThreads) void fs_topk_kernel(TopkArgs a) {
         if (j < kk) {
             id = static_cast<int32_t>(base + cand_idx[j]);
             s = key_value(cand_key[j]);
-            my_tokens += a.fact_len[id];
+            if (!tokens_known) my_tokens += a.fact_len[id];
         }
         a.ids[int64_t(b) * k + j] = id;
         if (a.out_scores) a.out_scores[int64_t(b) * k + j] = s;
     }
     if (a.num_tokens) {
-        if (my_tokens) atomicAdd(&s_tokens, my_tokens);
-        __syncthreads();
+        if (!tokens_known) {
+            if (my_tokens) atomicAdd(&s_tokens, my_tokens);
+            __syncthreads();
+        }
         if (tid == 0) a.num_tokens[b] = s_tokens;
     }
 }
@@ -317,8 +479,7 @@ hipError_t fsi_launch_retrieve(const RetrieveLaunch& r) {
         sa.scores = st->d_scores;
         sa.stride = st->max_user_facts;
         dim3 grid((st->max_user_facts + kScoreRowsPerBlock - 1) / kScoreRowsPerBlock, r.batch);
-        size_t lds = sizeof(float4) * sa.e4;
-        fs_score_kernel<<<grid, 256, lds, r.stream>>>(sa);
+        fs_score_kernel<<<grid, 256, 0, r.stream>>>(sa);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -23,8 +23,8 @@ import pytest
 import torch
 
 import oracle
-from _parity import (bf16_ulp_distance, check_injection, check_retrieval, check_sentinel,
-                     gpu_retrieve, say, table_mask, written_mask)
+from _parity import (SCORE_ABS_TOL, bf16_ulp_distance, check_injection, check_retrieval,
+                     check_sentinel, gpu_retrieve, say, table_mask, written_mask)
 from kv_cache_injection_amd import fs, synth
 from kv_cache_injection_amd.workload import build_store, make_desc, request_tensors
 
@@ -142,6 +142,45 @@ def test_retrieval_ties_padding_and_empty_user():
     ids = torch.empty((4, 3), dtype=torch.int32, device="cuda")
     fs.fs_retrieve_topk(st, 4, user_t, q_t, 3, ids, None, None)
     assert list(_host(ids)[0][:2]) == [12, 17]
+    st.close()
+
+
+@pytest.mark.parametrize("k", [1, 50, 64, 65, 200, 1024])
+def test_retrieval_select_paths_with_ties(k):
+    """k <= 64 selects in the last score block, k > 64 in the radix-select
+    launch; both must give the oracle's ids.  Rows are drawn from a small
+    pool of distinct vectors, so exact ties straddle every rank, and the
+    call repeats to show the per-request block counters start from zero."""
+    rng = np.random.default_rng(100 + k)
+    E = 96
+    pool = rng.standard_normal((40, E)).astype(np.float32)
+    pool /= np.linalg.norm(pool, axis=1, keepdims=True)
+    F = 5000
+    emb = pool[rng.integers(0, 40, F)]
+    ufb = np.array([0, 3000, 3040, 5000], np.int64)    # 3000, 40 and 1960 facts
+    fl = rng.integers(1, 9, F).astype(np.int32)
+    st, _, _ = _small_store(emb, ufb, fl, max_k=1024, max_batch=3)
+    users = np.array([0, 1, 2], np.int32)
+    q = np.stack([pool[3], rng.standard_normal(E), pool[7]]).astype(np.float32)
+    q[1] /= np.linalg.norm(q[1])
+    user_t = torch.from_numpy(users).cuda()
+    q_t = torch.from_numpy(q).cuda()
+    for rep in range(2):
+        ids = torch.full((3, k), -7, dtype=torch.int32, device="cuda")
+        sc = torch.zeros((3, k), dtype=torch.float64, device="cuda")
+        nt = torch.full((3,), -7, dtype=torch.int32, device="cuda")
+        say(f"select k={k} rep={rep}")
+        fs.fs_retrieve_topk(st, 3, user_t, q_t, k, ids, sc, nt)
+        assert fs.fs_poll_errors(st) == 0
+        g, gs, gn = _host(ids), _host(sc), _host(nt)
+        for b in range(3):
+            u = users[b]
+            o_ids, o_sc = oracle.retrieve(emb, ufb, u, q[b], k)
+            assert np.array_equal(g[b].astype(np.int64), o_ids), (k, b)
+            kk = min(k, ufb[u + 1] - ufb[u])
+            assert np.all(np.abs(gs[b][:kk] - o_sc[:kk]) <= SCORE_ABS_TOL)
+            assert np.all(np.isneginf(gs[b][kk:]))
+            assert gn[b] == oracle.compose(o_ids, fl)[1]
     st.close()
 
 
