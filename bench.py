@@ -9,6 +9,12 @@ cache).  Inputs are resident in HBM before the timed region; every step uses
 a different (query, start position, block table) set, cycling through
 --sets pre-drawn sets, so the selected facts change from step to step.
 
+Steps are issued as a serving loop would: retrieval on one stream, injection
+on another, so that step i+1's retrieval (latency-bound, a few MB) overlaps
+step i's injection (bandwidth-bound); step i's injection waits on an event
+after step i's retrieval.  ms_per_step_in_order repeats the steps on one
+stream, strictly one after the other.
+
 Prints ONE JSON line:
   value       whole-step algorithmic HBM bytes / step time (GB/s)
   roofline    the inject kernel: its algorithmic bytes per launch over its
@@ -86,32 +92,49 @@ def main():
         sets.append(t)
     mb = wl.block_table.shape[1]
     user = base["user"]
-    ids = torch.empty((B, k), dtype=torch.int32, device="cuda")
     total = args.warmup + args.steps
+    ids = torch.empty((total, B, k), dtype=torch.int32, device="cuda")   # one slot per step
     ntok = torch.zeros((total, B), dtype=torch.int32, device="cuda")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(total)]
 
-    # arguments marshalled once per request set and step slot; the timed loops
-    # only issue the foreign calls
-    inj_calls = [fs.prepare_inject(ds.store, fs.FS_ALL_LAYERS, B, user, ids, k, r["block_table"],
-                                   mb, r["start_pos"], caches) for r in sets]
-    ret_calls = [fs.prepare_retrieve_topk(ds.store, B, user, sets[i % len(sets)]["query"], k, ids,
-                                          None, ntok[i]) for i in range(total)]
+    # two streams at the default priority: retrieval of step i+1 runs while
+    # step i injects (the calls share no scratch; ids have a slot per step)
+    s_ret, s_inj = torch.cuda.Stream(), torch.cuda.Stream()
+    ready = [torch.cuda.Event() for _ in range(total)]
 
-    def step(i):
-        ret_calls[i]()
-        inj_calls[i % len(sets)]()
+    # arguments marshalled once per step slot; the timed loops only issue
+    # the foreign calls
+    def prep(stream_ret, stream_inj):
+        rc = [fs.prepare_retrieve_topk(ds.store, B, user, sets[i % len(sets)]["query"], k, ids[i],
+                                       None, ntok[i], stream=stream_ret) for i in range(total)]
+        ic = [fs.prepare_inject(ds.store, fs.FS_ALL_LAYERS, B, user, ids[i], k,
+                                sets[i % len(sets)]["block_table"], mb, sets[i % len(sets)]["start_pos"],
+                                caches, stream=stream_inj) for i in range(total)]
+        return rc, ic
+    ret_p, inj_p = prep(s_ret, s_inj)                  # pipelined
+    cur = torch.cuda.current_stream()
+    ret_s, inj_s = prep(cur, cur)                      # one stream, in order
+
+    def step_pipelined(i):
+        ret_p[i]()
+        ready[i].record(s_ret)
+        s_inj.wait_event(ready[i])
+        inj_p[i]()
+
+    def step_serial(i):
+        ret_s[i]()
+        inj_s[i]()
 
     print(f"[bench] warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
-        step(i)
+        step_pipelined(i)
     torch.cuda.synchronize()
-    # timed region 1: the whole hot path, back to back (no timing events: an
-    # event between two kernels costs the stream a few microseconds)
+    # timed region 1: the whole hot path for every step, retrieval of the
+    # next step overlapping injection of the current one (no timing events)
     t0 = time.perf_counter()
     for i in range(args.warmup, total):
-        step(i)
+        step_pipelined(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     flags = fs.fs_poll_errors(ds.store)
@@ -119,14 +142,23 @@ def main():
         raise RuntimeError(f"device error bits 0x{flags:x}")
     L = ntok.cpu().numpy().astype(np.int64)[args.warmup:]          # [steps, B]
 
-    # timed region 2: the same steps with HIP events around each launch on the
-    # launch stream, for the per-kernel durations the roofline uses
+    # timed region 1b: the same steps on one stream, strictly in order
+    torch.cuda.synchronize()
+    u0 = time.perf_counter()
+    for i in range(args.warmup, total):
+        step_serial(i)
+    torch.cuda.synchronize()
+    u1 = time.perf_counter()
+
+    # timed region 2: the same steps in order with HIP events around each
+    # launch on the launch stream, for the per-kernel durations the roofline
+    # uses
     for i in range(args.warmup, total):
         e0, e1, e2 = ev[i]
         e0.record()
-        ret_calls[i]()
+        ret_s[i]()
         e1.record()
-        inj_calls[i % len(sets)]()
+        inj_s[i]()
         e2.record()
     torch.cuda.synchronize()
 
@@ -170,6 +202,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_in_order": round((u1 - u0) / args.steps * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -28,8 +28,13 @@
  *     legacy default stream).  Every call except create/destroy/poll only
  *     enqueues work and returns; results are ready when the stream reaches
  *     that point.
- *   - A store must not be used from two streams at the same time (shared
- *     scratch); this is not detected.
+ *   - Concurrency on one store (not detected): fs_retrieve_topk calls share
+ *     the score scratch, so they must not overlap one another; on pinned
+ *     stores fs_inject calls share the token-map scratch and the staging
+ *     ring, so they must not overlap one another or an fs_fetch_async.  On
+ *     device stores fs_inject uses no scratch, so one stream may inject
+ *     while another retrieves for a later request (the caller orders each
+ *     inject after the retrieval that produced its ids, e.g. with an event).
  *   - Errors: a call returns a status.  Host-checkable errors return before
  *     anything is enqueued and nothing is written.  Conditions only the GPU
  *     can see set bits in the store's device error word (fs_poll_errors) and
