@@ -57,6 +57,9 @@ def parse():
                    help="requests of the oracle's bounded CPU sample (0 = skip)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--pinned", action="store_true",
+                   help="K/V arenas in pinned host memory: time the per-layer fetch -> inject "
+                        "pipeline against a plain host-to-device copy (the host link is the bound)")
     return p.parse_args()
 
 
@@ -74,6 +77,8 @@ def main():
     from kv_cache_injection_amd.workload import build_store, request_tensors
 
     torch.cuda.set_device(0)
+    if args.pinned:
+        return bench_pinned(args)
     wl = synth.make_workload(args.config, k=args.k)
     s = wl.shape
     nl = args.layers or s.num_layers
@@ -230,6 +235,110 @@ def main():
     ds.close()
 
 
+def bench_pinned(args):
+    """Pinned-host store: per step, retrieval, then for every layer l the
+    fetch of layer l's selected rows over the host link (side stream, staging
+    slot l % 2) and the injection of layer l (main stream).  The fetch of
+    layer l+1 waits only for the injection of layer l-1 (which read the slot
+    it refills), so the host link stays busy while layers are injected.
+    Reported against a plain pinned-host -> device copy of the same bytes."""
+    import numpy as np
+    import torch
+
+    from kv_cache_injection_amd import fs, synth
+    from kv_cache_injection_amd.workload import build_store, request_tensors
+
+    wl = synth.make_workload(args.config, k=args.k)
+    s = wl.shape
+    nl = args.layers or min(8, s.num_layers)
+    layers = list(range(nl))
+    B, k = s.batch, wl.k
+    print(f"[bench] {s.name} pinned: building store ({nl} layers in pinned host memory)",
+          file=sys.stderr, flush=True)
+    ds = build_store(wl, layers, pinned=True, staging_layers=2)
+    kc, vc = synth.make_caches(wl, layers, "cuda")
+    caches = fs.CacheTable(ds.store, kc, vc, kc[0].shape[0])
+    sets = [request_tensors(wl, queries=r["queries"], start_pos=r["start_pos"], block_table=r["block_table"])
+            for r in synth.request_sets(wl, max(args.sets, 1), seed=wl.seed + 1)]
+    user = sets[0]["user"]
+    mb = wl.block_table.shape[1]
+    steps = max(1, min(args.steps, 10))
+    warm = max(1, min(args.warmup, 2))
+    total = warm + steps
+    ids = torch.empty((total, B, k), dtype=torch.int32, device="cuda")
+    ntok = torch.zeros((total, B), dtype=torch.int32, device="cuda")
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+
+    def step(i, inject=True):
+        r = sets[i % len(sets)]
+        fs.fs_retrieve_topk(ds.store, B, user, r["query"], k, ids[i], None, ntok[i])
+        fetched = [torch.cuda.Event() for _ in layers]
+        injected = [torch.cuda.Event() for _ in layers]
+        side.wait_stream(main)                        # ids are ready
+        for l in layers:
+            if l >= 2:
+                side.wait_event(injected[l - 2])      # slot l % 2 is free again
+            fs.fs_fetch_async(ds.store, B, user, ids[i], k, l, l + 1, stream=side)
+            fetched[l].record(side)
+            if inject:
+                main.wait_event(fetched[l])
+                fs.fs_inject(ds.store, l, B, user, ids[i], k, r["block_table"], mb, r["start_pos"], caches)
+                injected[l].record(main)
+            else:
+                injected[l].record(side)
+        main.wait_stream(side)
+
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(warm, total):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    flags = fs.fs_poll_errors(ds.store)
+    if flags:
+        raise RuntimeError(f"device error bits 0x{flags:x}")
+    L = ntok.cpu().numpy().astype(np.int64)[warm:]
+    link_bytes = 4 * int(L.sum()) * nl * s.num_kv_heads * s.head_dim    # K and V rows read once
+    # fetch alone, same steps
+    u0 = time.perf_counter()
+    for i in range(warm, total):
+        step(i, inject=False)
+    torch.cuda.synchronize()
+    u1 = time.perf_counter()
+    # a plain host -> device copy of one step's bytes, pinned source
+    per_step = link_bytes // steps
+    h = torch.empty(per_step, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(per_step, dtype=torch.uint8, device="cuda")
+    d.copy_(h, non_blocking=True)
+    torch.cuda.synchronize()
+    c0 = time.perf_counter()
+    for _ in range(steps):
+        d.copy_(h, non_blocking=True)
+    torch.cuda.synchronize()
+    c1 = time.perf_counter()
+    wall = t1 - t0
+    link = link_bytes / wall / 1e9
+    h2d = per_step * steps / (c1 - c0) / 1e9
+    out = {
+        "metric": "pinned-host KV fetch + inject: host-link GB/s per batch (k=50)",
+        "value": round(link, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(wall / steps * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "fetch_only_ms_per_step": round((u1 - u0) / steps * 1e3, 3),
+        "h2d_copy_probe_GBps": round(h2d, 2), "frac_of_h2d_probe": round(link / h2d, 4),
+        "requests_per_s": round(B * steps / wall, 2),
+        "config": {"workload": f"{s.name} (pinned host arenas): {nl} of {s.num_layers} layers resident, "
+                               f"{s.num_kv_heads} KV heads x {s.head_dim}; {B} request(s) per step, k={k}; "
+                               f"staging ring of 2 layers, per-layer fetch -> inject pipeline",
+                   "batch": B, "k": k, "layers": nl, "mean_segment_tokens": round(float(L.mean()), 1)},
+    }
+    print(json.dumps(out), flush=True)
+    ds.close()
+
+
 def inject_source_digest() -> str:
     """sha256 over the sources of the inject kernel (counters taken on another
     build of it no longer describe it)."""
@@ -259,41 +368,46 @@ def recorded_traffic(config: str, layers: int):
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(wl, ds, layers, n_req):
+def cpu_baseline(wl, ds, layers, n_req, max_host_bytes=16 << 30):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    retrieve + compose + rotate + scatter for ``n_req`` requests over every
-    resident layer, single thread.  Same algorithmic-bytes accounting."""
+    retrieve + compose + rotate + scatter for ``n_req`` requests, single
+    thread, over the resident layers whose arenas fit ``max_host_bytes`` of
+    host memory (all of them for the Llama-shaped store).  Same
+    algorithmic-bytes accounting."""
     import numpy as np
 
     import oracle
     from kv_cache_injection_amd import synth
 
     s = wl.shape
-    print(f"[bench] cpu baseline: copying arenas to host", file=sys.stderr, flush=True)
-    kb = [synth.bf16_bits(t) for t in ds.k_pre]
-    vb = [synth.bf16_bits(t) for t in ds.v]
+    per_layer = 2 * ds.k_pre[0].numel() * 2
+    nl = max(1, min(len(layers), int(max_host_bytes // per_layer)))
+    use = list(range(nl))
+    print(f"[bench] cpu baseline: copying {nl} layer(s) of arenas to host", file=sys.stderr, flush=True)
+    kb = [synth.bf16_bits(ds.k_pre[i]) for i in use]
+    vb = [synth.bf16_bits(ds.v[i]) for i in use]
     nb = s.pool_blocks
     shape = (nb, s.block_size, s.num_kv_heads, s.head_dim)
-    kc = [np.full(shape, synth.SENTINEL_BITS, np.uint16) for _ in layers]
-    vc = [np.full(shape, synth.SENTINEL_BITS, np.uint16) for _ in layers]
+    kc = [np.full(shape, synth.SENTINEL_BITS, np.uint16) for _ in use]
+    vc = [np.full(shape, synth.SENTINEL_BITS, np.uint16) for _ in use]
     total_bytes = 0
     t0 = time.perf_counter()
     sets = synth.request_sets(wl, n_req, seed=wl.seed + 1)   # the bench's first sets
-    for b in range(n_req):
-        r = sets[b]
+    for i in range(n_req):
+        r = sets[i]
         u = int(wl.users[0])
         ids, _ = oracle.retrieve(wl.emb, wl.user_fact_begin, u, r["queries"][0], wl.k)
         L = oracle.inject_request(kb, vb, kc, vc, ids, wl.fact_len, wl.fact_token_begin,
                                   int(r["start_pos"][0]), r["block_table"][0], s.block_size,
-                                  s.rope_theta, layers)
+                                  s.rope_theta, use)
         n_user = int(wl.user_fact_begin[u + 1] - wl.user_fact_begin[u])
-        total_bytes += 8 * L * len(layers) * s.num_kv_heads * s.head_dim + 4 * n_user * s.embed_dim
+        total_bytes += 8 * L * nl * s.num_kv_heads * s.head_dim + 4 * n_user * s.embed_dim
     dt = time.perf_counter() - t0
     return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s",
             "requests_per_s": round(n_req / dt, 4), "cores": 1, "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": f"{n_req} request(s) of the {s.name} workload, {len(layers)} layers, "
-                      f"k={wl.k}: numpy fp64 oracle, one thread"}
+            "sample": f"{n_req} request(s) of the {s.name} workload (the first request of each "
+                      f"set), {nl} layer(s), k={wl.k}: numpy fp64 oracle, one thread"}
 
 
 if __name__ == "__main__":
