@@ -12,6 +12,10 @@
 //                ...), accumulates them in order, then a fixed butterfly
 //                reduces the wave.  The reduction order depends only on the
 //                column, never on the row, which is what makes equal rows tie.
+//                Consecutive requests of one user (up to 8) are scored by one
+//                block, which reads its rows once for all their queries: a
+//                batch of one user's requests scans the table once, not once
+//                per request.
 // top-k kernel   one 1024-thread block per request.  First try: the min and
 //                max of the request's scores define 2048 equal-width value
 //                bins (the bin is a monotone function of the score, so equal
@@ -38,6 +42,7 @@ namespace {
 constexpr int kScoreWaves = 4;
 constexpr int kScoreRowsPerWave = 2;
 constexpr int kScoreRowsPerBlock = kScoreWaves * kScoreRowsPerWave;
+constexpr int kScoreGroup = 8;       // queries of one user scored per block
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kBins = 2048;          // value bins of the threshold search
@@ -78,53 +83,71 @@ struct ScoreArgs {
     int32_t num_users;
     const int32_t* user;
     const float4* query;      // [B][E/4]
+    int32_t batch;
     double* scores;           // [B][stride]
     int32_t stride;
 };
 
+__device__ __forceinline__ void fma4(double& acc, const float4& e, const float4& q) {
+    acc = fma(double(e.x), double(q.x), acc);
+    acc = fma(double(e.y), double(q.y), acc);
+    acc = fma(double(e.z), double(q.z), acc);
+    acc = fma(double(e.w), double(q.w), acc);
+}
+
+// Block (row tile, request b).  Requests of one user that follow each other
+// (within an aligned group of kScoreGroup) are scored together by the block
+// of the first of them: its rows are read once for all their queries.  The
+// other blocks of the run exit at once.  Every score still accumulates the
+// same products in the same order, so it does not depend on the grouping.
 __global__ __launch_bounds__(256) void fs_score_kernel(ScoreArgs a) {
     const int b = blockIdx.y;
     const int u = a.user[b];
     if (u < 0 || u >= a.num_users) return;
+    if (b % kScoreGroup != 0 && a.user[b - 1] == u) return;   // scored by the run's first block
+    int nq = 1;
+    while (nq < kScoreGroup && (b + nq) % kScoreGroup != 0 && b + nq < a.batch && a.user[b + nq] == u) ++nq;
     const int64_t base = a.user_begin[u];
     const int32_t n = static_cast<int32_t>(a.user_begin[u + 1] - base);
     const int32_t row0 = blockIdx.x * kScoreRowsPerBlock;
     if (row0 >= n) return;
-    // the query is read straight from global memory (cached after the first
-    // wave touches it), so its loads overlap the embedding loads
-    const float4* qv = a.query + int64_t(b) * a.e4;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int32_t r0 = row0 + wave * kScoreRowsPerWave;
     const bool v0 = r0 < n, v1 = r0 + 1 < n;
-    const float4* e0 = a.emb + (base + r0) * a.e4;
-    const float4* e1 = e0 + a.e4;
-    double acc0 = 0.0, acc1 = 0.0;
-#pragma unroll 4
+    const float4* e0 = a.emb + (base + (v0 ? r0 : 0)) * a.e4;
+    const float4* e1 = a.emb + (base + (v1 ? r0 + 1 : 0)) * a.e4;
+    // the queries are read straight from global memory (cached after the
+    // first wave touches them), so their loads overlap the embedding loads
+    const float4* qv = a.query + int64_t(b) * a.e4;
+    double acc[kScoreGroup][2];
+#pragma unroll
+    for (int q = 0; q < kScoreGroup; ++q) acc[q][0] = acc[q][1] = 0.0;
+#pragma unroll 2
     for (int c = lane; c < a.e4; c += 64) {
-        const float4 q = qv[c];
-        if (v0) {
-            const float4 e = e0[c];
-            acc0 = fma(double(e.x), double(q.x), acc0);
-            acc0 = fma(double(e.y), double(q.y), acc0);
-            acc0 = fma(double(e.z), double(q.z), acc0);
-            acc0 = fma(double(e.w), double(q.w), acc0);
-        }
-        if (v1) {
-            const float4 e = e1[c];
-            acc1 = fma(double(e.x), double(q.x), acc1);
-            acc1 = fma(double(e.y), double(q.y), acc1);
-            acc1 = fma(double(e.z), double(q.z), acc1);
-            acc1 = fma(double(e.w), double(q.w), acc1);
+        const float4 ea = e0[c];
+        const float4 eb = e1[c];
+#pragma unroll
+        for (int q = 0; q < kScoreGroup; ++q) {
+            if (q < nq) {
+                const float4 qq = qv[int64_t(q) * a.e4 + c];
+                fma4(acc[q][0], ea, qq);
+                fma4(acc[q][1], eb, qq);
+            }
         }
     }
-    acc0 = wave_sum(acc0);
-    acc1 = wave_sum(acc1);
-    if (lane == 0) {
-        double* out = a.scores + int64_t(b) * a.stride;
-        if (v0) out[r0] = acc0;
-        if (v1) out[r0 + 1] = acc1;
+#pragma unroll
+    for (int q = 0; q < kScoreGroup; ++q) {
+        if (q < nq) {
+            const double s0 = wave_sum(acc[q][0]);
+            const double s1 = wave_sum(acc[q][1]);
+            if (lane == 0) {
+                double* out = a.scores + int64_t(b + q) * a.stride;
+                if (v0) out[r0] = s0;
+                if (v1) out[r0 + 1] = s1;
+            }
+        }
     }
 }
 
@@ -476,6 +499,7 @@ hipError_t fsi_launch_retrieve(const RetrieveLaunch& r) {
         sa.num_users = d.num_users;
         sa.user = r.user;
         sa.query = reinterpret_cast<const float4*>(r.query);
+        sa.batch = r.batch;
         sa.scores = st->d_scores;
         sa.stride = st->max_user_facts;
         dim3 grid((st->max_user_facts + kScoreRowsPerBlock - 1) / kScoreRowsPerBlock, r.batch);
