@@ -57,6 +57,9 @@ def parse():
                    help="requests of the oracle's bounded CPU sample (0 = skip)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--overlap", action="store_true",
+                   help="per-layer injection on a side stream under a synthetic per-layer forward "
+                        "(two bf16 GEMMs per layer): how much of the injection stays exposed")
     p.add_argument("--pinned", action="store_true",
                    help="K/V arenas in pinned host memory: time the per-layer fetch -> inject "
                         "pipeline against a plain host-to-device copy (the host link is the bound)")
@@ -79,6 +82,8 @@ def main():
     torch.cuda.set_device(0)
     if args.pinned:
         return bench_pinned(args)
+    if args.overlap:
+        return bench_overlap(args)
     wl = synth.make_workload(args.config, k=args.k)
     s = wl.shape
     nl = args.layers or s.num_layers
@@ -235,6 +240,98 @@ def main():
     ds.close()
 
 
+def bench_overlap(args):
+    """Layer-pipelined injection (device store): per step, retrieval, then
+    fs_inject layer by layer on a side stream with one event per layer, while
+    the main stream runs a synthetic forward whose layer l waits for layer l's
+    event.  The forward is a stand-in load (a prefill chunk through an MLP of
+    the model's width: two bf16 GEMMs per layer), not part of the library.
+    Reported: forward alone, injection alone, both overlapped."""
+    import numpy as np
+    import torch
+
+    from kv_cache_injection_amd import fs, synth
+    from kv_cache_injection_amd.pipeline import LayerInjector
+    from kv_cache_injection_amd.workload import build_store, request_tensors
+
+    wl = synth.make_workload(args.config, k=args.k)
+    s = wl.shape
+    nl = args.layers or s.num_layers
+    layers = list(range(nl))
+    B, k = s.batch, wl.k
+    print(f"[bench] {s.name} overlap: building store ({nl} layers)", file=sys.stderr, flush=True)
+    ds = build_store(wl, layers)
+    kc, vc = synth.make_caches(wl, layers, "cuda")
+    caches = fs.CacheTable(ds.store, kc, vc, kc[0].shape[0])
+    sets = [request_tensors(wl, queries=r["queries"], start_pos=r["start_pos"], block_table=r["block_table"])
+            for r in synth.request_sets(wl, max(args.sets, 1), seed=wl.seed + 1)]
+    user = sets[0]["user"]
+    mb = wl.block_table.shape[1]
+    steps = max(1, min(args.steps, 50))
+    warm = max(1, min(args.warmup, 5))
+    total = warm + steps
+    ids = torch.empty((total, B, k), dtype=torch.int32, device="cuda")
+    ntok = torch.zeros((total, B), dtype=torch.int32, device="cuda")
+    hidden, inter, tokens = 4096, 14336, 512           # Llama-3.1-8B MLP width, one prefill chunk
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed + 7)
+    w_up = [torch.randn((hidden, inter), generator=g, device="cuda", dtype=torch.bfloat16) * 0.02
+            for _ in layers]
+    w_dn = [torch.randn((inter, hidden), generator=g, device="cuda", dtype=torch.bfloat16) * 0.02
+            for _ in layers]
+    x0 = torch.randn((tokens, hidden), generator=g, device="cuda", dtype=torch.bfloat16)
+    inj = LayerInjector(ds.store, caches, nl)
+    ret = [fs.prepare_retrieve_topk(ds.store, B, user, sets[i % len(sets)]["query"], k, ids[i], None,
+                                    ntok[i]) for i in range(total)]
+    calls = [inj.prepare(B, user, ids[i], k, sets[i % len(sets)]["block_table"], mb,
+                         sets[i % len(sets)]["start_pos"]) for i in range(total)]
+
+    def forward(wait_layers: bool):
+        x = x0
+        for l in layers:
+            if wait_layers:
+                inj.wait(l)
+            x = torch.matmul(torch.matmul(x, w_up[l]), w_dn[l])
+        return x
+
+    def run(mode, i):
+        if mode in ("both", "inject"):
+            ret[i]()
+            inj.launch(calls[i])
+        if mode in ("both", "forward"):
+            forward(mode == "both")
+        torch.cuda.current_stream().wait_stream(inj.stream)
+
+    res = {}
+    for mode in ("forward", "inject", "both"):
+        for i in range(warm):
+            run(mode, i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(warm, total):
+            run(mode, i)
+        torch.cuda.synchronize()
+        res[mode] = (time.perf_counter() - t0) / steps * 1e3
+    flags = fs.fs_poll_errors(ds.store)
+    if flags:
+        raise RuntimeError(f"device error bits 0x{flags:x}")
+    exposed = max(0.0, res["both"] - res["forward"])
+    out = {
+        "metric": "layer-pipelined injection under a synthetic per-layer forward: exposed injection time",
+        "value": round(exposed, 4), "unit": "ms per step", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(res["both"], 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "forward_only_ms": round(res["forward"], 4),
+        "retrieve_and_inject_only_ms": round(res["inject"], 4),
+        "hidden_frac": round(1.0 - exposed / res["inject"], 4) if res["inject"] > 0 else None,
+        "config": {"workload": f"{s.name}: {nl} layers, per-layer fs_inject on a side stream; forward "
+                               f"stand-in {tokens} tokens x ({hidden}->{inter}->{hidden}) bf16 GEMMs per layer",
+                   "batch": B, "k": k, "layers": nl},
+    }
+    print(json.dumps(out), flush=True)
+    ds.close()
+
+
 def bench_pinned(args):
     """Pinned-host store: per step, retrieval, then for every layer l the
     fetch of layer l's selected rows over the host link (side stream, staging
@@ -246,6 +343,7 @@ def bench_pinned(args):
     import torch
 
     from kv_cache_injection_amd import fs, synth
+    from kv_cache_injection_amd.pipeline import PinnedLayerInjector
     from kv_cache_injection_amd.workload import build_store, request_tensors
 
     wl = synth.make_workload(args.config, k=args.k)
@@ -268,26 +366,13 @@ def bench_pinned(args):
     ids = torch.empty((total, B, k), dtype=torch.int32, device="cuda")
     ntok = torch.zeros((total, B), dtype=torch.int32, device="cuda")
     main = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
+    pipe = PinnedLayerInjector(ds.store, caches, nl, staging_layers=2)
 
     def step(i, inject=True):
         r = sets[i % len(sets)]
         fs.fs_retrieve_topk(ds.store, B, user, r["query"], k, ids[i], None, ntok[i])
-        fetched = [torch.cuda.Event() for _ in layers]
-        injected = [torch.cuda.Event() for _ in layers]
-        side.wait_stream(main)                        # ids are ready
-        for l in layers:
-            if l >= 2:
-                side.wait_event(injected[l - 2])      # slot l % 2 is free again
-            fs.fs_fetch_async(ds.store, B, user, ids[i], k, l, l + 1, stream=side)
-            fetched[l].record(side)
-            if inject:
-                main.wait_event(fetched[l])
-                fs.fs_inject(ds.store, l, B, user, ids[i], k, r["block_table"], mb, r["start_pos"], caches)
-                injected[l].record(main)
-            else:
-                injected[l].record(side)
-        main.wait_stream(side)
+        pipe.launch(B, user, ids[i], k, r["block_table"], mb, r["start_pos"], inject=inject)
+        pipe.wait_all(main)
 
     for i in range(warm):
         step(i)

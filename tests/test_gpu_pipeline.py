@@ -1,0 +1,99 @@
+"""Layer-pipelined injection (kv_cache_injection_amd.pipeline) on the GPU.
+
+The per-layer pipelines must write exactly what one all-layer fs_inject
+writes (which the parity tests compare with the oracle), whatever runs on the
+other streams meanwhile, and across consecutive batches that reuse the
+staging slots."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from _parity import check_injection, check_retrieval, gpu_retrieve, say
+from kv_cache_injection_amd import fs, synth
+from kv_cache_injection_amd.pipeline import LayerInjector, PinnedLayerInjector
+from kv_cache_injection_amd.workload import build_store, request_tensors
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    return t.view(torch.int16)
+
+
+def test_layer_injector_under_forward_matches_all_layer_inject():
+    wl = synth.make_workload("llama", seed=1003)
+    s = wl.shape
+    layers = [0, 1, 2, 3]
+    say("layer pipeline: building store")
+    ds = build_store(wl, layers)
+    req = request_tensors(wl)
+    B, k = s.batch, wl.k
+    mb = wl.block_table.shape[1]
+    ids, scores, ntok = gpu_retrieve(ds, req, k, B)
+    ref_k, ref_v = synth.make_caches(wl, layers, "cuda")
+    fs.fs_inject(ds.store, fs.FS_ALL_LAYERS, B, req["user"], ids, k, req["block_table"], mb,
+                 req["start_pos"], ref_k, ref_v, ref_k[0].shape[0])
+    kc, vc = synth.make_caches(wl, layers, "cuda")
+    caches = fs.CacheTable(ds.store, kc, vc, kc[0].shape[0])
+    inj = LayerInjector(ds.store, caches, len(layers))
+    calls = inj.prepare(B, req["user"], ids, k, req["block_table"], mb, req["start_pos"])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    x = torch.randn((256, 1024), generator=g, device="cuda")
+    w = torch.randn((1024, 1024), generator=g, device="cuda") * 0.03
+    say("layer pipeline: inject on the side stream under a stand-in forward")
+    inj.launch(calls)
+    for l in layers:
+        inj.wait(l)
+        # the consumer reads layer l's cache only after its event
+        x = torch.tanh(x @ w) + _bits(kc[l])[:1].float().sum() * 0
+    torch.cuda.current_stream().wait_stream(inj.stream)
+    torch.cuda.synchronize()
+    assert fs.fs_poll_errors(ds.store) == 0
+    for l in layers:
+        assert torch.equal(_bits(kc[l]), _bits(ref_k[l])), f"layer {l} K"
+        assert torch.equal(_bits(vc[l]), _bits(ref_v[l])), f"layer {l} V"
+    o = check_retrieval(wl, ids.cpu().numpy(), scores.cpu().numpy(), ntok.cpu().numpy(), [0], k)
+    check_injection(wl, ds, kc, vc, o, [0, 3])
+    ds.close()
+
+
+def test_pinned_layer_pipeline_two_batches_match_device_store():
+    # Mistral shape, 4 layers: the pinned store's arenas are drawn on the GPU
+    # from the same seeds as the device store's, so both hold the same bytes
+    wl = synth.make_workload("large")
+    s = wl.shape
+    layers = [0, 1, 2, 3]
+    B, k = s.batch, wl.k
+    mb = wl.block_table.shape[1]
+    say("pinned pipeline: building device and pinned stores")
+    dev = build_store(wl, layers)
+    pin = build_store(wl, layers, pinned=True, staging_layers=2)
+    sets = [request_tensors(wl, queries=r["queries"], start_pos=r["start_pos"],
+                            block_table=r["block_table"])
+            for r in synth.request_sets(wl, 2, seed=wl.seed + 11)]
+    kc, vc = synth.make_caches(wl, layers, "cuda")
+    caches = fs.CacheTable(pin.store, kc, vc, kc[0].shape[0])
+    pipe = PinnedLayerInjector(pin.store, caches, len(layers), staging_layers=2)
+    ids = [torch.empty((B, k), dtype=torch.int32, device="cuda") for _ in sets]
+    for i, r in enumerate(sets):
+        fs.fs_retrieve_topk(pin.store, B, r["user"], r["query"], k, ids[i], None, None)
+        say(f"pinned pipeline: batch {i}")
+        pipe.launch(B, r["user"], ids[i], k, r["block_table"], mb, r["start_pos"])
+    pipe.wait_all()
+    torch.cuda.synchronize()
+    assert fs.fs_poll_errors(pin.store) == 0
+    # reference: the same two batches through the device store, all layers
+    rk, rv = synth.make_caches(wl, layers, "cuda")
+    for i, r in enumerate(sets):
+        fs.fs_inject(dev.store, fs.FS_ALL_LAYERS, B, r["user"], ids[i], k, r["block_table"], mb,
+                     r["start_pos"], rk, rv, rk[0].shape[0])
+    assert fs.fs_poll_errors(dev.store) == 0
+    for l in layers:
+        assert torch.equal(_bits(kc[l]), _bits(rk[l])), f"layer {l} K"
+        assert torch.equal(_bits(vc[l]), _bits(rv[l])), f"layer {l} V"
+    pin.close()
+    dev.close()
