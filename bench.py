@@ -60,6 +60,10 @@ def parse():
     p.add_argument("--overlap", action="store_true",
                    help="per-layer injection on a side stream under a synthetic per-layer forward "
                         "(two bf16 GEMMs per layer): how much of the injection stays exposed")
+    p.add_argument("--attend", action="store_true",
+                   help="time fs_attend_prefill: query tokens over one layer's injected cache")
+    p.add_argument("--tq", type=int, default=128, help="query tokens per request (--attend)")
+    p.add_argument("--batch", type=int, default=1, help="requests (--attend)")
     p.add_argument("--pinned", action="store_true",
                    help="K/V arenas in pinned host memory: time the per-layer fetch -> inject "
                         "pipeline against a plain host-to-device copy (the host link is the bound)")
@@ -84,6 +88,8 @@ def main():
         return bench_pinned(args)
     if args.overlap:
         return bench_overlap(args)
+    if args.attend:
+        return bench_attend(args)
     wl = synth.make_workload(args.config, k=args.k)
     s = wl.shape
     nl = args.layers or s.num_layers
@@ -237,6 +243,80 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+    ds.close()
+
+
+def bench_attend(args):
+    """fs_attend_prefill on the Llama-3.1-8B head layout (32 query heads, 8 KV
+    heads, head_dim 128): --batch requests of --tq query tokens, each after a
+    context of start + injected segment (start U[0,256) + 50 facts of
+    U[12,48] tokens, about 1.7k positions), one layer.  FLOPs count the two
+    products per attended (token, position, head): 4 * D per pair."""
+    import numpy as np
+    import torch
+
+    from kv_cache_injection_amd import fs, synth
+    from kv_cache_injection_amd.workload import build_store
+
+    wl = synth.make_workload("llama")
+    s = wl.shape
+    B, tq, hq = args.batch, args.tq, 32
+    D = s.head_dim
+    ds = build_store(wl, [0], max_batch=max(B, 1))
+    rng = np.random.default_rng(wl.seed + 5)
+    ctx_len = rng.integers(0, 256, B) + 1488                      # start + mean segment
+    q_pos = ctx_len.astype(np.int32)
+    bs = s.block_size
+    need = int((q_pos.max() + tq + bs - 1) // bs)
+    nb = need * B
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed + 6)
+    kc = torch.randn((nb, bs, s.num_kv_heads, D), generator=g, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((nb, bs, s.num_kv_heads, D), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((B, tq, hq, D), generator=g, device="cuda").to(torch.bfloat16)
+    table = torch.from_numpy(rng.permutation(nb)[: need * B].reshape(B, need).astype(np.int32)).cuda()
+    ctx = torch.zeros(B, dtype=torch.int32, device="cuda")
+    qp = torch.from_numpy(q_pos).cuda()
+    out = torch.empty((B, tq, hq, D), device="cuda")
+    scale = 1.0 / np.sqrt(D)
+
+    def call():
+        fs.fs_attend_prefill(ds.store, B, q, kc, vc, table, need, ctx, qp, scale, out)
+
+    for _ in range(max(args.warmup, 5)):
+        call()
+    torch.cuda.synchronize()
+    steps = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    if fs.fs_poll_errors(ds.store):
+        raise RuntimeError("device error bits set")
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    pairs = sum(int(q_pos[b]) * tq + tq * (tq + 1) // 2 for b in range(B))   # (token, position)
+    flops = 4.0 * D * hq * pairs
+    kv_bytes = sum(2 * (int(q_pos[b]) + tq) * s.num_kv_heads * D * 2 for b in range(B))
+    io_bytes = B * tq * hq * D * (2 + 4)
+    t = float(ms.mean()) * 1e-3
+    tf = flops / t / 1e12
+    out_line = {
+        "metric": "paged-attention prefill over the injected cache: TFLOP/s",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": round(float(ms.mean()), 5), "ms_median": round(float(np.median(ms)), 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tf / 2500.0, 5),
+                     "hbm_GBps_unique": round((kv_bytes + io_bytes) / t / 1e9, 1)},
+        "config": {"workload": f"Llama-3.1-8B heads (32 q / 8 kv, D 128), {B} request(s) x {tq} query "
+                               f"tokens after a context of {int(q_pos.min())}..{int(q_pos.max())} positions, "
+                               f"one layer, block_size {bs}",
+                   "batch": B, "tq": tq},
+    }
+    print(json.dumps(out_line), flush=True)
     ds.close()
 
 
@@ -429,7 +509,7 @@ def inject_source_digest() -> str:
     build of it no longer describe it)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("inject.hip", "fs_internal.h"):
+    for f in ("inject.hip", "fs_internal.h", "fs_device.h"):
         with open(os.path.join(ROOT, "kv_cache_injection_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

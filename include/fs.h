@@ -239,6 +239,51 @@ FS_API fs_status fs_fetch_async(const fs_store* store, int32_t batch,
                          int32_t layer_begin, int32_t layer_end, void* stream);
 
 /*
+ * fs_attend_prefill — the attention read of one layer's injected cache: a
+ * causal prefill of each request's own tokens over the paged K/V cache.
+ * Retrieve-and-inject inference rests on the equivalence of KV states
+ * injected at the intended positions with the same memory given as prompt,
+ * for causal decoders (Theorem 3 as the gist.science summary states it,
+ * "Contributions Clés").
+ *   batch          requests, 1 .. 65535
+ *   num_q_tokens   Tq >= 1 query tokens per request
+ *   num_q_heads    Hq, a multiple of the store's num_kv_heads (at most 8
+ *                  query heads per KV head); query head h reads KV head
+ *                  h / (Hq / num_kv_heads)
+ *   q              device bf16 [batch][Tq][Hq][head_dim], BEFORE RoPE; token
+ *                  j of request b is at position q_pos[b] + j and is rotated
+ *                  here (the store's theta, rotate-half, fp64, one rounding
+ *                  to bf16)
+ *   k_cache, v_cache  device bf16 [num_blocks][block_size][num_kv_heads]
+ *                  [head_dim] of ONE layer, holding rotated K and raw V for
+ *                  every attended position, the query tokens' own included
+ *                  (the caller writes those, as an engine's prefill does)
+ *   block_table    device int32 [batch][max_blocks]: position p lives in
+ *                  block block_table[b][p / block_size], slot p % block_size
+ *   ctx_begin      device int32 [batch]: first attended position
+ *   q_pos          device int32 [batch]: position of query token 0
+ *   scale          softmax scale (typically 1/sqrt(head_dim)), finite, > 0
+ *   out            device fp32 [batch][Tq][Hq][head_dim]: for token j,
+ *                  softmax over p in [ctx_begin, q_pos + j] of
+ *                  scale * <q_j, k_p>, applied to v_p
+ * head_dim must be 128 (else FS_E_UNSUPPORTED).  Precision: Q, K, V bf16;
+ * scores and accumulation fp32 on the matrix cores; the softmax weights are
+ * rounded to bf16 before they multiply V and the normaliser sums the rounded
+ * weights.  Device-checked (the request's output rows are then not written):
+ * FS_ERR_START_POS (ctx_begin < 0, ctx_begin > q_pos, or q_pos + Tq past
+ * INT32_MAX), FS_ERR_BLOCK_SHORT, FS_ERR_BLOCK_ID.  Errors: FS_E_ARG
+ * (null or misaligned: q, caches and out 16-byte aligned), FS_E_RANGE,
+ * FS_E_BLOCKTABLE, FS_E_UNSUPPORTED, FS_E_HIP.  Uses no library scratch, so
+ * it may overlap any other call on the store.
+ */
+FS_API fs_status fs_attend_prefill(const fs_store* store, int32_t batch, int32_t num_q_tokens,
+                                   int32_t num_q_heads, const void* q, const void* k_cache,
+                                   const void* v_cache, int32_t num_blocks,
+                                   const int32_t* block_table, int32_t max_blocks,
+                                   const int32_t* ctx_begin, const int32_t* q_pos, float scale,
+                                   float* out, void* stream);
+
+/*
  * fs_poll_errors — synchronise `stream`, return the device error bits
  * accumulated since the last poll in *flags, and clear them.  Returns
  * FS_E_DEVICE when any bit was set, FS_OK otherwise (FS_E_ARG, FS_E_HIP).

@@ -88,6 +88,23 @@ struct InjectLaunch {
 };
 hipError_t fsi_launch_inject(const InjectLaunch& a);
 
+struct AttendLaunch {
+    const fs_store* st;
+    int32_t batch, num_q_tokens, num_q_heads;
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    int32_t num_blocks;
+    const int32_t* block_table;
+    int32_t max_blocks;
+    const int32_t* ctx_begin;
+    const int32_t* q_pos;
+    float scale;
+    float* out;
+    hipStream_t stream;
+};
+hipError_t fsi_launch_attend(const AttendLaunch& a);
+
 struct FetchLaunch {
     const fs_store* st;
     int32_t layer_begin, layer_end;

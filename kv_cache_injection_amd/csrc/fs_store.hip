@@ -348,6 +348,39 @@ fs_status fs_fetch_async(const fs_store* store, int32_t batch, const int32_t* us
     return FS_OK;
 }
 
+fs_status fs_attend_prefill(const fs_store* store, int32_t batch, int32_t num_q_tokens,
+                            int32_t num_q_heads, const void* q, const void* k_cache,
+                            const void* v_cache, int32_t num_blocks, const int32_t* block_table,
+                            int32_t max_blocks, const int32_t* ctx_begin, const int32_t* q_pos,
+                            float scale, float* out, void* stream) {
+    g_msg[0] = 0;
+    if (!store) return fail(FS_E_ARG, "null store");
+    const fs_store_desc& d = store->desc;
+    if (d.head_dim != 128) return fail(FS_E_UNSUPPORTED, "attention needs head_dim 128 (store has %d)", d.head_dim);
+    if (batch < 1 || batch > 65535) return fail(FS_E_RANGE, "batch %d outside [1, 65535]", batch);
+    if (num_q_tokens < 1) return fail(FS_E_RANGE, "num_q_tokens %d < 1", num_q_tokens);
+    if (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0)
+        return fail(FS_E_RANGE, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                    d.num_kv_heads);
+    if (num_q_heads / d.num_kv_heads > 8)
+        return fail(FS_E_UNSUPPORTED, "more than 8 query heads per KV head");
+    if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(FS_E_ARG, "scale must be finite and > 0");
+    if (!q || !k_cache || !v_cache || !block_table || !ctx_begin || !q_pos || !out)
+        return fail(FS_E_ARG, "null pointer argument");
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+        return fail(FS_E_ARG, "q, caches and out must be 16-byte aligned");
+    if (!aligned(block_table, 4) || !aligned(ctx_begin, 4) || !aligned(q_pos, 4))
+        return fail(FS_E_ARG, "int32 argument not 4-byte aligned");
+    if (max_blocks < 1) return fail(FS_E_BLOCKTABLE, "max_blocks %d < 1", max_blocks);
+    if (num_blocks < 1) return fail(FS_E_BLOCKTABLE, "num_blocks %d < 1", num_blocks);
+    AttendLaunch a{store, batch, num_q_tokens, num_q_heads, q, k_cache, v_cache, num_blocks,
+                   block_table, max_blocks, ctx_begin, q_pos, scale, out,
+                   reinterpret_cast<hipStream_t>(stream)};
+    hipError_t e = fsi_launch_attend(a);
+    if (e != hipSuccess) return hip_fail(e, "attend launch");
+    return FS_OK;
+}
+
 fs_status fs_poll_errors(const fs_store* store, void* stream, uint32_t* flags) {
     g_msg[0] = 0;
     if (!store || !flags) return fail(FS_E_ARG, "null pointer argument");

@@ -42,7 +42,8 @@ FS_KV_DEVICE = 0
 FS_KV_PINNED_HOST = 1
 
 EXPORTS = ("fs_create_store", "fs_destroy_store", "fs_retrieve_topk", "fs_inject",
-           "fs_fetch_async", "fs_poll_errors", "fs_strerror", "fs_last_error_message")
+           "fs_fetch_async", "fs_attend_prefill", "fs_poll_errors", "fs_strerror",
+           "fs_last_error_message")
 
 
 class fs_store_desc(ctypes.Structure):
@@ -84,6 +85,8 @@ def _load() -> ctypes.CDLL:
         "fs_retrieve_topk": (i32, [P, i32, P, P, i32, P, P, P, P]),
         "fs_inject": (i32, [P, i32, i32, P, P, i32, P, i32, P, P, P, i32, P]),
         "fs_fetch_async": (i32, [P, i32, P, P, i32, i32, i32, P]),
+        "fs_attend_prefill": (i32, [P, i32, i32, i32, P, P, P, i32, P, i32, P, P, ctypes.c_float,
+                                    P, P]),
         "fs_poll_errors": (i32, [P, P, ctypes.POINTER(ctypes.c_uint32)]),
         "fs_strerror": (ctypes.c_char_p, [i32]),
         "fs_last_error_message": (ctypes.c_char_p, []),
@@ -267,6 +270,34 @@ def fs_fetch_async(store, batch: int, user: torch.Tensor, ids: torch.Tensor, k: 
         _ptr(ids, torch.int32, shape=(batch, k), name="ids"), int(k),
         int(layer_begin), int(layer_end), _stream(stream))
     _check(st, "fs_fetch_async")
+
+
+def fs_attend_prefill(store, batch: int, q: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, block_table: torch.Tensor, max_blocks: int,
+                      ctx_begin: torch.Tensor, q_pos: torch.Tensor, scale: float,
+                      out: torch.Tensor, stream=None) -> None:
+    """q: bf16 [batch, Tq, Hq, D] before RoPE; k_cache/v_cache: one layer's
+    bf16 [num_blocks, block_size, Hkv, D]; out: fp32 [batch, Tq, Hq, D]."""
+    if q.dim() != 4 or q.shape[0] != batch:
+        raise ValueError(f"q must be [batch, Tq, Hq, D], got {tuple(q.shape)}")
+    _, tq, hq, d = q.shape
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape or k_cache.shape[-1] != d:
+        raise ValueError("k_cache/v_cache must be [num_blocks, block_size, Hkv, D], equal shapes")
+    for name, c in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if c.dtype not in (torch.bfloat16, torch.int16):
+            raise TypeError(f"{name}: dtype {c.dtype}, expected bf16 (or its int16 bits)")
+    nb = k_cache.shape[0]
+    st = _lib.fs_attend_prefill(
+        _handle(store), int(batch), int(tq), int(hq),
+        _ptr(q, torch.bfloat16, shape=(batch, tq, hq, d), name="q"),
+        _ptr(k_cache, k_cache.dtype, name="k_cache"), _ptr(v_cache, v_cache.dtype, name="v_cache"),
+        int(nb),
+        _ptr(block_table, torch.int32, shape=(batch, max_blocks), name="block_table"),
+        int(max_blocks),
+        _ptr(ctx_begin, torch.int32, shape=(batch,), name="ctx_begin"),
+        _ptr(q_pos, torch.int32, shape=(batch,), name="q_pos"), float(scale),
+        _ptr(out, torch.float32, shape=(batch, tq, hq, d), name="out"), _stream(stream))
+    _check(st, "fs_attend_prefill")
 
 
 def fs_poll_errors(store, stream=None) -> int:

@@ -51,7 +51,7 @@ __all__ = [
     "bf16_to_f64", "f64_to_bf16", "score", "select_topk", "decisive_gap",
     "retrieve", "compose", "segment_rows", "placement", "request_problem",
     "rope_inv_freq", "rope_rotate", "inject_request", "expected_rows",
-    "gather_rows",
+    "gather_rows", "causal_attention", "attend_prefill",
 ]
 
 
@@ -279,3 +279,56 @@ def gather_rows(arena: np.ndarray, rows: np.ndarray) -> np.ndarray:
     store can be offloaded to host DRAM] moves bytes only: the staged rows are
     the arena rows, unchanged."""
     return np.array(arena[np.asarray(rows, np.int64)], copy=True)
+
+
+# --------------------------------------------------------------------------
+# Attention read of the injected cache
+# --------------------------------------------------------------------------
+
+def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos, k_pos,
+                     scale: float) -> np.ndarray:
+    """Softmax attention of queries over keys at positions not after their own
+    (a causal decoder's attention, the setting of Theorem 3 as the pages state
+    it [contrib]), in fp64: for query i,
+        out_i = sum_j a_ij v_j,  a_ij = exp(scale <q_i, k_j>) / sum_j' (...)
+    over the keys j with k_pos[j] <= q_pos[i].  q [Nq, D], k and v [Nk, D]."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    q_pos = np.asarray(q_pos, np.int64)
+    k_pos = np.asarray(k_pos, np.int64)
+    out = np.zeros((q.shape[0], v.shape[1]))
+    for i in range(q.shape[0]):
+        sel = k_pos <= q_pos[i]
+        s = scale * (k[sel] @ q[i])
+        w = np.exp(s - s.max())
+        out[i] = (w / w.sum()) @ v[sel]
+    return out
+
+
+def attend_prefill(q_pre: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                   block_table: np.ndarray, block_size: int, ctx_begin: int, q_pos: int,
+                   theta: float, scale: float) -> np.ndarray:
+    """One request's prefill attention over one layer's paged cache.
+
+    q_pre: uint16 bf16 bits [Tq, Hq, D], before RoPE; token j is at position
+    q_pos + j and is rotated by R(q_pos + j) and rounded once to bf16 (the
+    same treatment the injected keys get).  k_cache / v_cache: uint16 bits
+    [num_blocks, block_size, Hkv, D]; position p is read from
+    (block_table[p // block_size], p % block_size).  Query head h reads KV head
+    h // (Hq / Hkv).  Token j attends to positions ctx_begin .. q_pos + j.
+    Returns fp64 [Tq, Hq, D]."""
+    tq, hq, D = q_pre.shape
+    hkv = k_cache.shape[2]
+    group = hq // hkv
+    qpos = q_pos + np.arange(tq, dtype=np.int64)
+    qr = bf16_to_f64(f64_to_bf16(rope_rotate(bf16_to_f64(q_pre), qpos[:, None], theta)))
+    kpos = np.arange(ctx_begin, q_pos + tq, dtype=np.int64)
+    blk, slot = placement(kpos, block_table, block_size)
+    kr = bf16_to_f64(k_cache[blk, slot])             # [N, Hkv, D]
+    vr = bf16_to_f64(v_cache[blk, slot])
+    out = np.zeros((tq, hq, D))
+    for h in range(hq):
+        g = h // group
+        out[:, h] = causal_attention(qr[:, h], kr[:, g], vr[:, g], qpos, kpos, scale)
+    return out
