@@ -279,9 +279,11 @@ def bench_attend(args):
     qp = torch.from_numpy(q_pos).cuda()
     out = torch.empty((B, tq, hq, D), device="cuda")
     scale = 1.0 / np.sqrt(D)
+    ws_bytes = fs.fs_attend_workspace_size(ds.store, B, tq, hq)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
 
     def call():
-        fs.fs_attend_prefill(ds.store, B, q, kc, vc, table, need, ctx, qp, scale, out)
+        fs.fs_attend_prefill(ds.store, B, q, kc, vc, table, need, ctx, qp, scale, out, ws)
 
     for _ in range(max(args.warmup, 5)):
         call()
@@ -314,7 +316,7 @@ def bench_attend(args):
         "config": {"workload": f"Llama-3.1-8B heads (32 q / 8 kv, D 128), {B} request(s) x {tq} query "
                                f"tokens after a context of {int(q_pos.min())}..{int(q_pos.max())} positions, "
                                f"one layer, block_size {bs}",
-                   "batch": B, "tq": tq},
+                   "batch": B, "tq": tq, "workspace_bytes": ws_bytes},
     }
     print(json.dumps(out_line), flush=True)
     ds.close()

@@ -57,6 +57,7 @@
 #ifndef FS_H_
 #define FS_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 /* the library is built with hidden visibility; only these entry points are exported */
@@ -266,10 +267,17 @@ FS_API fs_status fs_fetch_async(const fs_store* store, int32_t batch,
  *   out            device fp32 [batch][Tq][Hq][head_dim]: for token j,
  *                  softmax over p in [ctx_begin, q_pos + j] of
  *                  scale * <q_j, k_p>, applied to v_p
+ *   workspace      device memory of workspace_bytes bytes (16-byte aligned),
+ *                  or NULL.  When one pass per (16 query tokens, KV head,
+ *                  request) would leave the device idle, the context is split
+ *                  into ranges whose partial results go here and are merged
+ *                  by a second launch; fs_attend_workspace_size gives the
+ *                  bytes for the full split.  A smaller workspace splits less,
+ *                  NULL not at all; the result is the same up to rounding.
+ *                  Calls that share a workspace must not overlap.
  * head_dim must be 128 (else FS_E_UNSUPPORTED).  Precision: Q, K, V bf16;
  * scores and accumulation fp32 on the matrix cores; the softmax weights are
- * rounded to bf16 before they multiply V and the normaliser sums the rounded
- * weights.  Device-checked (the request's output rows are then not written):
+ * rounded to bf16 before they multiply V (the normaliser sums them in fp32).  Device-checked (the request's output rows are then not written):
  * FS_ERR_START_POS (ctx_begin < 0, ctx_begin > q_pos, or q_pos + Tq past
  * INT32_MAX), FS_ERR_BLOCK_SHORT, FS_ERR_BLOCK_ID.  Errors: FS_E_ARG
  * (null or misaligned: q, caches and out 16-byte aligned), FS_E_RANGE,
@@ -281,7 +289,17 @@ FS_API fs_status fs_attend_prefill(const fs_store* store, int32_t batch, int32_t
                                    const void* v_cache, int32_t num_blocks,
                                    const int32_t* block_table, int32_t max_blocks,
                                    const int32_t* ctx_begin, const int32_t* q_pos, float scale,
-                                   float* out, void* stream);
+                                   float* out, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
+ * fs_attend_workspace_size — bytes of workspace fs_attend_prefill uses for
+ * this batch shape at its full context split (0 when it would not split).
+ * Errors: FS_E_ARG, FS_E_RANGE.
+ */
+FS_API fs_status fs_attend_workspace_size(const fs_store* store, int32_t batch,
+                                          int32_t num_q_tokens, int32_t num_q_heads,
+                                          size_t* bytes);
 
 /*
  * fs_poll_errors — synchronise `stream`, return the device error bits

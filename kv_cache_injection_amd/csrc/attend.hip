@@ -15,13 +15,18 @@
 // for keys, so Q and K carry the same rounding.
 //
 // One block = 16 query tokens x one KV head (all the query heads of its GQA
-// group).  Scores and P.V run on the matrix cores (16x16x16 bf16 MFMA, fp32
-// accumulation); softmax is online in fp32 (exp2).  Scores are computed
-// transposed, S^T = K Q^T, so that each lane's four scores are exactly the
-// four P entries it must supply as the A operand of P V: no shuffle of P.
-// K tiles of 16 positions are staged in LDS row-major, V tiles transposed
-// (d-major), double-buffered, with the next tile's global loads in flight
-// while the current one is consumed.
+// group, one per wave, two per wave for groups of 5..8).  Scores and P.V run
+// on the matrix cores (gfx950 16x16x32 bf16 MFMA, fp32 accumulation);
+// softmax is online in fp32 (exp2); the weights are rounded to bf16 for P.V
+// and summed unrounded for the normaliser.  Both products are computed transposed,
+// S^T = K Q^T and O^T += V^T P^T: a lane's scores are then exactly the P^T
+// entries it supplies, and the O^T column it accumulates is the query whose
+// softmax state it holds, so rescaling and normalising need no shuffles; only
+// the running maximum is reduced across lanes, once per 64 positions.  The
+// contraction index of P.V maps to positions in the order the score tiles
+// produce them (any order works if both operands agree).  K/V tiles of 64
+// positions are staged in LDS (K row-major, V transposed), with the next
+// tile's global loads in flight while the current one is consumed.
 
 #include <hip/hip_runtime.h>
 
@@ -35,11 +40,13 @@ using fsd::wave_or;
 
 constexpr int kD = 128;               // head dim handled
 constexpr int kQT = 16;               // query tokens per block
-constexpr int kKT = 16;               // cache positions per tile
+constexpr int kKT = 64;               // cache positions per tile
 constexpr int kThreads = 256;         // 4 waves
 constexpr int kWaves = kThreads / 64;
+constexpr int kKPad = kD + 8;         // sK row: 272 bytes, 16-byte aligned, spreads banks
+constexpr int kVPad = kKT + 4;        // sVt row: 136 bytes, 8-byte aligned, spreads banks
 
-typedef short s4 __attribute__((ext_vector_type(4)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 struct AttendArgs {
@@ -55,7 +62,13 @@ struct AttendArgs {
     float scale_log2;                 // softmax scale * log2(e)
     float* out;                       // [B][Tq][Hq][D] fp32
     uint32_t* err;
+    int32_t splits;                   // context split into this many ranges (1: no workspace)
+    float* part_o;                    // [splits][B][Tq][Hq][D] unnormalised partial outputs
+    float2* part_ml;                  // [splits][B][Tq][Hq] (running max, weight sum)
 };
+
+constexpr int kBtCache = 1024;        // block-table entries a block caches in LDS
+constexpr int kMaxSplits = 16;
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
     uint32_t u = __float_as_uint(x);
@@ -65,23 +78,40 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-template <int kHS>                    // head slots per wave: group <= 4 * kHS
-__global__ __launch_bounds__(kThreads) void fs_attend_kernel(AttendArgs a) {
-    __shared__ uint16_t sK[2][kKT][kD + 8];      // [pos][d], rows padded against bank conflicts
-    __shared__ uint16_t sVt[2][kD][kKT + 4];     // [d][pos], rows padded against bank conflicts
-    __shared__ int s_ok;
+__device__ __forceinline__ __bf16 as_bf16(uint16_t h) {
+    __bf16 r;
+    __builtin_memcpy(&r, &h, 2);
+    return r;
+}
 
-    const int qt = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+template <int kHS>                    // head slots per wave: group <= 4 * kHS
+__global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 1) void fs_attend_kernel(AttendArgs a) {
+    // the fp64 (cos, sin) table of the block's queries is only needed before
+    // the first tile, so it shares storage with the K/V tiles
+    constexpr int kTileBytes = (kKT * kKPad + kD * kVPad) * 2;
+    constexpr int kCSBytes = kQT * (kD / 2) * 16;
+    __shared__ __attribute__((aligned(16))) unsigned char s_raw[kTileBytes > kCSBytes ? kTileBytes : kCSBytes];
+    __shared__ int s_bt[kBtCache];
+    __shared__ int s_ok;
+    auto sK = reinterpret_cast<uint16_t(*)[kKPad]>(s_raw);                       // [pos][d]
+    auto sVt = reinterpret_cast<uint16_t(*)[kVPad]>(s_raw + kKT * kKPad * 2);   // [d][pos]
+    auto s_cs = reinterpret_cast<double2(*)[kD / 2]>(s_raw);                    // [query][i]
+
+    const int qt = blockIdx.x / a.splits, sp = blockIdx.x - qt * a.splits;
+    const int hk = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int col = lane & 15;        // S^T column = query; O column = d within a chunk
+    const int col = lane & 15;        // the query this lane's S^T / O^T column holds
     const int grp = lane >> 4;        // 4-row group of the MFMA layouts
     const int c0 = a.ctx_begin[b];
     const int qp0 = a.q_pos[b];
     const int64_t bs_mask = (int64_t(1) << a.log2_block) - 1;
     const int32_t* bt = a.bt + int64_t(b) * a.max_blocks;
+    const int j_lo = qt * kQT;
+    const int jq = j_lo + col;
+    const bool q_real = jq < a.tq;
 
-    // ---- validation of the request (every block checks, block (0, 0) reports)
+    // ---- validation of the request (every block checks, one block reports)
     if (wave == 0) {
         uint32_t bits = 0;
         const int64_t last = int64_t(qp0) + a.tq - 1;
@@ -98,23 +128,65 @@ __global__ __launch_bounds__(kThreads) void fs_attend_kernel(AttendArgs a) {
         bits = wave_or(bits);
         if (lane == 0) {
             s_ok = bits == 0;
-            if (bits && qt == 0 && hk == 0) atomicOr(a.err, bits);
+            if (bits && qt == 0 && hk == 0 && sp == 0) atomicOr(a.err, bits);
         }
     }
     __syncthreads();
-    if (!s_ok) return;
+    if (!s_ok) {
+        // a split run marks its partials so the combine writes nothing
+        if (a.splits > 1 && q_real) {
+#pragma unroll
+            for (int hs = 0; hs < kHS; ++hs) {
+                const int hw = wave + kWaves * hs;
+                if (hw < a.group && grp == 0)
+                    a.part_ml[((int64_t(sp) * gridDim.z + b) * a.tq + jq) * a.hq + hk * a.group + hw] =
+                        make_float2(__builtin_nanf(""), 0.0f);
+            }
+        }
+        return;
+    }
 
-    const int j_lo = qt * kQT;
     const int j_hi = min(a.tq, j_lo + kQT) - 1;            // last real query of the block
     const int p_end = qp0 + j_hi;                           // last position any of them reads
     const int ntiles = (p_end - c0) / kKT + 1;
-    const int jq = j_lo + col;                              // this lane's query (S^T column)
-    const bool q_real = jq < a.tq;
+    const int tps = (ntiles + a.splits - 1) / a.splits;     // tiles per split
+    const int t_begin = sp * tps;
+    const int t_end = min(ntiles, t_begin + tps);
     const int qpos = qp0 + jq;
+    if (t_begin >= t_end) {
+        // nothing of the context falls in this split: an empty partial
+        if (q_real && grp == 0) {
+#pragma unroll
+            for (int hs = 0; hs < kHS; ++hs) {
+                const int hw = wave + kWaves * hs;
+                if (hw < a.group)
+                    a.part_ml[((int64_t(sp) * gridDim.z + b) * a.tq + jq) * a.hq + hk * a.group + hw] =
+                        make_float2(-1e30f, 0.0f);
+            }
+        }
+        return;
+    }
 
-    // ---- Q fragments (B operand of S^T = K Q^T), rotated and rounded to bf16
-    // lane holds Q[jq][kk*16 + 4*grp + e]; chunks kk and kk+4 pair i with i+64
-    s4 qf[kHS][8];
+    // ---- block-table entries of this block's positions, cached in LDS
+    const int64_t e_first = int64_t(c0 + t_begin * kKT) >> a.log2_block;
+    const int64_t e_last = int64_t(min(p_end, c0 + t_end * kKT - 1)) >> a.log2_block;
+    const bool bt_cached = e_last - e_first + 1 <= kBtCache;
+    if (bt_cached)
+        for (int64_t j = e_first + threadIdx.x; j <= e_last; j += kThreads) s_bt[j - e_first] = bt[j];
+
+    // ---- fp64 (cos, sin) of (position of query j_lo + qq) * w_i, shared by the heads
+    for (int e = threadIdx.x; e < kQT * (kD / 2); e += kThreads) {
+        const int qq = e / (kD / 2);
+        const int i = e - qq * (kD / 2);
+        double sv, cv;
+        sincos(static_cast<double>(qp0 + j_lo + qq) * a.inv_freq[i], &sv, &cv);
+        s_cs[qq][i] = make_double2(cv, sv);
+    }
+    __syncthreads();
+
+    // ---- Q fragments (B operand of S^T = K Q^T), rotated and rounded to bf16:
+    // lane holds Q[jq][kk*32 + 8*grp + e]; chunks kk and kk+2 pair i with i+64
+    b8 qf[kHS][4];
 #pragma unroll
     for (int hs = 0; hs < kHS; ++hs) {
         const int hw = wave + kWaves * hs;
@@ -122,142 +194,207 @@ __global__ __launch_bounds__(kThreads) void fs_attend_kernel(AttendArgs a) {
         const uint16_t* qrow = a.q + ((int64_t(b) * a.tq + (q_real ? jq : 0)) * a.hq + hk * a.group +
                                       (hw < a.group ? hw : 0)) * kD;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = kk * 16 + 4 * grp + e;
+            for (int e = 0; e < 8; ++e) {
+                const int i = kk * 32 + 8 * grp + e;
                 uint16_t y1 = 0, y2 = 0;
                 if (hv) {
                     const double x1 = bf16_to_f32(qrow[i]);
                     const double x2 = bf16_to_f32(qrow[i + kD / 2]);
-                    double sv, cv;
-                    sincos(static_cast<double>(qpos) * a.inv_freq[i], &sv, &cv);
-                    y1 = static_cast<uint16_t>(f64_to_bf16_bits(fma(x1, cv, -(x2 * sv))));
-                    y2 = static_cast<uint16_t>(f64_to_bf16_bits(fma(x2, cv, x1 * sv)));
+                    const double2 cs = s_cs[col][i];
+                    y1 = static_cast<uint16_t>(f64_to_bf16_bits(fma(x1, cs.x, -(x2 * cs.y))));
+                    y2 = static_cast<uint16_t>(f64_to_bf16_bits(fma(x2, cs.x, x1 * cs.y)));
                 }
-                qf[hs][kk][e] = static_cast<short>(y1);
-                qf[hs][kk + 4][e] = static_cast<short>(y2);
+                qf[hs][kk][e] = as_bf16(y1);
+                qf[hs][kk + 2][e] = as_bf16(y2);
             }
         }
     }
+    __syncthreads();                                        // the table's storage becomes tiles
 
+    // O^T chunks: o[hs][dc][i] = O[jq][dc*16 + 4*grp + i]
     f4 o[kHS][8];
-    float m[kHS], l[kHS];
+    float m[kHS], lp[kHS];            // running max (uniform over a column), partial sum (this lane)
 #pragma unroll
     for (int hs = 0; hs < kHS; ++hs) {
         m[hs] = -1e30f;
-        l[hs] = 0.0f;
+        lp[hs] = 0.0f;
 #pragma unroll
         for (int dc = 0; dc < 8; ++dc) o[hs][dc] = f4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    // ---- K/V tile staging: thread -> (position tid/16, 16-byte vector tid%16)
-    const int lpos = threadIdx.x >> 4;
+    // ---- tile staging: thread -> 16-byte vector lvec of positions 4*lq .. 4*lq+3
     const int lvec = threadIdx.x & 15;
-    uint4 kreg = make_uint4(0, 0, 0, 0), vreg = make_uint4(0, 0, 0, 0);
+    const int lq = threadIdx.x >> 4;
+    uint4 kr[4], vr[4];
     auto gload = [&](int t) {
-        const int p = c0 + t * kKT + lpos;
-        if (p <= p_end) {
-            const int blk = bt[p >> a.log2_block];
-            const int64_t row = (int64_t(blk) << a.log2_block) | (p & bs_mask);
-            const int64_t off = (row * a.hkv + hk) * kD + lvec * 8;
-            kreg = *reinterpret_cast<const uint4*>(a.kc + off);
-            vreg = *reinterpret_cast<const uint4*>(a.vc + off);
-        } else {
-            kreg = make_uint4(0, 0, 0, 0);
-            vreg = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int p = c0 + t * kKT + 4 * lq + r;
+            if (p <= p_end) {
+                const int64_t ei = p >> a.log2_block;
+                const int blk = bt_cached ? s_bt[ei - e_first] : bt[ei];
+                const int64_t row = (int64_t(blk) << a.log2_block) | (p & bs_mask);
+                const int64_t off = (row * a.hkv + hk) * kD + lvec * 8;
+                kr[r] = *reinterpret_cast<const uint4*>(a.kc + off);
+                vr[r] = *reinterpret_cast<const uint4*>(a.vc + off);
+            } else {
+                kr[r] = make_uint4(0, 0, 0, 0);
+                vr[r] = make_uint4(0, 0, 0, 0);
+            }
         }
     };
-    auto lstore = [&](int buf) {
-        *reinterpret_cast<uint4*>(&sK[buf][lpos][lvec * 8]) = kreg;
-        const uint32_t w[4] = {vreg.x, vreg.y, vreg.z, vreg.w};
+    auto lstore = [&]() {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sVt[buf][lvec * 8 + 2 * e][lpos] = static_cast<uint16_t>(w[e] & 0xFFFFu);
-            sVt[buf][lvec * 8 + 2 * e + 1][lpos] = static_cast<uint16_t>(w[e] >> 16);
+        for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4*>(&sK[4 * lq + r][lvec * 8]) = kr[r];
+        // V transposed: for each d of the vector, the 4 positions side by side
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t x0 = (&vr[0].x)[w], x1 = (&vr[1].x)[w], x2 = (&vr[2].x)[w], x3 = (&vr[3].x)[w];
+            const uint2 lo = make_uint2((x0 & 0xFFFFu) | (x1 << 16), (x2 & 0xFFFFu) | (x3 << 16));
+            const uint2 hi = make_uint2((x0 >> 16) | (x1 & 0xFFFF0000u), (x2 >> 16) | (x3 & 0xFFFF0000u));
+            *reinterpret_cast<uint2*>(&sVt[lvec * 8 + 2 * w][4 * lq]) = lo;
+            *reinterpret_cast<uint2*>(&sVt[lvec * 8 + 2 * w + 1][4 * lq]) = hi;
         }
     };
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < ntiles) gload(t + 1);
-        const int pbase = c0 + t * kKT + 4 * grp;           // positions of this lane's 4 scores
+    gload(t_begin);
+    for (int t = t_begin; t < t_end; ++t) {
+        lstore();
+        __syncthreads();                                    // tile t staged
+        if (t + 1 < t_end) gload(t + 1);                   // in flight during the math
+        const int tbase = c0 + t * kKT;
 #pragma unroll
         for (int hs = 0; hs < kHS; ++hs) {
             if (wave + kWaves * hs >= a.group) continue;    // uniform over the wave
-            f4 st = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            // S^T for 4 sub-tiles of 16 positions: st[sub][i] = S[jq][tbase + 16*sub + 4*grp + i]
+            f4 st[4];
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const s4 ka = *reinterpret_cast<const s4*>(&sK[buf][col][kk * 16 + 4 * grp]);
-                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, qf[hs][kk], st, 0, 0, 0);
+            for (int sub = 0; sub < 4; ++sub) {
+                st[sub] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const b8 ka = *reinterpret_cast<const b8*>(&sK[16 * sub + col][kk * 32 + 8 * grp]);
+                    st[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[hs][kk], st[sub], 0, 0, 0);
+                }
             }
-            // st[i] = S^T[position pbase + i][query jq]
-            float sv[4];
+            // causal mask only where the tile reaches past the block's first
+            // query position; columns of absent queries are never written
+            const bool full = tbase + kKT - 1 <= qp0 + j_lo;
             float tmax = -1e30f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = q_real && (pbase + i <= qpos);
-                sv[i] = ok ? st[i] * a.scale_log2 : -1e30f;
-                tmax = fmaxf(tmax, sv[i]);
+            for (int sub = 0; sub < 4; ++sub) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x = st[sub][i] * a.scale_log2;
+                    if (!full && tbase + 16 * sub + 4 * grp + i > qpos) x = -1e30f;
+                    st[sub][i] = x;
+                    tmax = fmaxf(tmax, x);
+                }
             }
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
             const float m_new = fmaxf(m[hs], tmax);
-            const float alpha = exp2f(m[hs] - m_new);
-            s4 pa;
+            const float alpha = __builtin_amdgcn_exp2f(m[hs] - m_new);
+            m[hs] = m_new;
+            // P^T fragments for the two 32-position halves: k = 8*grp + e maps to
+            // position 32*hh + 16*(e/4) + 4*grp + e%4, the lane's own scores
+            b8 pb[2];
             float psum = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint16_t pb = f32_to_bf16_rne(exp2f(sv[i] - m_new));
-                pa[i] = static_cast<short>(pb);
-                psum += bf16_to_f32(pb);                      // normalise with the weights used
-            }
-            psum += __shfl_xor(psum, 16, 64);
-            psum += __shfl_xor(psum, 32, 64);
-            l[hs] = l[hs] * alpha + psum;
-            m[hs] = m_new;
-            // O rows are queries 4*grp + i: their rescale factors sit in lanes
-            // whose column is that query
+            for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float ai = __shfl(alpha, 4 * grp + i, 64);
-#pragma unroll
-                for (int dc = 0; dc < 8; ++dc) o[hs][dc][i] *= ai;
+                for (int e = 0; e < 8; ++e) {
+                    const float pe = __builtin_amdgcn_exp2f(st[2 * hh + e / 4][e % 4] - m_new);
+                    pb[hh][e] = static_cast<__bf16>(pe);
+                    psum += pe;
+                }
             }
+            lp[hs] = lp[hs] * alpha + psum;
 #pragma unroll
             for (int dc = 0; dc < 8; ++dc) {
-                const s4 vb = *reinterpret_cast<const s4*>(&sVt[buf][dc * 16 + col][4 * grp]);
-                o[hs][dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[hs][dc], 0, 0, 0);
+                o[hs][dc] *= alpha;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    // A = V^T row dc*16 + col, in the position order of pb
+                    const uint16_t* vrow = &sVt[dc * 16 + col][32 * hh + 4 * grp];
+                    const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
+                    const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
+                    const b8 va = __builtin_bit_cast(b8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+                    o[hs][dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hh], o[hs][dc], 0, 0, 0);
+                }
             }
         }
-        if (t + 1 < ntiles) lstore(buf ^ 1);
-        __syncthreads();
+        __syncthreads();                                    // tile t consumed
     }
 
-    // ---- normalise and write: lane holds O[query j_lo + 4*grp + i][dc*16 + col]
+    // ---- lane holds O[jq][dc*16 + 4*grp .. +3] (unnormalised)
 #pragma unroll
     for (int hs = 0; hs < kHS; ++hs) {
         const int hw = wave + kWaves * hs;
         if (hw >= a.group) continue;
-        const float linv = l[hs] > 0.0f ? 1.0f / l[hs] : 0.0f;
-        const int h = hk * a.group + hw;
+        float l = lp[hs];
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        if (!q_real) continue;
+        const int64_t row = (int64_t(b) * a.tq + jq) * a.hq + hk * a.group + hw;
+        if (a.splits == 1) {
+            const float linv = 1.0f / l;
+            float* orow = a.out + row * kD + 4 * grp;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float li = __shfl(linv, 4 * grp + i, 64);
-            const int jo = j_lo + 4 * grp + i;
-            if (jo < a.tq) {
-                float* orow = a.out + ((int64_t(b) * a.tq + jo) * a.hq + h) * kD;
+            for (int dc = 0; dc < 8; ++dc) *reinterpret_cast<f4*>(orow + dc * 16) = o[hs][dc] * linv;
+        } else {
+            const int64_t prow = int64_t(sp) * gridDim.z * a.tq * a.hq + row;
+            float* orow = a.part_o + prow * kD + 4 * grp;
 #pragma unroll
-                for (int dc = 0; dc < 8; ++dc) orow[dc * 16 + col] = o[hs][dc][i] * li;
-            }
+            for (int dc = 0; dc < 8; ++dc) *reinterpret_cast<f4*>(orow + dc * 16) = o[hs][dc];
+            if (grp == 0) a.part_ml[prow] = make_float2(m[hs], l);
         }
     }
 }
 
+// Merge of the split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+// with M = max_s m_s.  One thread per (row, d); a NaN max marks a rejected
+// request, whose rows are left unwritten.
+__global__ __launch_bounds__(256) void fs_attend_combine_kernel(AttendArgs a, int64_t rows) {
+    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t row = idx / kD;
+    if (row >= rows) return;
+    const int d = static_cast<int>(idx - row * kD);
+    float mx = -1e30f;
+    bool bad = false;
+    for (int s2 = 0; s2 < a.splits; ++s2) {
+        const float2 ml = a.part_ml[int64_t(s2) * rows + row];
+        if (ml.x != ml.x) bad = true;
+        mx = fmaxf(mx, ml.x);
+    }
+    if (bad) return;
+    float num = 0.0f, den = 0.0f;
+    for (int s2 = 0; s2 < a.splits; ++s2) {
+        const float2 ml = a.part_ml[int64_t(s2) * rows + row];
+        const float w = __builtin_amdgcn_exp2f(ml.x - mx);
+        if (w > 0.0f) {                  // empty splits leave no partial output
+            den += w * ml.y;
+            num += w * a.part_o[(int64_t(s2) * rows + row) * kD + d];
+        }
+    }
+    a.out[row * kD + d] = num / den;
+}
+
 }  // namespace
+
+int fsi_attend_splits(const fs_store* st, int32_t batch, int32_t num_q_tokens) {
+    const int64_t base = int64_t((num_q_tokens + kQT - 1) / kQT) * st->desc.num_kv_heads * batch;
+    int64_t sp = (2 * int64_t(st->num_cus) + base - 1) / base;
+    return static_cast<int>(sp < 1 ? 1 : (sp > kMaxSplits ? kMaxSplits : sp));
+}
+
+size_t fsi_attend_workspace_bytes(int splits, int32_t batch, int32_t num_q_tokens, int32_t num_q_heads) {
+    if (splits <= 1) return 0;
+    const size_t rows = size_t(batch) * num_q_tokens * num_q_heads;
+    return size_t(splits) * rows * (kD * sizeof(float) + sizeof(float2));
+}
 
 hipError_t fsi_launch_attend(const AttendLaunch& r) {
     const fs_store* st = r.st;
@@ -280,11 +417,28 @@ hipError_t fsi_launch_attend(const AttendLaunch& r) {
     a.scale_log2 = r.scale * 1.4426950408889634f;
     a.out = r.out;
     a.err = st->d_err;
-    const dim3 grid(static_cast<unsigned>((r.num_q_tokens + kQT - 1) / kQT),
+    // split the context when one range per (query tile, KV head, request)
+    // would leave the device idle and the workspace holds the partials
+    int splits = fsi_attend_splits(st, r.batch, r.num_q_tokens);
+    while (splits > 1 && fsi_attend_workspace_bytes(splits, r.batch, r.num_q_tokens, r.num_q_heads) >
+                             r.workspace_bytes)
+        --splits;
+    if (!r.workspace) splits = 1;
+    a.splits = splits;
+    if (splits > 1) {
+        const size_t rows = size_t(r.batch) * r.num_q_tokens * r.num_q_heads;
+        a.part_o = static_cast<float*>(r.workspace);
+        a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(r.workspace) + size_t(splits) * rows * kD * sizeof(float));
+    }
+    const dim3 grid(static_cast<unsigned>((r.num_q_tokens + kQT - 1) / kQT * splits),
                     static_cast<unsigned>(d.num_kv_heads), static_cast<unsigned>(r.batch));
     if (a.group <= kWaves)
         fs_attend_kernel<1><<<grid, kThreads, 0, r.stream>>>(a);
     else
         fs_attend_kernel<2><<<grid, kThreads, 0, r.stream>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    const int64_t rows = int64_t(r.batch) * r.num_q_tokens * r.num_q_heads;
+    fs_attend_combine_kernel<<<static_cast<unsigned>((rows * kD + 255) / 256), 256, 0, r.stream>>>(a, rows);
     return hipGetLastError();
 }

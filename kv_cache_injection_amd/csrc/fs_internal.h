@@ -101,9 +101,14 @@ struct AttendLaunch {
     const int32_t* q_pos;
     float scale;
     float* out;
+    void* workspace;
+    size_t workspace_bytes;
     hipStream_t stream;
 };
 hipError_t fsi_launch_attend(const AttendLaunch& a);
+// context splits the launch would use, and the workspace that many need
+int fsi_attend_splits(const fs_store* st, int32_t batch, int32_t num_q_tokens);
+size_t fsi_attend_workspace_bytes(int splits, int32_t batch, int32_t num_q_tokens, int32_t num_q_heads);
 
 struct FetchLaunch {
     const fs_store* st;

@@ -352,7 +352,8 @@ fs_status fs_attend_prefill(const fs_store* store, int32_t batch, int32_t num_q_
                             int32_t num_q_heads, const void* q, const void* k_cache,
                             const void* v_cache, int32_t num_blocks, const int32_t* block_table,
                             int32_t max_blocks, const int32_t* ctx_begin, const int32_t* q_pos,
-                            float scale, float* out, void* stream) {
+                            float scale, float* out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
     g_msg[0] = 0;
     if (!store) return fail(FS_E_ARG, "null store");
     const fs_store_desc& d = store->desc;
@@ -373,11 +374,23 @@ fs_status fs_attend_prefill(const fs_store* store, int32_t batch, int32_t num_q_
         return fail(FS_E_ARG, "int32 argument not 4-byte aligned");
     if (max_blocks < 1) return fail(FS_E_BLOCKTABLE, "max_blocks %d < 1", max_blocks);
     if (num_blocks < 1) return fail(FS_E_BLOCKTABLE, "num_blocks %d < 1", num_blocks);
+    if (workspace && !aligned(workspace, 16)) return fail(FS_E_ARG, "workspace not 16-byte aligned");
     AttendLaunch a{store, batch, num_q_tokens, num_q_heads, q, k_cache, v_cache, num_blocks,
                    block_table, max_blocks, ctx_begin, q_pos, scale, out,
-                   reinterpret_cast<hipStream_t>(stream)};
+                   workspace, workspace ? workspace_bytes : 0, reinterpret_cast<hipStream_t>(stream)};
     hipError_t e = fsi_launch_attend(a);
     if (e != hipSuccess) return hip_fail(e, "attend launch");
+    return FS_OK;
+}
+
+fs_status fs_attend_workspace_size(const fs_store* store, int32_t batch, int32_t num_q_tokens,
+                                   int32_t num_q_heads, size_t* bytes) {
+    g_msg[0] = 0;
+    if (!store || !bytes) return fail(FS_E_ARG, "null pointer argument");
+    if (batch < 1 || num_q_tokens < 1 || num_q_heads < 1)
+        return fail(FS_E_RANGE, "batch, num_q_tokens and num_q_heads must be >= 1");
+    *bytes = fsi_attend_workspace_bytes(fsi_attend_splits(store, batch, num_q_tokens), batch,
+                                        num_q_tokens, num_q_heads);
     return FS_OK;
 }
 

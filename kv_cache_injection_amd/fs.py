@@ -42,8 +42,8 @@ FS_KV_DEVICE = 0
 FS_KV_PINNED_HOST = 1
 
 EXPORTS = ("fs_create_store", "fs_destroy_store", "fs_retrieve_topk", "fs_inject",
-           "fs_fetch_async", "fs_attend_prefill", "fs_poll_errors", "fs_strerror",
-           "fs_last_error_message")
+           "fs_fetch_async", "fs_attend_prefill", "fs_attend_workspace_size", "fs_poll_errors",
+           "fs_strerror", "fs_last_error_message")
 
 
 class fs_store_desc(ctypes.Structure):
@@ -86,7 +86,8 @@ def _load() -> ctypes.CDLL:
         "fs_inject": (i32, [P, i32, i32, P, P, i32, P, i32, P, P, P, i32, P]),
         "fs_fetch_async": (i32, [P, i32, P, P, i32, i32, i32, P]),
         "fs_attend_prefill": (i32, [P, i32, i32, i32, P, P, P, i32, P, i32, P, P, ctypes.c_float,
-                                    P, P]),
+                                    P, P, ctypes.c_size_t, P]),
+        "fs_attend_workspace_size": (i32, [P, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]),
         "fs_poll_errors": (i32, [P, P, ctypes.POINTER(ctypes.c_uint32)]),
         "fs_strerror": (ctypes.c_char_p, [i32]),
         "fs_last_error_message": (ctypes.c_char_p, []),
@@ -275,9 +276,12 @@ def fs_fetch_async(store, batch: int, user: torch.Tensor, ids: torch.Tensor, k: 
 def fs_attend_prefill(store, batch: int, q: torch.Tensor, k_cache: torch.Tensor,
                       v_cache: torch.Tensor, block_table: torch.Tensor, max_blocks: int,
                       ctx_begin: torch.Tensor, q_pos: torch.Tensor, scale: float,
-                      out: torch.Tensor, stream=None) -> None:
+                      out: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
     """q: bf16 [batch, Tq, Hq, D] before RoPE; k_cache/v_cache: one layer's
-    bf16 [num_blocks, block_size, Hkv, D]; out: fp32 [batch, Tq, Hq, D]."""
+    bf16 [num_blocks, block_size, Hkv, D]; out: fp32 [batch, Tq, Hq, D];
+    workspace: optional uint8 device tensor (fs_attend_workspace_size bytes
+    for the full context split)."""
     if q.dim() != 4 or q.shape[0] != batch:
         raise ValueError(f"q must be [batch, Tq, Hq, D], got {tuple(q.shape)}")
     _, tq, hq, d = q.shape
@@ -296,8 +300,18 @@ def fs_attend_prefill(store, batch: int, q: torch.Tensor, k_cache: torch.Tensor,
         int(max_blocks),
         _ptr(ctx_begin, torch.int32, shape=(batch,), name="ctx_begin"),
         _ptr(q_pos, torch.int32, shape=(batch,), name="q_pos"), float(scale),
-        _ptr(out, torch.float32, shape=(batch, tq, hq, d), name="out"), _stream(stream))
+        _ptr(out, torch.float32, shape=(batch, tq, hq, d), name="out"),
+        _ptr(workspace, torch.uint8, name="workspace"),
+        ctypes.c_size_t(0 if workspace is None else workspace.numel()), _stream(stream))
     _check(st, "fs_attend_prefill")
+
+
+def fs_attend_workspace_size(store, batch: int, num_q_tokens: int, num_q_heads: int) -> int:
+    n = ctypes.c_size_t(0)
+    st = _lib.fs_attend_workspace_size(_handle(store), int(batch), int(num_q_tokens),
+                                       int(num_q_heads), ctypes.byref(n))
+    _check(st, "fs_attend_workspace_size")
+    return int(n.value)
 
 
 def fs_poll_errors(store, stream=None) -> int:
