@@ -301,6 +301,67 @@ FS_API fs_status fs_attend_workspace_size(const fs_store* store, int32_t batch,
                                           int32_t num_q_tokens, int32_t num_q_heads,
                                           size_t* bytes);
 
+/* ---- approximate retrieval: inverted-file index ------------------------- */
+
+/*
+ * The pages keep a GPU-resident semantic retrieval index beside the KV store
+ * (gist.science summary, "Contributions Clés") and name it without
+ * describing it.  This is an index of its own design for users whose fact
+ * tables are too large for the flat scan of fs_retrieve_topk: the user's
+ * embeddings are clustered (spherical k-means, inner product) into nlist
+ * lists; a probe scores the nlist centroids, scans the nprobe best lists and
+ * returns the top k of their facts.
+ *
+ * What a probe returns, exactly: with the lists ranked by (centroid score
+ * desc, list index asc), the k best facts of the union of the first nprobe
+ * lists by (score desc, fact id asc), scored exactly as fs_retrieve_topk
+ * scores them (same bits).  With nprobe = nlist it equals fs_retrieve_topk.
+ */
+typedef struct fs_ivf fs_ivf;
+
+typedef struct {
+    int32_t user;            /* the indexed user                              */
+    int32_t nlist;           /* lists (= centroids)                           */
+    int32_t num_facts;       /* the user's facts, all in exactly one list     */
+    int32_t max_list;        /* longest list                                  */
+    int32_t max_nprobe;
+    const float* centroids;  /* device fp32 [nlist][embed_dim], unit norm     */
+    const int32_t* list_begin; /* device [nlist + 1]: list c is members[list_begin[c] ..
+                                  list_begin[c+1])                          */
+    const int32_t* members;  /* device [num_facts] global fact ids, ascending within a list */
+} fs_ivf_view;
+
+/*
+ * fs_ivf_build — cluster user `user`'s embeddings into `nlist` lists
+ * (1 .. 4096, at most the user's fact count) with `iters` k-means
+ * iterations (0 .. 100; centroids start at the rows floor(c * N / nlist)),
+ * and allocate probe scratch for up to `max_nprobe` lists and the store's
+ * max_batch requests.  Runs on `stream` and synchronises it; deterministic
+ * for a given store.  The index keeps a copy of the rows in list order (4 *
+ * N * embed_dim bytes) and reads the store's embeddings only while building.
+ * Errors: FS_E_ARG, FS_E_RANGE, FS_E_NOMEM, FS_E_HIP.
+ */
+FS_API fs_status fs_ivf_build(const fs_store* store, int32_t user, int32_t nlist, int32_t iters,
+                              int32_t max_nprobe, void* stream, fs_ivf** out);
+
+/* fs_ivf_destroy — free an index (NULL is a no-op); no call may be in flight. */
+FS_API fs_status fs_ivf_destroy(fs_ivf* ivf);
+
+/* fs_ivf_arrays — sizes and read-only device pointers of a built index. */
+FS_API fs_status fs_ivf_arrays(const fs_ivf* ivf, fs_ivf_view* view);
+
+/*
+ * fs_ivf_retrieve_topk — approximate retrieval for `batch` requests of the
+ * indexed user (query device fp32 [batch][embed_dim], 16-byte aligned),
+ * probing `nprobe` lists (1 .. max_nprobe).  ids / scores / num_tokens as in
+ * fs_retrieve_topk (rank order, -1 / -inf pads when the probed lists hold
+ * fewer than k facts).  Uses the index's probe scratch: calls on one index
+ * must not overlap.  Errors: FS_E_ARG, FS_E_RANGE, FS_E_HIP.
+ */
+FS_API fs_status fs_ivf_retrieve_topk(const fs_store* store, const fs_ivf* ivf, int32_t batch,
+                                      const float* query, int32_t nprobe, int32_t k, int32_t* ids,
+                                      double* scores, int32_t* num_tokens, void* stream);
+
 /*
  * fs_poll_errors — synchronise `stream`, return the device error bits
  * accumulated since the last poll in *flags, and clear them.  Returns

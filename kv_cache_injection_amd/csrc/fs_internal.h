@@ -110,6 +110,40 @@ hipError_t fsi_launch_attend(const AttendLaunch& a);
 int fsi_attend_splits(const fs_store* st, int32_t batch, int32_t num_q_tokens);
 size_t fsi_attend_workspace_bytes(int splits, int32_t batch, int32_t num_q_tokens, int32_t num_q_heads);
 
+// Inverted-file index over one user's facts (approximate retrieval).
+struct fs_ivf {
+    const fs_store* store = nullptr;
+    int32_t user = 0, nlist = 0, num_facts = 0, max_nprobe = 0, max_list = 0, iters = 0;
+    int32_t max_batch = 0;
+    int64_t fact_base = 0;             // global id of the user's first fact
+    float* d_cent = nullptr;           // [nlist][E] unit-norm centroids
+    int32_t* d_list_begin = nullptr;   // [nlist+1] offsets into members
+    int32_t* d_members = nullptr;      // [num_facts] global fact ids, by list, ascending within a list
+    float* d_emb_sorted = nullptr;     // [num_facts][E] the members' embedding rows, same order
+    int64_t* d_cent_range = nullptr;   // {0, nlist}: the centroids as one "user"
+    int32_t* d_zero_users = nullptr;   // [max_batch] zeros
+    double* d_cscores = nullptr;       // [max_batch][nlist] centroid scores
+    int32_t* d_chosen = nullptr;       // [max_batch][max_nprobe] probed lists
+    int32_t cand_stride = 0;           // max_nprobe lists of at most max_list facts
+    double* d_cand_scores = nullptr;   // [max_batch][cand_stride]
+    int32_t* d_cand_ids = nullptr;     // [max_batch][cand_stride]
+    int32_t* d_counts = nullptr;       // [max_batch] candidates per request
+};
+
+struct IvfProbeLaunch {
+    const fs_ivf* ivf;
+    int32_t batch;
+    const float* query;
+    int32_t nprobe, k;
+    int32_t* ids;
+    double* scores;
+    int32_t* num_tokens;
+    hipStream_t stream;
+};
+hipError_t fsi_launch_ivf_probe(const IvfProbeLaunch& a);
+// builds ix's centroids, lists and sorted rows (index arrays already allocated)
+hipError_t fsi_ivf_build(fs_ivf* ix, hipStream_t stream);
+
 struct FetchLaunch {
     const fs_store* st;
     int32_t layer_begin, layer_end;

@@ -6,11 +6,13 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <new>
+#include <vector>
 
 #include "fs_internal.h"
 
@@ -391,6 +393,137 @@ fs_status fs_attend_workspace_size(const fs_store* store, int32_t batch, int32_t
         return fail(FS_E_RANGE, "batch, num_q_tokens and num_q_heads must be >= 1");
     *bytes = fsi_attend_workspace_bytes(fsi_attend_splits(store, batch, num_q_tokens), batch,
                                         num_q_tokens, num_q_heads);
+    return FS_OK;
+}
+
+static void free_ivf(fs_ivf* ix) {
+    if (!ix) return;
+    void* bufs[] = {ix->d_cent, ix->d_list_begin, ix->d_members, ix->d_emb_sorted, ix->d_cent_range,
+                    ix->d_zero_users, ix->d_cscores, ix->d_chosen, ix->d_cand_scores, ix->d_cand_ids,
+                    ix->d_counts};
+    for (void* p : bufs)
+        if (p) (void)hipFree(p);
+    delete ix;
+}
+
+fs_status fs_ivf_build(const fs_store* store, int32_t user, int32_t nlist, int32_t iters,
+                       int32_t max_nprobe, void* stream, fs_ivf** out) {
+    g_msg[0] = 0;
+    if (!store || !out) return fail(FS_E_ARG, "null pointer argument");
+    *out = nullptr;
+    const fs_store_desc& d = store->desc;
+    if (user < 0 || user >= d.num_users) return fail(FS_E_RANGE, "user %d outside [0, %d)", user, d.num_users);
+    if (nlist < 1 || nlist > 4096) return fail(FS_E_RANGE, "nlist %d outside [1, 4096]", nlist);
+    if (iters < 0 || iters > 100) return fail(FS_E_RANGE, "iters %d outside [0, 100]", iters);
+    if (max_nprobe < 1 || max_nprobe > nlist)
+        return fail(FS_E_RANGE, "max_nprobe %d outside [1, nlist]", max_nprobe);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int64_t range[2] = {0, 0};
+    hipError_t e = hipMemcpy(range, store->d_user_begin + user, sizeof(range), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy(user range)");
+    const int64_t n = range[1] - range[0];
+    if (n < nlist) return fail(FS_E_RANGE, "user %d has %lld facts, fewer than nlist %d", user,
+                               static_cast<long long>(n), nlist);
+    if (n > INT32_MAX / 2) return fail(FS_E_RANGE, "user too large for one index");
+    fs_ivf* ix = new (std::nothrow) fs_ivf();
+    if (!ix) return fail(FS_E_NOMEM, "host allocation");
+    ix->store = store;
+    ix->user = user;
+    ix->nlist = nlist;
+    ix->num_facts = static_cast<int32_t>(n);
+    ix->max_nprobe = max_nprobe;
+    ix->iters = iters;
+    ix->max_batch = d.max_batch;
+    ix->fact_base = range[0];
+    const size_t E = d.embed_dim;
+    struct { void** p; size_t bytes; } a1[] = {
+        {(void**)&ix->d_cent, sizeof(float) * nlist * E},
+        {(void**)&ix->d_list_begin, sizeof(int32_t) * (nlist + 1)},
+        {(void**)&ix->d_members, sizeof(int32_t) * size_t(n)},
+        {(void**)&ix->d_emb_sorted, sizeof(float) * size_t(n) * E},
+        {(void**)&ix->d_cent_range, sizeof(int64_t) * 2},
+        {(void**)&ix->d_zero_users, sizeof(int32_t) * size_t(d.max_batch)},
+        {(void**)&ix->d_cscores, sizeof(double) * size_t(d.max_batch) * nlist},
+        {(void**)&ix->d_chosen, sizeof(int32_t) * size_t(d.max_batch) * max_nprobe},
+        {(void**)&ix->d_counts, sizeof(int32_t) * size_t(d.max_batch)},
+    };
+    for (auto& a : a1) {
+        e = hipMalloc(a.p, a.bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            free_ivf(ix);
+            return fail(FS_E_NOMEM, "hipMalloc(index, %zu bytes): %s", a.bytes, hipGetErrorString(e));
+        }
+    }
+    const int64_t cr[2] = {0, nlist};
+    std::vector<int32_t> zeros(size_t(d.max_batch), 0);
+    e = hipMemcpyAsync(ix->d_cent_range, cr, sizeof(cr), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(ix->d_zero_users, zeros.data(), sizeof(int32_t) * zeros.size(), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = fsi_ivf_build(ix, s);       // synchronises s
+    if (e != hipSuccess) {
+        free_ivf(ix);
+        return hip_fail(e, "index build");
+    }
+    const int64_t stride = int64_t(max_nprobe) * ix->max_list;
+    ix->cand_stride = static_cast<int32_t>(std::min<int64_t>(stride, n));
+    struct { void** p; size_t bytes; } a2[] = {
+        {(void**)&ix->d_cand_scores, sizeof(double) * size_t(d.max_batch) * ix->cand_stride},
+        {(void**)&ix->d_cand_ids, sizeof(int32_t) * size_t(d.max_batch) * ix->cand_stride},
+    };
+    for (auto& a : a2) {
+        e = hipMalloc(a.p, a.bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            free_ivf(ix);
+            return fail(FS_E_NOMEM, "hipMalloc(probe scratch, %zu bytes): %s", a.bytes, hipGetErrorString(e));
+        }
+    }
+    *out = ix;
+    return FS_OK;
+}
+
+fs_status fs_ivf_destroy(fs_ivf* ix) {
+    g_msg[0] = 0;
+    if (!ix) return FS_OK;
+    free_ivf(ix);
+    return FS_OK;
+}
+
+fs_status fs_ivf_arrays(const fs_ivf* ix, fs_ivf_view* view) {
+    g_msg[0] = 0;
+    if (!ix || !view) return fail(FS_E_ARG, "null pointer argument");
+    view->user = ix->user;
+    view->nlist = ix->nlist;
+    view->num_facts = ix->num_facts;
+    view->max_list = ix->max_list;
+    view->max_nprobe = ix->max_nprobe;
+    view->centroids = ix->d_cent;
+    view->list_begin = ix->d_list_begin;
+    view->members = ix->d_members;
+    return FS_OK;
+}
+
+fs_status fs_ivf_retrieve_topk(const fs_store* store, const fs_ivf* ix, int32_t batch, const float* query,
+                               int32_t nprobe, int32_t k, int32_t* ids, double* scores,
+                               int32_t* num_tokens, void* stream) {
+    g_msg[0] = 0;
+    if (!store || !ix) return fail(FS_E_ARG, "null store or index");
+    if (ix->store != store) return fail(FS_E_ARG, "index was built on another store");
+    const fs_store_desc& d = store->desc;
+    if (batch < 1 || batch > d.max_batch) return fail(FS_E_RANGE, "batch %d outside [1, %d]", batch, d.max_batch);
+    if (nprobe < 1 || nprobe > ix->max_nprobe)
+        return fail(FS_E_RANGE, "nprobe %d outside [1, %d]", nprobe, ix->max_nprobe);
+    if (k < 0 || k > d.max_k) return fail(FS_E_RANGE, "k %d outside [0, %d]", k, d.max_k);
+    if (!query) return fail(FS_E_ARG, "null query");
+    if (!aligned(query, 16)) return fail(FS_E_ARG, "query not 16-byte aligned");
+    if (k > 0 && !ids) return fail(FS_E_ARG, "null ids");
+    if ((ids && !aligned(ids, 4)) || (scores && !aligned(scores, 8)) || (num_tokens && !aligned(num_tokens, 4)))
+        return fail(FS_E_ARG, "output not aligned");
+    if (k == 0 && !num_tokens) return FS_OK;
+    IvfProbeLaunch a{ix, batch, query, nprobe, k, ids, scores, num_tokens, reinterpret_cast<hipStream_t>(stream)};
+    hipError_t e = fsi_launch_ivf_probe(a);
+    if (e != hipSuccess) return hip_fail(e, "index probe launch");
     return FS_OK;
 }
 

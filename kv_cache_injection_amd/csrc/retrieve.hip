@@ -151,6 +151,75 @@ __global__ __launch_bounds__(256) void fs_score_kernel(ScoreArgs a) {
     }
 }
 
+// ---- approximate retrieval: scan of the probed inverted lists -------------
+
+struct ListArgs {
+    const float4* emb_sorted;  // [N_u][E/4] rows in list order
+    int32_t e4;
+    const int32_t* list_begin; // [nlist+1]
+    const int32_t* members;    // [N_u] global fact ids
+    const int32_t* chosen;     // [B][np_stride] probed lists, best first
+    int32_t np_stride, nprobe;
+    const float4* query;       // [B][E/4]
+    double* cand_scores;       // [B][stride]
+    int32_t* cand_ids;         // [B][stride]
+    int32_t* counts;           // [B]
+    int32_t stride;
+};
+
+// Block (row tile, probed list pi, request b): scores 8 rows of list
+// chosen[b][pi] with the arithmetic of fs_score_kernel (same column
+// ownership, fma order and butterfly), so a fact scores the same bits here as
+// in the flat scan.  Candidates of request b are the probed lists in probe
+// order; the block of (0, 0) records their count.
+__global__ __launch_bounds__(256) void fs_list_score_kernel(ListArgs a) {
+    const int b = blockIdx.z;
+    const int pi = blockIdx.y;
+    const int32_t* ch = a.chosen + int64_t(b) * a.np_stride;
+    const int c = ch[pi];
+    int32_t off = 0, total = 0;
+    for (int j = 0; j < a.nprobe; ++j) {
+        const int cj = ch[j];
+        const int32_t len = a.list_begin[cj + 1] - a.list_begin[cj];
+        if (j < pi) off += len;
+        total += len;
+    }
+    if (blockIdx.x == 0 && pi == 0 && threadIdx.x == 0) a.counts[b] = total;
+    const int32_t beg = a.list_begin[c];
+    const int32_t n = a.list_begin[c + 1] - beg;
+    const int32_t row0 = blockIdx.x * kScoreRowsPerBlock;
+    if (row0 >= n) return;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int32_t r0 = row0 + wave * kScoreRowsPerWave;
+    const bool v0 = r0 < n, v1 = r0 + 1 < n;
+    const float4* e0 = a.emb_sorted + int64_t(beg + (v0 ? r0 : 0)) * a.e4;
+    const float4* e1 = a.emb_sorted + int64_t(beg + (v1 ? r0 + 1 : 0)) * a.e4;
+    const float4* qv = a.query + int64_t(b) * a.e4;
+    double acc0 = 0.0, acc1 = 0.0;
+#pragma unroll 2
+    for (int cc = lane; cc < a.e4; cc += 64) {
+        const float4 ea = e0[cc];
+        const float4 eb = e1[cc];
+        const float4 qq = qv[cc];
+        fma4(acc0, ea, qq);
+        fma4(acc1, eb, qq);
+    }
+    const double s0 = wave_sum(acc0);
+    const double s1 = wave_sum(acc1);
+    if (lane == 0) {
+        const int64_t o = int64_t(b) * a.stride + off + r0;
+        if (v0) {
+            a.cand_scores[o] = s0;
+            a.cand_ids[o] = a.members[beg + r0];
+        }
+        if (v1) {
+            a.cand_scores[o + 1] = s1;
+            a.cand_ids[o + 1] = a.members[beg + r0 + 1];
+        }
+    }
+}
+
 struct TopkArgs {
     const double* scores;     // [B][stride]
     int32_t stride;
@@ -163,6 +232,11 @@ struct TopkArgs {
     double* out_scores;       // [B][k] or null
     int32_t* num_tokens;      // [B] or null
     uint32_t* err;
+    // candidate mode (approximate retrieval): request b has counts[b]
+    // candidates, candidate i is fact idmap[b * stride + i]; ties go to the
+    // lower fact id
+    const int32_t* counts;
+    const int32_t* idmap;
 };
 
 __global__ __launch_bounds__(kTopkThreads) void fs_topk_kernel(TopkArgs a) {
@@ -179,11 +253,16 @@ __global__ __launch_bounds__(kTopkThreads) void fs_topk_kernel(TopkArgs a) {
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int k = a.k;
-    const int u = a.user[b];
-    const bool bad_user = (u < 0 || u >= a.num_users);
-    const int64_t base = bad_user ? 0 : a.user_begin[u];
-    const int32_t n = bad_user ? 0 : static_cast<int32_t>(a.user_begin[u + 1] - base);
+    const bool mapped = a.counts != nullptr;
+    const int u = mapped ? 0 : a.user[b];
+    const bool bad_user = !mapped && (u < 0 || u >= a.num_users);
+    const int64_t base = (mapped || bad_user) ? 0 : a.user_begin[u];
+    const int32_t n = mapped ? a.counts[b]
+                             : (bad_user ? 0 : static_cast<int32_t>(a.user_begin[u + 1] - base));
     const int kk = n < k ? n : k;
+    const int32_t* imap = mapped ? a.idmap + int64_t(b) * a.stride : nullptr;
+    // the id a candidate is ranked and reported by
+    auto cand_id = [&](int i) -> int32_t { return mapped ? imap[i] : i; };
 
     if (bad_user && tid == 0) atomicOr(a.err, FS_ERR_USER);
     if (kk == 0) {
@@ -252,7 +331,7 @@ __global__ __launch_bounds__(kTopkThreads) void fs_topk_kernel(TopkArgs a) {
         }
         const double range = hi - lo;
         const double scale = (kBins - 0.5) / range;
-        if (!bad && range == 0.0) {
+        if (!bad && range == 0.0 && !mapped) {
             // every score is equal: the lowest kk indices win, in order
             for (int j = tid; j < kk; j += blockDim.x) {
                 cand_key[j] = order_key(lo);
@@ -297,9 +376,10 @@ __global__ __launch_bounds__(kTopkThreads) void fs_topk_kernel(TopkArgs a) {
                 auto gather = [&](double x, int i) {
                     if (value_bin(x, lo, scale) >= t) {
                         const int slot = atomicAdd(&s_nc, 1);
+                        const int32_t id = cand_id(i);
                         s_ck[slot] = order_key(x);
-                        s_ci[slot] = i;
-                        s_cl[slot] = a.fact_len[base + i];
+                        s_ci[slot] = id;
+                        s_cl[slot] = a.fact_len ? a.fact_len[base + id] : 0;
                     }
                 };
 #pragma unroll
@@ -326,6 +406,54 @@ __global__ __launch_bounds__(kTopkThreads) void fs_topk_kernel(TopkArgs a) {
                 goto outputs;
             }
         }
+    }
+
+    if (mapped) {
+        // exact fallback for candidate mode: the r-th winner is the best
+        // candidate worse than the (r-1)-th on (score desc, fact id asc)
+        __shared__ uint64_t s_rk[kTopkWaves];
+        __shared__ int32_t s_ri[kTopkWaves];
+        uint64_t pk = 0;
+        int32_t pi = 0;
+        for (int r = 0; r < kk; ++r) {
+            uint64_t bk = 0;
+            int32_t bi = INT32_MAX;
+            for (int i = tid; i < n; i += kTopkThreads) {
+                const uint64_t key = order_key(sc[i]);
+                const int32_t id = imap[i];
+                if ((r == 0 || better(pk, pi, key, id)) && better(key, id, bk, bi)) {
+                    bk = key;
+                    bi = id;
+                }
+            }
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) {
+                const uint64_t ok = __shfl_xor(bk, m, 64);
+                const int32_t oi = __shfl_xor(bi, m, 64);
+                if (better(ok, oi, bk, bi)) {
+                    bk = ok;
+                    bi = oi;
+                }
+            }
+            if (lane == 0) {
+                s_rk[wave] = bk;
+                s_ri[wave] = bi;
+            }
+            __syncthreads();
+            for (int w = 0; w < kTopkWaves; ++w)
+                if (better(s_rk[w], s_ri[w], bk, bi)) {
+                    bk = s_rk[w];
+                    bi = s_ri[w];
+                }
+            if (tid == 0) {
+                cand_key[r] = bk;
+                cand_idx[r] = bi;
+            }
+            pk = bk;
+            pi = bi;
+            __syncthreads();
+        }
+        goto outputs;
     }
 
     {
@@ -472,7 +600,7 @@ outputs:
         if (j < kk) {
             id = static_cast<int32_t>(base + cand_idx[j]);
             s = key_value(cand_key[j]);
-            if (!tokens_known) my_tokens += a.fact_len[id];
+            if (!tokens_known && a.fact_len) my_tokens += a.fact_len[id];
         }
         a.ids[int64_t(b) * k + j] = id;
         if (a.out_scores) a.out_scores[int64_t(b) * k + j] = s;
@@ -507,7 +635,7 @@ hipError_t fsi_launch_retrieve(const RetrieveLaunch& r) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    TopkArgs ta;
+    TopkArgs ta{};
     ta.scores = st->d_scores;
     ta.stride = st->max_user_facts;
     ta.user_begin = st->d_user_begin;
@@ -522,5 +650,75 @@ hipError_t fsi_launch_retrieve(const RetrieveLaunch& r) {
     const int lds_keys = st->max_user_facts < fsi::kTopkLdsKeys ? st->max_user_facts : fsi::kTopkLdsKeys;
     size_t lds = sizeof(uint64_t) * size_t(lds_keys);
     fs_topk_kernel<<<dim3(r.batch), kTopkThreads, lds, r.stream>>>(ta);
+    return hipGetLastError();
+}
+
+// Approximate retrieval through an inverted-file index: centroid scores,
+// top-nprobe lists, scan of those lists, top-k of the candidates by
+// (score desc, fact id asc).
+hipError_t fsi_launch_ivf_probe(const IvfProbeLaunch& r) {
+    const fs_ivf* ix = r.ivf;
+    const fs_store* st = ix->store;
+    const fs_store_desc& d = st->desc;
+    const int e4 = d.embed_dim / 4;
+    ScoreArgs sa{};
+    sa.emb = reinterpret_cast<const float4*>(ix->d_cent);
+    sa.e4 = e4;
+    sa.user_begin = ix->d_cent_range;
+    sa.num_users = 1;
+    sa.user = ix->d_zero_users;
+    sa.query = reinterpret_cast<const float4*>(r.query);
+    sa.batch = r.batch;
+    sa.scores = ix->d_cscores;
+    sa.stride = ix->nlist;
+    dim3 g1((ix->nlist + kScoreRowsPerBlock - 1) / kScoreRowsPerBlock, r.batch);
+    fs_score_kernel<<<g1, 256, 0, r.stream>>>(sa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    TopkArgs t1{};
+    t1.scores = ix->d_cscores;
+    t1.stride = ix->nlist;
+    t1.user_begin = ix->d_cent_range;
+    t1.num_users = 1;
+    t1.user = ix->d_zero_users;
+    t1.k = r.nprobe;
+    t1.ids = ix->d_chosen;          // row stride nprobe: written as [B][nprobe]
+    t1.err = st->d_err;
+    const int lds1 = ix->nlist < fsi::kTopkLdsKeys ? ix->nlist : fsi::kTopkLdsKeys;
+    fs_topk_kernel<<<dim3(r.batch), kTopkThreads, sizeof(uint64_t) * size_t(lds1), r.stream>>>(t1);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    ListArgs la{};
+    la.emb_sorted = reinterpret_cast<const float4*>(ix->d_emb_sorted);
+    la.e4 = e4;
+    la.list_begin = ix->d_list_begin;
+    la.members = ix->d_members;
+    la.chosen = ix->d_chosen;
+    la.np_stride = r.nprobe;
+    la.nprobe = r.nprobe;
+    la.query = reinterpret_cast<const float4*>(r.query);
+    la.cand_scores = ix->d_cand_scores;
+    la.cand_ids = ix->d_cand_ids;
+    la.counts = ix->d_counts;
+    la.stride = ix->cand_stride;
+    dim3 g3((ix->max_list + kScoreRowsPerBlock - 1) / kScoreRowsPerBlock, r.nprobe, r.batch);
+    fs_list_score_kernel<<<g3, 256, 0, r.stream>>>(la);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    TopkArgs t2{};
+    t2.scores = ix->d_cand_scores;
+    t2.stride = ix->cand_stride;
+    t2.fact_len = st->d_fact_len;
+    t2.k = r.k;
+    t2.ids = r.ids;
+    t2.out_scores = r.scores;
+    t2.num_tokens = r.num_tokens;
+    t2.err = st->d_err;
+    t2.counts = ix->d_counts;
+    t2.idmap = ix->d_cand_ids;
+    fs_topk_kernel<<<dim3(r.batch), kTopkThreads, 0, r.stream>>>(t2);
     return hipGetLastError();
 }

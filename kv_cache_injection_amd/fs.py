@@ -42,7 +42,8 @@ FS_KV_DEVICE = 0
 FS_KV_PINNED_HOST = 1
 
 EXPORTS = ("fs_create_store", "fs_destroy_store", "fs_retrieve_topk", "fs_inject",
-           "fs_fetch_async", "fs_attend_prefill", "fs_attend_workspace_size", "fs_poll_errors",
+           "fs_fetch_async", "fs_attend_prefill", "fs_attend_workspace_size", "fs_ivf_build",
+           "fs_ivf_destroy", "fs_ivf_arrays", "fs_ivf_retrieve_topk", "fs_poll_errors",
            "fs_strerror", "fs_last_error_message")
 
 
@@ -61,6 +62,19 @@ class fs_store_desc(ctypes.Structure):
         ("staging_layers", ctypes.c_int32),
         ("num_facts", ctypes.c_int64),
         ("num_tokens", ctypes.c_int64),
+    ]
+
+
+class fs_ivf_view(ctypes.Structure):
+    _fields_ = [
+        ("user", ctypes.c_int32),
+        ("nlist", ctypes.c_int32),
+        ("num_facts", ctypes.c_int32),
+        ("max_list", ctypes.c_int32),
+        ("max_nprobe", ctypes.c_int32),
+        ("centroids", ctypes.c_void_p),
+        ("list_begin", ctypes.c_void_p),
+        ("members", ctypes.c_void_p),
     ]
 
 
@@ -88,6 +102,10 @@ def _load() -> ctypes.CDLL:
         "fs_attend_prefill": (i32, [P, i32, i32, i32, P, P, P, i32, P, i32, P, P, ctypes.c_float,
                                     P, P, ctypes.c_size_t, P]),
         "fs_attend_workspace_size": (i32, [P, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]),
+        "fs_ivf_build": (i32, [P, i32, i32, i32, i32, P, ctypes.POINTER(P)]),
+        "fs_ivf_destroy": (i32, [P]),
+        "fs_ivf_arrays": (i32, [P, ctypes.POINTER(fs_ivf_view)]),
+        "fs_ivf_retrieve_topk": (i32, [P, P, i32, P, i32, i32, P, P, P, P]),
         "fs_poll_errors": (i32, [P, P, ctypes.POINTER(ctypes.c_uint32)]),
         "fs_strerror": (ctypes.c_char_p, [i32]),
         "fs_last_error_message": (ctypes.c_char_p, []),
@@ -312,6 +330,70 @@ def fs_attend_workspace_size(store, batch: int, num_q_tokens: int, num_q_heads: 
                                        int(num_q_heads), ctypes.byref(n))
     _check(st, "fs_attend_workspace_size")
     return int(n.value)
+
+
+class Ivf:
+    """Handle returned by fs_ivf_build; keeps its store alive."""
+
+    def __init__(self, handle: ctypes.c_void_p, store):
+        self.handle = handle
+        self.store = store
+
+    def close(self) -> None:
+        if self.handle:
+            _check(_lib.fs_ivf_destroy(self.handle), "fs_ivf_destroy")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class _DeviceArray:
+    """A read-only device array of the library seen through the CUDA array
+    interface, so torch can view it without a copy."""
+
+    def __init__(self, ptr: int, shape, typestr: str):
+        self.__cuda_array_interface__ = {"shape": tuple(shape), "typestr": typestr,
+                                         "data": (int(ptr), False), "version": 2, "strides": None}
+
+
+def fs_ivf_build(store, user: int, nlist: int, iters: int, max_nprobe: int, stream=None) -> Ivf:
+    out = ctypes.c_void_p()
+    st = _lib.fs_ivf_build(_handle(store), int(user), int(nlist), int(iters), int(max_nprobe),
+                           _stream(stream), ctypes.byref(out))
+    _check(st, "fs_ivf_build")
+    return Ivf(out, store)
+
+
+def fs_ivf_arrays(ivf: Ivf) -> dict:
+    """Sizes and torch views (device, read-only by contract) of the index."""
+    v = fs_ivf_view()
+    _check(_lib.fs_ivf_arrays(ivf.handle, ctypes.byref(v)), "fs_ivf_arrays")
+    E = ivf.store.desc.embed_dim
+    dev = torch.device("cuda", torch.cuda.current_device())
+    return {
+        "user": v.user, "nlist": v.nlist, "num_facts": v.num_facts, "max_list": v.max_list,
+        "max_nprobe": v.max_nprobe,
+        "centroids": torch.as_tensor(_DeviceArray(v.centroids, (v.nlist, E), "<f4"), device=dev),
+        "list_begin": torch.as_tensor(_DeviceArray(v.list_begin, (v.nlist + 1,), "<i4"), device=dev),
+        "members": torch.as_tensor(_DeviceArray(v.members, (v.num_facts,), "<i4"), device=dev),
+    }
+
+
+def fs_ivf_retrieve_topk(store, ivf: Ivf, batch: int, query: torch.Tensor, nprobe: int, k: int,
+                         ids: torch.Tensor, scores: Optional[torch.Tensor] = None,
+                         num_tokens: Optional[torch.Tensor] = None, stream=None) -> None:
+    E = store.desc.embed_dim
+    st = _lib.fs_ivf_retrieve_topk(
+        _handle(store), ivf.handle, int(batch),
+        _ptr(query, torch.float32, shape=(batch, E), name="query"), int(nprobe), int(k),
+        _ptr(ids, torch.int32, shape=(batch, k), name="ids"),
+        _ptr(scores, torch.float64, shape=(batch, k), name="scores"),
+        _ptr(num_tokens, torch.int32, shape=(batch,), name="num_tokens"), _stream(stream))
+    _check(st, "fs_ivf_retrieve_topk")
 
 
 def fs_poll_errors(store, stream=None) -> int:

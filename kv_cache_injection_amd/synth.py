@@ -267,3 +267,22 @@ def bf16_bits(t) -> np.ndarray:
     """Host uint16 copy of a bf16 tensor's bit patterns."""
     import torch
     return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def clustered_embeddings(n: int, dim: int, topics: int, spread: float, seed: int):
+    """Unit rows drawn around ``topics`` random unit centres (centre +
+    spread * N(0, I/dim), normalised in fp64, rounded to fp32), and each row's
+    topic.  Stands in for the topical structure of a user's memory, which an
+    approximate index relies on; no real text is involved."""
+    ss = np.random.SeedSequence(seed)
+    g_c, g_t, g_n = [np.random.default_rng(x) for x in ss.spawn(3)]
+    centres = g_c.standard_normal((topics, dim))
+    centres /= np.linalg.norm(centres, axis=1, keepdims=True)
+    topic = g_t.integers(0, topics, n)
+    out = np.empty((n, dim), np.float32)
+    step = 65536
+    for a in range(0, n, step):
+        b = min(n, a + step)
+        x = centres[topic[a:b]] + spread * g_n.standard_normal((b - a, dim)) / np.sqrt(dim)
+        out[a:b] = (x / np.linalg.norm(x, axis=1, keepdims=True)).astype(np.float32)
+    return out, topic

@@ -51,7 +51,7 @@ __all__ = [
     "bf16_to_f64", "f64_to_bf16", "score", "select_topk", "decisive_gap",
     "retrieve", "compose", "segment_rows", "placement", "request_problem",
     "rope_inv_freq", "rope_rotate", "inject_request", "expected_rows",
-    "gather_rows", "causal_attention", "attend_prefill",
+    "gather_rows", "causal_attention", "attend_prefill", "ivf_probe",
 ]
 
 
@@ -332,3 +332,29 @@ def attend_prefill(q_pre: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         g = h // group
         out[:, h] = causal_attention(qr[:, h], kr[:, g], vr[:, g], qpos, kpos, scale)
     return out
+
+
+# --------------------------------------------------------------------------
+# Approximate retrieval through an inverted-file index
+# --------------------------------------------------------------------------
+
+def ivf_probe(emb: np.ndarray, centroids: np.ndarray, list_begin: np.ndarray,
+              members: np.ndarray, query: np.ndarray, nprobe: int, k: int):
+    """What an inverted-file probe returns (the pages keep a GPU-resident
+    retrieval index [contrib] and do not describe it; this is the index's own
+    definition): lists ranked by (centroid score desc, list index asc); the
+    candidates are the facts of the first ``nprobe`` lists; the result is their
+    k best by (score desc, fact id asc), scores exact as in ``score``.
+    ``members`` holds global fact ids (rows of ``emb``).  Returns (ids padded
+    with -1, scores padded with -inf)."""
+    cs = score(centroids, query)
+    lists = select_topk(cs, nprobe)
+    cand = np.concatenate([np.asarray(members[list_begin[c]:list_begin[c + 1]], np.int64)
+                           for c in lists]) if len(lists) else np.zeros(0, np.int64)
+    s = score(emb[cand], query) if cand.size else np.zeros(0)
+    order = np.lexsort((cand, -s))[:k]
+    ids = np.full(k, -1, np.int64)
+    sc = np.full(k, -np.inf)
+    ids[: order.size] = cand[order]
+    sc[: order.size] = s[order]
+    return ids, sc

@@ -1,0 +1,155 @@
+"""GPU checks of the inverted-file index: the build's invariants, probe parity
+with the oracle's exact definition (ids exact when the deciding score gaps are
+certified), equality with the flat scan when every list is probed, exact ties
+and the candidate-mode fallback."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _parity import CERT_GAP, SCORE_ABS_TOL, say
+from kv_cache_injection_amd import fs, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _store(emb: np.ndarray, fact_len: np.ndarray, max_batch=4, max_k=256):
+    F, E = emb.shape
+    T = int(fact_len.sum())
+    k_pre = [torch.zeros((T, 2, 128), dtype=torch.bfloat16, device="cuda")]
+    v = [torch.zeros((T, 2, 128), dtype=torch.bfloat16, device="cuda")]
+    desc = fs.make_desc(num_layers=1, num_kv_heads=2, head_dim=128, embed_dim=E, rope_theta=1e6,
+                        block_size=16, num_users=1, max_batch=max_batch, max_k=max_k,
+                        num_facts=F, num_tokens=T)
+    e = torch.from_numpy(emb).cuda()
+    st = fs.fs_create_store(desc, np.array([0, F], np.int64), fact_len, e, k_pre, v)
+    return st, e
+
+
+def _host_index(ix):
+    a = fs.fs_ivf_arrays(ix)
+    return (a["centroids"].cpu().numpy().copy(), a["list_begin"].cpu().numpy().astype(np.int64),
+            a["members"].cpu().numpy().astype(np.int64), a)
+
+
+def _gap(s, k):
+    """Smallest score difference that decides a (score desc, index asc)
+    top-k of s (inf when none does)."""
+    return oracle.decisive_gap(s, k)
+
+
+@pytest.fixture(scope="module")
+def clustered():
+    n, dim = 6000, 128
+    emb, _ = synth.clustered_embeddings(n, dim, topics=40, spread=0.6, seed=77)
+    rng = np.random.default_rng(78)
+    fact_len = rng.integers(1, 9, n).astype(np.int32)
+    st, e = _store(emb, fact_len)
+    say("ivf: building 48 lists, 5 iterations")
+    ix = fs.fs_ivf_build(st, 0, 48, 5, 48)
+    q, _ = synth.clustered_embeddings(4, dim, topics=40, spread=0.6, seed=79)
+    yield emb, fact_len, st, ix, q
+    ix.close()
+    st.close()
+
+
+def test_build_invariants(clustered):
+    emb, _, st, ix, _ = clustered
+    cent, lb, mem, a = _host_index(ix)
+    n = emb.shape[0]
+    assert a["nlist"] == 48 and a["num_facts"] == n
+    assert lb[0] == 0 and lb[-1] == n and np.all(np.diff(lb) >= 0)
+    assert a["max_list"] == int(np.diff(lb).max())
+    assert np.array_equal(np.sort(mem), np.arange(n)), "lists are not a partition"
+    for c in range(48):
+        seg = mem[lb[c]:lb[c + 1]]
+        assert np.all(np.diff(seg) > 0), "list not ascending"
+    assert np.allclose(np.linalg.norm(cent.astype(np.float64), axis=1), 1.0, atol=1e-5)
+    # every fact sits in the list of its best centroid (fp32 assignment:
+    # within 1e-5 of the best fp64 score)
+    s = emb.astype(np.float64) @ cent.astype(np.float64).T
+    lst = np.empty(n, np.int64)
+    for c in range(48):
+        lst[mem[lb[c]:lb[c + 1]]] = c
+    assert np.all(s[np.arange(n), lst] >= s.max(axis=1) - 1e-5)
+
+
+@pytest.mark.parametrize("nprobe", [1, 6, 48])
+@pytest.mark.parametrize("k", [1, 50, 256])
+def test_probe_matches_oracle(clustered, nprobe, k):
+    emb, fact_len, st, ix, q = clustered
+    cent, lb, mem, _ = _host_index(ix)
+    B = q.shape[0]
+    ids = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((B, k), dtype=torch.float64, device="cuda")
+    nt = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    fs.fs_ivf_retrieve_topk(st, ix, B, torch.from_numpy(q).cuda(), nprobe, k, ids, sc, nt)
+    assert fs.fs_poll_errors(st) == 0
+    g, gs, gn = ids.cpu().numpy(), sc.cpu().numpy(), nt.cpu().numpy()
+    checked = 0
+    for b in range(B):
+        cs = oracle.score(cent, q[b])
+        if nprobe < 48 and _gap(cs, nprobe) <= CERT_GAP:
+            say(f"request {b}: list choice not certified, skipped")
+            continue
+        o_ids, o_sc = oracle.ivf_probe(emb, cent, lb, mem, q[b], nprobe, k)
+        lists = oracle.select_topk(cs, nprobe)
+        cand = np.concatenate([mem[lb[c]:lb[c + 1]] for c in lists])
+        kk = min(k, cand.size)
+        s_c = oracle.score(emb[np.sort(cand)], q[b])
+        if _gap(s_c, k) > CERT_GAP:
+            assert np.array_equal(g[b].astype(np.int64), o_ids), f"request {b}: ids differ"
+        else:
+            assert set(g[b][:kk]) <= set(cand.tolist())
+            say(f"request {b}: near-tie, validity checked")
+        assert np.all(np.abs(gs[b][:kk] - o_sc[:kk]) <= SCORE_ABS_TOL)
+        assert np.all(g[b][kk:] == -1) and np.all(np.isneginf(gs[b][kk:]))
+        assert gn[b] == int(fact_len[o_ids[o_ids >= 0]].sum())
+        checked += 1
+    assert checked >= 2
+
+
+def test_all_lists_equals_flat_scan_bitwise(clustered):
+    emb, _, st, ix, q = clustered
+    B, k = q.shape[0], 100
+    qt = torch.from_numpy(q).cuda()
+    ids_a = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    sc_a = torch.empty((B, k), dtype=torch.float64, device="cuda")
+    fs.fs_ivf_retrieve_topk(st, ix, B, qt, 48, k, ids_a, sc_a)
+    ids_b = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    sc_b = torch.empty((B, k), dtype=torch.float64, device="cuda")
+    fs.fs_retrieve_topk(st, B, torch.zeros(B, dtype=torch.int32, device="cuda"), qt, k, ids_b, sc_b, None)
+    assert fs.fs_poll_errors(st) == 0
+    assert torch.equal(ids_a, ids_b)
+    assert torch.equal(sc_a.view(torch.int64), sc_b.view(torch.int64))
+
+
+def test_exact_ties_and_candidate_fallback():
+    # score = first coordinate for the query e_1; it takes 3 exact values, so
+    # thousands of candidates tie and the exact fallback must order them by id
+    rng = np.random.default_rng(5)
+    n, dim = 3000, 64
+    emb = rng.standard_normal((n, dim)).astype(np.float32)
+    emb[:, 0] = rng.choice(np.array([0.25, 0.5, 0.75], np.float32), n)
+    fact_len = np.ones(n, np.int32)
+    st, _ = _store(emb, fact_len, max_batch=2, max_k=64)
+    ix = fs.fs_ivf_build(st, 0, 16, 3, 16)
+    cent, lb, mem, _ = _host_index(ix)
+    q = np.zeros((2, dim), np.float32)
+    q[0, 0] = 1.0                                          # ties within each value
+    for nprobe in (3, 16):
+        ids = torch.empty((2, 50), dtype=torch.int32, device="cuda")
+        fs.fs_ivf_retrieve_topk(st, ix, 2, torch.from_numpy(q).cuda(), nprobe, 50, ids)
+        assert fs.fs_poll_errors(st) == 0
+        g = ids.cpu().numpy().astype(np.int64)
+        for b in range(2):                                 # request 1: all scores 0
+            o_ids, _ = oracle.ivf_probe(emb, cent, lb, mem, q[b], nprobe, 50)
+            cs = oracle.score(cent, q[b])
+            if nprobe < 16 and _gap(cs, nprobe) <= CERT_GAP:
+                continue
+            assert np.array_equal(g[b], o_ids), f"nprobe {nprobe} request {b}"
+    ix.close()
+    st.close()
