@@ -128,6 +128,7 @@ struct fs_ivf {
     double* d_cand_scores = nullptr;   // [max_batch][cand_stride]
     int32_t* d_cand_ids = nullptr;     // [max_batch][cand_stride]
     int32_t* d_counts = nullptr;       // [max_batch] candidates per request
+    int32_t* d_offs = nullptr;         // [max_batch][max_nprobe + 1] list starts in the candidates
 };
 
 struct IvfProbeLaunch {

@@ -400,7 +400,7 @@ static void free_ivf(fs_ivf* ix) {
     if (!ix) return;
     void* bufs[] = {ix->d_cent, ix->d_list_begin, ix->d_members, ix->d_emb_sorted, ix->d_cent_range,
                     ix->d_zero_users, ix->d_cscores, ix->d_chosen, ix->d_cand_scores, ix->d_cand_ids,
-                    ix->d_counts};
+                    ix->d_counts, ix->d_offs};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
     delete ix;
@@ -446,6 +446,7 @@ fs_status fs_ivf_build(const fs_store* store, int32_t user, int32_t nlist, int32
         {(void**)&ix->d_cscores, sizeof(double) * size_t(d.max_batch) * nlist},
         {(void**)&ix->d_chosen, sizeof(int32_t) * size_t(d.max_batch) * max_nprobe},
         {(void**)&ix->d_counts, sizeof(int32_t) * size_t(d.max_batch)},
+        {(void**)&ix->d_offs, sizeof(int32_t) * size_t(d.max_batch) * (max_nprobe + 1)},
     };
     for (auto& a : a1) {
         e = hipMalloc(a.p, a.bytes);

@@ -160,6 +160,7 @@ struct ListArgs {
     const int32_t* members;    // [N_u] global fact ids
     const int32_t* chosen;     // [B][np_stride] probed lists, best first
     int32_t np_stride, nprobe;
+    int32_t* offs;             // [B][np_stride + 1] first candidate of each probed list
     const float4* query;       // [B][E/4]
     double* cand_scores;       // [B][stride]
     int32_t* cand_ids;         // [B][stride]
@@ -167,24 +168,46 @@ struct ListArgs {
     int32_t stride;
 };
 
+// One wave per request: where each probed list's candidates start (probe
+// order), and how many candidates there are.
+__global__ __launch_bounds__(64) void fs_list_offsets_kernel(ListArgs a) {
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int32_t* ch = a.chosen + int64_t(b) * a.np_stride;
+    int32_t* off = a.offs + int64_t(b) * (a.np_stride + 1);
+    int32_t carry = 0;
+    for (int j0 = 0; j0 < a.nprobe; j0 += 64) {
+        const int j = j0 + lane;
+        int32_t len = 0;
+        if (j < a.nprobe) {
+            const int c = ch[j];
+            len = a.list_begin[c + 1] - a.list_begin[c];
+        }
+        int32_t incl = len;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        if (j < a.nprobe) off[j] = carry + incl - len;
+        carry += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) {
+        off[a.nprobe] = carry;
+        a.counts[b] = carry;
+    }
+}
+
 // Block (row tile, probed list pi, request b): scores 8 rows of list
 // chosen[b][pi] with the arithmetic of fs_score_kernel (same column
 // ownership, fma order and butterfly), so a fact scores the same bits here as
 // in the flat scan.  Candidates of request b are the probed lists in probe
-// order; the block of (0, 0) records their count.
+// order.
 __global__ __launch_bounds__(256) void fs_list_score_kernel(ListArgs a) {
     const int b = blockIdx.z;
     const int pi = blockIdx.y;
-    const int32_t* ch = a.chosen + int64_t(b) * a.np_stride;
-    const int c = ch[pi];
-    int32_t off = 0, total = 0;
-    for (int j = 0; j < a.nprobe; ++j) {
-        const int cj = ch[j];
-        const int32_t len = a.list_begin[cj + 1] - a.list_begin[cj];
-        if (j < pi) off += len;
-        total += len;
-    }
-    if (blockIdx.x == 0 && pi == 0 && threadIdx.x == 0) a.counts[b] = total;
+    const int c = a.chosen[int64_t(b) * a.np_stride + pi];
+    const int32_t off = a.offs[int64_t(b) * (a.np_stride + 1) + pi];
     const int32_t beg = a.list_begin[c];
     const int32_t n = a.list_begin[c + 1] - beg;
     const int32_t row0 = blockIdx.x * kScoreRowsPerBlock;
@@ -703,6 +726,10 @@ hipError_t fsi_launch_ivf_probe(const IvfProbeLaunch& r) {
     la.cand_ids = ix->d_cand_ids;
     la.counts = ix->d_counts;
     la.stride = ix->cand_stride;
+    la.offs = ix->d_offs;
+    fs_list_offsets_kernel<<<dim3(r.batch), 64, 0, r.stream>>>(la);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     dim3 g3((ix->max_list + kScoreRowsPerBlock - 1) / kScoreRowsPerBlock, r.nprobe, r.batch);
     fs_list_score_kernel<<<g3, 256, 0, r.stream>>>(la);
     e = hipGetLastError();
