@@ -68,6 +68,9 @@ def parse():
                    help="approximate retrieval on a 1M-fact clustered store: build time, latency and "
                         "recall@k of the inverted-file probe against the flat scan")
     p.add_argument("--facts", type=int, default=1_000_000, help="facts of the --ivf store")
+    p.add_argument("--ingest", action="store_true",
+                   help="store ingest (Context-Window Encoding capture) on the Llama-8B shape: facts/s "
+                        "and captured GB/s")
     p.add_argument("--pinned", action="store_true",
                    help="K/V arenas in pinned host memory: time the per-layer fetch -> inject "
                         "pipeline against a plain host-to-device copy (the host link is the bound)")
@@ -96,6 +99,8 @@ def main():
         return bench_attend(args)
     if args.ivf:
         return bench_ivf(args)
+    if args.ingest:
+        return bench_ingest(args)
     wl = synth.make_workload(args.config, k=args.k)
     s = wl.shape
     nl = args.layers or s.num_layers
@@ -250,6 +255,73 @@ def main():
     }
     print(json.dumps(out), flush=True)
     ds.close()
+
+
+def bench_ingest(args):
+    """fs_ingest_facts on the Llama-3.1-8B shape (32 layers, 8 KV heads, head
+    dim 128): 2,048 facts of U[12,48] tokens, each with a window of the 2
+    turns before it (turns of U[12,48] tokens), in calls of 64 facts.  The
+    window arrays stand in for the encoder's per-layer output (random bf16;
+    their content does not matter to the copy).  Bytes: each kept row is read
+    from the window and written to the arena, K and V, every layer:
+    8 * rows * layers * H * D bytes per fact, plus its embedding read and
+    written (8 * E)."""
+    import numpy as np
+    import torch
+
+    from kv_cache_injection_amd import fs
+
+    L, H, D, E, slots, max_len, per_call, w = 32, 8, 128, 768, 2048, 48, 64, 2
+    T = slots * max_len
+    print(f"[bench] ingest: arenas of {T} rows x {L} layers", file=sys.stderr, flush=True)
+    k_pre = [torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    v = [torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    emb = torch.zeros((slots, E), device="cuda")
+    desc = fs.make_desc(num_layers=L, num_kv_heads=H, head_dim=D, embed_dim=E, rope_theta=5e5,
+                        block_size=16, num_users=1, max_batch=1, max_k=50, num_facts=slots, num_tokens=T)
+    st = fs.fs_create_store(desc, np.array([0, slots], np.int64), np.full(slots, max_len, np.int32), emb,
+                            k_pre, v)
+    rng = np.random.default_rng(9)
+    turns = rng.integers(12, max_len + 1, (slots // per_call, per_call, w + 1))
+    wrows = int(turns.sum(axis=2).max()) * per_call
+    win_k = [torch.randn((wrows, H, D), device="cuda").to(torch.bfloat16) for _ in range(L)]
+    win_v = [torch.randn((wrows, H, D), device="cuda").to(torch.bfloat16) for _ in range(L)]
+    new_emb = torch.nn.functional.normalize(torch.randn((per_call, E), device="cuda"), dim=1).contiguous()
+    calls = []
+    for c in range(slots // per_call):
+        lens = turns[c]                                   # [facts, w + 1]: w context turns then the fact
+        start = np.concatenate([[0], np.cumsum(lens.sum(axis=1))[:-1]])
+        calls.append((start + lens[:, :w].sum(axis=1), lens[:, w].astype(np.int32)))
+
+    def run():
+        fs.fs_ingest_init(st, [0], 0)
+        kept = 0
+        for kb, kl in calls:
+            fs.fs_ingest_facts(st, [0] * per_call, win_k, win_v, kb, kl, new_emb)
+            kept += int(kl.sum())
+        return kept
+
+    run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    reps = max(1, min(args.steps, 3))
+    for _ in range(reps):
+        kept = run()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    gb = (4.0 * kept * L * H * D * 2 + 8.0 * slots * E) / dt / 1e9      # bf16: 2 bytes
+    out = {
+        "metric": "store ingest (Context-Window Encoding capture): facts/s and GB/s moved",
+        "value": round(slots / dt, 1), "unit": "facts/s", "n_gpus": 1, "steps": reps, "warmup": 1,
+        "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 bytes", "data": "synthetic",
+        "GBps": round(gb, 1), "rows_kept": kept, "calls": len(calls),
+        "config": {"workload": f"Llama-3.1-8B KV shape ({L} layers x {H} x {D}); {slots} facts of "
+                               f"U[12,{max_len}] tokens, window {w} turns, {per_call} facts per call",
+                   "facts": slots, "window_turns": w},
+    }
+    print(json.dumps(out), flush=True)
+    st.close()
 
 
 def bench_ivf(args):

@@ -116,7 +116,8 @@ typedef struct fs_store_desc {
     int32_t staging_layers;  /* pinned stores: layers the device staging ring
                                 holds (1 .. num_layers); ignored otherwise       */
     int64_t num_facts;       /* >= 1                                             */
-    int64_t num_tokens;      /* == sum of fact_len                               */
+    int64_t num_tokens;      /* arena rows, >= sum of fact_len; rows past the sum
+                                are free for fs_ingest_facts                    */
 } fs_store_desc;
 
 /*
@@ -300,6 +301,65 @@ FS_API fs_status fs_attend_prefill(const fs_store* store, int32_t batch, int32_t
 FS_API fs_status fs_attend_workspace_size(const fs_store* store, int32_t batch,
                                           int32_t num_q_tokens, int32_t num_q_heads,
                                           size_t* bytes);
+
+/* ---- store ingest and eviction (Context-Window Encoding capture) -------- */
+
+/*
+ * Facts are encoded offline with a window of the w conversation turns before
+ * them, and only the fact's own KV is kept: keys taken before RoPE, values
+ * raw (gist.science summary, "Phase Hors-ligne" and "Stockage Pré-RoPE").
+ * The encoder is the serving model's own prefill over [w turns ; fact]; these
+ * calls take its per-layer output and maintain the store.
+ *
+ * Slots: user u owns fact ids user_fact_begin[u] .. user_fact_begin[u+1]-1
+ * (its capacity); the first live_count[u] of them are live.  Retrieval and
+ * injection see live facts only.  Arena rows are handed out in order from
+ * rows_used and are not reused after an eviction (rebuild the store to
+ * compact).  An inverted-file index is not updated: rebuild it after ingest
+ * or eviction.  These calls write the caller's embedding matrix and arenas,
+ * synchronise `stream` before they return, and must not overlap any other
+ * call on the store.
+ */
+
+/*
+ * fs_ingest_init — declare the live facts per user (host [num_users], each
+ * at most the user's capacity) and the first free arena row (every live
+ * fact's rows lie below it).  At creation every slot is live and every row
+ * used.  Errors: FS_E_ARG, FS_E_RANGE, FS_E_HIP.
+ */
+FS_API fs_status fs_ingest_init(fs_store* store, const int32_t* live_counts, int64_t rows_used,
+                                void* stream);
+
+/*
+ * fs_ingest_facts — append n facts (1 .. 4096) in one launch.  Fact i goes to
+ * user user[i] (host array), into that user's next free slot.  k_window /
+ * v_window: host arrays [num_layers] of device-visible bf16 [rows][H][D]
+ * holding the encoder's pre-RoPE keys and raw values of the windows (all
+ * facts' windows in one array per layer); fact i keeps rows keep_begin[i] ..
+ * keep_begin[i] + keep_len[i] - 1 (host arrays; 1 <= keep_len <= the longest
+ * fact at creation), the rest of its window is discarded.  emb: device fp32
+ * [n][embed_dim], fact i's embedding.  fact_ids (host [n], out): the ids
+ * given.  All-or-nothing: a host-checked error (no free slot, arenas full, a
+ * length out of range) writes nothing.  Errors: FS_E_ARG, FS_E_RANGE,
+ * FS_E_HIP.
+ */
+FS_API fs_status fs_ingest_facts(fs_store* store, int32_t n, const int32_t* user,
+                                 const void* const* k_window, const void* const* v_window,
+                                 const int64_t* keep_begin, const int32_t* keep_len,
+                                 const float* emb, void* stream, int32_t* fact_ids);
+
+/*
+ * fs_evict_fact — remove a live fact.  Its user's last live fact moves into
+ * the freed slot (metadata and embedding row), so live ids stay dense;
+ * *moved_from (optional) receives the moved fact's former id, or -1.  Ids
+ * held by the caller for the moved fact change.  Errors: FS_E_ARG,
+ * FS_E_RANGE (not a live fact), FS_E_HIP.
+ */
+FS_API fs_status fs_evict_fact(fs_store* store, int32_t fact_id, void* stream, int32_t* moved_from);
+
+/* fs_store_live — live facts of `user` and the first free arena row. */
+FS_API fs_status fs_store_live(const fs_store* store, int32_t user, int32_t* live,
+                               int64_t* rows_used);
 
 /* ---- approximate retrieval: inverted-file index ------------------------- */
 

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(HERE, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libfs.so")
 
-SOURCES = ["fs_store.hip", "retrieve.hip", "inject.hip", "attend.hip", "ivf.hip"]
+SOURCES = ["fs_store.hip", "retrieve.hip", "inject.hip", "attend.hip", "ivf.hip", "ingest.hip"]
 ARCH = "gfx950"
 
 

@@ -33,7 +33,8 @@ struct fs_store {
     // library-owned device memory
     int64_t* d_fact_begin = nullptr;   // [F+1] first arena row of each fact
     int32_t* d_fact_len = nullptr;     // [F]
-    int64_t* d_user_begin = nullptr;   // [U+1]
+    int64_t* d_user_begin = nullptr;   // [U+1] first fact slot of each user
+    int32_t* d_user_count = nullptr;   // [U] live facts of each user: slots user_begin[u] .. + count
     double* d_inv_freq = nullptr;      // [head_dim/2] theta^(-2i/D)
     uint32_t* d_err = nullptr;         // device error word
     double* d_scores = nullptr;        // [max_batch][max_user_facts] score scratch
@@ -50,6 +51,14 @@ struct fs_store {
     void* d_stage_v = nullptr;
     int32_t* d_stage_ids = nullptr;    // [staging_layers][max_batch][max_k]
     int32_t* d_stage_meta = nullptr;   // [staging_layers][4]: k, batch, layer of the last fetch
+
+    // host mirrors of the metadata that ingest and eviction change
+    std::vector<int64_t> h_user_begin;     // [U+1]
+    std::vector<int32_t> h_user_count;     // [U]
+    std::vector<int64_t> h_fact_begin;     // [F]
+    std::vector<int32_t> h_fact_len;       // [F]
+    int64_t next_row = 0;                  // first arena row never handed out
+    void* d_ingest_items = nullptr;        // [kIngestMax] per-call fact descriptors
 
     // caller-owned, referenced
     const float* emb = nullptr;
@@ -144,6 +153,25 @@ struct IvfProbeLaunch {
 hipError_t fsi_launch_ivf_probe(const IvfProbeLaunch& a);
 // builds ix's centroids, lists and sorted rows (index arrays already allocated)
 hipError_t fsi_ivf_build(fs_ivf* ix, hipStream_t stream);
+
+// one ingested fact: rows [src_row, src_row + len) of the window arrays go to
+// arena rows [dst_row, dst_row + len), slot `slot`, embedding row `emb_row`
+struct IngestItem {
+    int64_t src_row, dst_row;
+    int32_t len, slot, emb_row, pad;
+};
+constexpr int kIngestMax = 4096;          // facts per fs_ingest_facts call
+
+struct IngestLaunch {
+    const fs_store* st;
+    int32_t n;
+    int32_t max_len;
+    const void* const* k_window;           // host array [num_layers] of device-visible [rows][H][D]
+    const void* const* v_window;
+    const float* emb_new;                  // device [n][E]
+    hipStream_t stream;
+};
+hipError_t fsi_launch_ingest(const IngestLaunch& a);
 
 struct FetchLaunch {
     const fs_store* st;

@@ -44,7 +44,8 @@ int ilog2(int64_t x) {
 
 void free_store(fs_store* s) {
     if (!s) return;
-    void* bufs[] = {s->d_fact_begin, s->d_fact_len, s->d_user_begin, s->d_inv_freq, s->d_err,
+    void* bufs[] = {s->d_fact_begin, s->d_fact_len, s->d_user_begin, s->d_user_count,
+                    s->d_ingest_items, s->d_inv_freq, s->d_err,
                     s->d_scores, (void*)s->d_src_k, (void*)s->d_src_v, s->d_tok_src,
                     s->d_tok_dst, s->d_req_len, s->d_stage_k,
                     s->d_stage_v, s->d_stage_ids, s->d_stage_meta};
@@ -134,7 +135,7 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
         total += fact_len[f];
         if (fact_len[f] > max_len) max_len = fact_len[f];
     }
-    if (total != d.num_tokens) return fail(FS_E_ARG, "sum(fact_len) != num_tokens");
+    if (total > d.num_tokens) return fail(FS_E_ARG, "sum(fact_len) exceeds num_tokens");
     if (int64_t(max_len) * d.max_k > INT32_MAX)
         return fail(FS_E_UNSUPPORTED, "max_k * longest fact exceeds 2^31-1 tokens");
 
@@ -201,6 +202,8 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
         {(void**)&st->d_fact_begin, sizeof(int64_t) * (d.num_facts + 1), "fact offsets"},
         {(void**)&st->d_fact_len, sizeof(int32_t) * d.num_facts, "fact lengths"},
         {(void**)&st->d_user_begin, sizeof(int64_t) * (d.num_users + 1), "user offsets"},
+        {(void**)&st->d_user_count, sizeof(int32_t) * d.num_users, "user counts"},
+        {(void**)&st->d_ingest_items, sizeof(IngestItem) * kIngestMax, "ingest descriptors"},
         {(void**)&st->d_inv_freq, sizeof(double) * (D / 2), "frequency table"},
         {(void**)&st->d_err, sizeof(uint32_t), "error word"},
         {(void**)&st->d_scores, sizeof(double) * size_t(d.max_batch) * size_t(max_user > 0 ? max_user : 1), "score scratch"},
@@ -236,12 +239,20 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
         }
     }
 
+    st->h_user_begin.assign(user_fact_begin, user_fact_begin + d.num_users + 1);
+    st->h_user_count.resize(d.num_users);
+    for (int u = 0; u < d.num_users; ++u)
+        st->h_user_count[u] = static_cast<int32_t>(user_fact_begin[u + 1] - user_fact_begin[u]);
+    st->h_fact_begin.assign(fb.begin(), fb.end() - 1);
+    st->h_fact_len.assign(fact_len, fact_len + d.num_facts);
+    st->next_row = total;                     // rows past the facts are free for ingest
     std::vector<int32_t> meta_init(4 * size_t(pinned ? d.staging_layers : 0), -1);
     uint32_t zero = 0;
     struct { void* dst; const void* src; size_t bytes; } cps[] = {
         {st->d_fact_begin, fb.data(), sizeof(int64_t) * fb.size()},
         {st->d_fact_len, fact_len, sizeof(int32_t) * d.num_facts},
         {st->d_user_begin, user_fact_begin, sizeof(int64_t) * (d.num_users + 1)},
+        {st->d_user_count, st->h_user_count.data(), sizeof(int32_t) * d.num_users},
         {st->d_inv_freq, inv.data(), sizeof(double) * inv.size()},
         {st->d_err, &zero, sizeof(uint32_t)},
         {(void*)st->d_src_k, st->src_k.data(), sizeof(void*) * d.num_layers},
@@ -396,6 +407,139 @@ fs_status fs_attend_workspace_size(const fs_store* store, int32_t batch, int32_t
     return FS_OK;
 }
 
+fs_status fs_ingest_init(fs_store* store, const int32_t* live_counts, int64_t rows_used, void* stream) {
+    g_msg[0] = 0;
+    if (!store || !live_counts) return fail(FS_E_ARG, "null pointer argument");
+    const fs_store_desc& d = store->desc;
+    if (rows_used < 0 || rows_used > d.num_tokens)
+        return fail(FS_E_RANGE, "rows_used %lld outside [0, num_tokens]", static_cast<long long>(rows_used));
+    for (int u = 0; u < d.num_users; ++u) {
+        const int64_t cap = store->h_user_begin[u + 1] - store->h_user_begin[u];
+        if (live_counts[u] < 0 || live_counts[u] > cap)
+            return fail(FS_E_RANGE, "user %d: %d live facts, capacity %lld", u, live_counts[u],
+                        static_cast<long long>(cap));
+        for (int32_t j = 0; j < live_counts[u]; ++j) {
+            const int64_t f = store->h_user_begin[u] + j;
+            if (store->h_fact_begin[f] + store->h_fact_len[f] > rows_used)
+                return fail(FS_E_RANGE, "live fact %lld uses rows at or past rows_used", static_cast<long long>(f));
+        }
+    }
+    store->h_user_count.assign(live_counts, live_counts + d.num_users);
+    store->next_row = rows_used;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(store->d_user_count, live_counts, sizeof(int32_t) * d.num_users,
+                                  hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "user counts upload");
+    return FS_OK;
+}
+
+fs_status fs_ingest_facts(fs_store* store, int32_t n, const int32_t* user, const void* const* k_window,
+                          const void* const* v_window, const int64_t* keep_begin, const int32_t* keep_len,
+                          const float* emb, void* stream, int32_t* fact_ids) {
+    g_msg[0] = 0;
+    if (!store || !user || !k_window || !v_window || !keep_begin || !keep_len || !emb || !fact_ids)
+        return fail(FS_E_ARG, "null pointer argument");
+    const fs_store_desc& d = store->desc;
+    if (n < 1 || n > kIngestMax) return fail(FS_E_RANGE, "n %d outside [1, %d]", n, kIngestMax);
+    if (!aligned(emb, 16)) return fail(FS_E_ARG, "emb not 16-byte aligned");
+    for (int l = 0; l < d.num_layers; ++l) {
+        if (!k_window[l] || !v_window[l]) return fail(FS_E_ARG, "layer %d window pointer is null", l);
+        if (!aligned(k_window[l], 16) || !aligned(v_window[l], 16))
+            return fail(FS_E_ARG, "layer %d window not 16-byte aligned", l);
+    }
+    // plan every fact before touching anything: slots and rows
+    std::vector<int32_t> count = store->h_user_count;
+    int64_t row = store->next_row;
+    std::vector<IngestItem> items(n);
+    int32_t max_len = 0;
+    for (int i = 0; i < n; ++i) {
+        const int u = user[i];
+        if (u < 0 || u >= d.num_users) return fail(FS_E_RANGE, "fact %d: user %d outside [0, %d)", i, u, d.num_users);
+        if (keep_len[i] < 1 || keep_len[i] > store->max_fact_len)
+            return fail(FS_E_RANGE, "fact %d: length %d outside [1, %d]", i, keep_len[i], store->max_fact_len);
+        if (keep_begin[i] < 0) return fail(FS_E_RANGE, "fact %d: negative window row", i);
+        const int64_t cap = store->h_user_begin[u + 1] - store->h_user_begin[u];
+        if (count[u] >= cap) return fail(FS_E_RANGE, "user %d has no free fact slot", u);
+        if (row + keep_len[i] > d.num_tokens) return fail(FS_E_RANGE, "arenas full (%lld rows)",
+                                                          static_cast<long long>(d.num_tokens));
+        items[i].src_row = keep_begin[i];
+        items[i].dst_row = row;
+        items[i].len = keep_len[i];
+        items[i].slot = static_cast<int32_t>(store->h_user_begin[u] + count[u]);
+        items[i].emb_row = i;
+        items[i].pad = 0;
+        ++count[u];
+        row += keep_len[i];
+        max_len = std::max(max_len, keep_len[i]);
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(store->d_ingest_items, items.data(), sizeof(IngestItem) * n,
+                                  hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(ingest descriptors)");
+    IngestLaunch a{store, n, max_len, k_window, v_window, emb, s};
+    e = fsi_launch_ingest(a);
+    if (e != hipSuccess) return hip_fail(e, "ingest launch");
+    e = hipMemcpyAsync(store->d_user_count, count.data(), sizeof(int32_t) * d.num_users,
+                       hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);   // host descriptors and counts are consumed
+    if (e != hipSuccess) return hip_fail(e, "ingest");
+    for (int i = 0; i < n; ++i) {
+        store->h_fact_begin[items[i].slot] = items[i].dst_row;
+        store->h_fact_len[items[i].slot] = items[i].len;
+        fact_ids[i] = items[i].slot;
+    }
+    store->h_user_count = count;
+    store->next_row = row;
+    return FS_OK;
+}
+
+fs_status fs_evict_fact(fs_store* store, int32_t fact_id, void* stream, int32_t* moved_from) {
+    g_msg[0] = 0;
+    if (!store) return fail(FS_E_ARG, "null store");
+    const fs_store_desc& d = store->desc;
+    if (fact_id < 0 || fact_id >= d.num_facts) return fail(FS_E_RANGE, "fact %d outside [0, %lld)", fact_id,
+                                                            static_cast<long long>(d.num_facts));
+    const auto it = std::upper_bound(store->h_user_begin.begin(), store->h_user_begin.end(), int64_t(fact_id));
+    const int u = static_cast<int>(it - store->h_user_begin.begin()) - 1;
+    const int64_t first = store->h_user_begin[u];
+    if (fact_id >= first + store->h_user_count[u]) return fail(FS_E_RANGE, "fact %d is not live", fact_id);
+    const int64_t last = first + store->h_user_count[u] - 1;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (last != fact_id) {
+        // the user's last live fact moves into the freed slot
+        store->h_fact_begin[fact_id] = store->h_fact_begin[last];
+        store->h_fact_len[fact_id] = store->h_fact_len[last];
+        e = hipMemcpyAsync(store->d_fact_begin + fact_id, &store->h_fact_begin[fact_id], sizeof(int64_t),
+                           hipMemcpyHostToDevice, s);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(store->d_fact_len + fact_id, &store->h_fact_len[fact_id], sizeof(int32_t),
+                               hipMemcpyHostToDevice, s);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(const_cast<float*>(store->emb) + int64_t(fact_id) * d.embed_dim,
+                               store->emb + last * d.embed_dim, sizeof(float) * d.embed_dim,
+                               hipMemcpyDeviceToDevice, s);
+    }
+    --store->h_user_count[u];
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(store->d_user_count + u, &store->h_user_count[u], sizeof(int32_t),
+                           hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);   // the host sources above must stay unchanged until copied
+    if (e != hipSuccess) return hip_fail(e, "eviction copies");
+    if (moved_from) *moved_from = last != fact_id ? static_cast<int32_t>(last) : -1;
+    return FS_OK;
+}
+
+fs_status fs_store_live(const fs_store* store, int32_t user, int32_t* live, int64_t* rows_used) {
+    g_msg[0] = 0;
+    if (!store) return fail(FS_E_ARG, "null store");
+    if (user < 0 || user >= store->desc.num_users) return fail(FS_E_RANGE, "user %d out of range", user);
+    if (live) *live = store->h_user_count[user];
+    if (rows_used) *rows_used = store->next_row;
+    return FS_OK;
+}
+
 static void free_ivf(fs_ivf* ix) {
     if (!ix) return;
     void* bufs[] = {ix->d_cent, ix->d_list_begin, ix->d_members, ix->d_emb_sorted, ix->d_cent_range,
@@ -421,7 +565,7 @@ fs_status fs_ivf_build(const fs_store* store, int32_t user, int32_t nlist, int32
     int64_t range[2] = {0, 0};
     hipError_t e = hipMemcpy(range, store->d_user_begin + user, sizeof(range), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpy(user range)");
-    const int64_t n = range[1] - range[0];
+    const int64_t n = store->h_user_count[user];
     if (n < nlist) return fail(FS_E_RANGE, "user %d has %lld facts, fewer than nlist %d", user,
                                static_cast<long long>(n), nlist);
     if (n > INT32_MAX / 2) return fail(FS_E_RANGE, "user too large for one index");

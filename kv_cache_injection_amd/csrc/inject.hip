@@ -71,6 +71,7 @@ struct PlanArgs {
     const int64_t* fact_begin;
     const int32_t* fact_len;
     const int64_t* user_begin;
+    const int32_t* user_count;      // live facts per user (from user_begin[u])
     int32_t num_users;
     int32_t layer_begin, layer_end, heads;
     const int32_t* stage_ids;       // non-null for pinned stores
@@ -126,7 +127,7 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 // Returns the error bits (0 when the request can be served); *L and *nf get
 // the segment length and the number of real (non-pad) ids.
 __device__ uint32_t plan_request(const int32_t* user, const int32_t* ids, int k,
-                                 const int64_t* user_begin, int num_users,
+                                 const int64_t* user_begin, const int32_t* user_count, int num_users,
                                  const int32_t* fact_len, const int64_t* fact_begin, int b,
                                  int32_t* off, int64_t* row0, int* L_out, int* nf_out) {
     const int lane = threadIdx.x & 63;
@@ -135,7 +136,7 @@ __device__ uint32_t plan_request(const int32_t* user, const int32_t* ids, int k,
     const bool bad_user = (u < 0 || u >= num_users);
     if (bad_user) bits |= FS_ERR_USER;
     const int64_t ub0 = bad_user ? 0 : user_begin[u];
-    const int64_t ub1 = bad_user ? 0 : user_begin[u + 1];
+    const int64_t ub1 = bad_user ? 0 : ub0 + user_count[u];     // the user's live facts
     // Lengths are counted only up to the first -1 pad, so every token t < L
     // maps into a valid fact of the user even when the request is rejected
     // (the kernels may read before the verdict is in, never out of bounds).
@@ -206,6 +207,7 @@ struct FetchArgs {
     const int64_t* fact_begin;
     const int32_t* fact_len;
     const int64_t* user_begin;
+    const int32_t* user_count;      // live facts per user (from user_begin[u])
     int32_t num_users;
     int32_t heads;
     int32_t layer_begin, layer_end, layers_per_block;
@@ -280,7 +282,7 @@ __global__ __launch_bounds__(kPlanThreads) void fs_plan_kernel(PlanArgs a) {
     const int b = blockIdx.x;
     if (threadIdx.x < 64) {
         int L = 0, nf = 0;
-        uint32_t bits = plan_request(a.user, a.ids, a.k, a.user_begin, a.num_users, a.fact_len,
+        uint32_t bits = plan_request(a.user, a.ids, a.k, a.user_begin, a.user_count, a.num_users, a.fact_len,
                                      a.fact_begin, b, off, row0, &L, &nf);
         bits |= check_request(a, b, L);
         bits = wave_or(bits);
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(kInjectThreads, kInjectOcc) void fs_inject_kernel(I
         }
     } else if (wave == 0) {
         int Lr = 0, nf = 0;
-        const uint32_t bits = plan_request(pa.user, pa.ids, pa.k, pa.user_begin, pa.num_users,
+        const uint32_t bits = plan_request(pa.user, pa.ids, pa.k, pa.user_begin, pa.user_count, pa.num_users,
                                            pa.fact_len, pa.fact_begin, b, off, row0, &Lr, &nf);
         const uint32_t any = wave_or(bits);
         if (lane == 0) {
@@ -455,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void fs_fetch_kernel(FetchArgs a) {
     const int b = blockIdx.y;
     const int lane = threadIdx.x;
     int L = 0, nf = 0;
-    uint32_t bits = plan_request(a.user, a.ids, a.k, a.user_begin, a.num_users, a.fact_len,
+    uint32_t bits = plan_request(a.user, a.ids, a.k, a.user_begin, a.user_count, a.num_users, a.fact_len,
                                  a.fact_begin, b, off, row0, &L, &nf);
     bits = wave_or(bits);
     const int l0 = a.layer_begin + blockIdx.z * a.layers_per_block;
@@ -536,6 +538,7 @@ hipError_t launch_inject(const InjectLaunch& r) {
     pa.fact_begin = st->d_fact_begin;
     pa.fact_len = st->d_fact_len;
     pa.user_begin = st->d_user_begin;
+    pa.user_count = st->d_user_count;
     pa.num_users = d.num_users;
     pa.layer_begin = r.layer_begin;
     pa.layer_end = r.layer_end;
@@ -605,6 +608,7 @@ hipError_t launch_fetch(const FetchLaunch& r) {
     a.fact_begin = st->d_fact_begin;
     a.fact_len = st->d_fact_len;
     a.user_begin = st->d_user_begin;
+    a.user_count = st->d_user_count;
     a.num_users = d.num_users;
     a.heads = d.num_kv_heads;
     a.layer_begin = r.layer_begin;

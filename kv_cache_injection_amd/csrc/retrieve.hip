@@ -80,6 +80,7 @@ struct ScoreArgs {
     const float4* emb;        // [F][E/4]
     int32_t e4;               // E/4
     const int64_t* user_begin;
+    const int32_t* user_count;  // live facts per user, or null: user_begin[u + 1] ends the user
     int32_t num_users;
     const int32_t* user;
     const float4* query;      // [B][E/4]
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(256) void fs_score_kernel(ScoreArgs a) {
     int nq = 1;
     while (nq < kScoreGroup && (b + nq) % kScoreGroup != 0 && b + nq < a.batch && a.user[b + nq] == u) ++nq;
     const int64_t base = a.user_begin[u];
-    const int32_t n = static_cast<int32_t>(a.user_begin[u + 1] - base);
+    const int32_t n = a.user_count ? a.user_count[u] : static_cast<int32_t>(a.user_begin[u + 1] - base);
     const int32_t row0 = blockIdx.x * kScoreRowsPerBlock;
     if (row0 >= n) return;
 
@@ -247,6 +248,7 @@ struct TopkArgs {
     const double* scores;     // [B][stride]
     int32_t stride;
     const int64_t* user_begin;
+    const int32_t* user_count;  // live facts per user, or null: user_begin[u + 1] ends the user
     int32_t num_users;
     const int32_t* user;
     const int32_t* fact_len;
@@ -281,7 +283,8 @@ __global__ __launch_bounds__(kTopkThreads) void fs_topk_kernel(TopkArgs a) {
     const bool bad_user = !mapped && (u < 0 || u >= a.num_users);
     const int64_t base = (mapped || bad_user) ? 0 : a.user_begin[u];
     const int32_t n = mapped ? a.counts[b]
-                             : (bad_user ? 0 : static_cast<int32_t>(a.user_begin[u + 1] - base));
+                             : (bad_user ? 0 : (a.user_count ? a.user_count[u]
+                                                            : static_cast<int32_t>(a.user_begin[u + 1] - base)));
     const int kk = n < k ? n : k;
     const int32_t* imap = mapped ? a.idmap + int64_t(b) * a.stride : nullptr;
     // the id a candidate is ranked and reported by
@@ -647,6 +650,7 @@ hipError_t fsi_launch_retrieve(const RetrieveLaunch& r) {
         sa.emb = reinterpret_cast<const float4*>(st->emb);
         sa.e4 = d.embed_dim / 4;
         sa.user_begin = st->d_user_begin;
+        sa.user_count = st->d_user_count;
         sa.num_users = d.num_users;
         sa.user = r.user;
         sa.query = reinterpret_cast<const float4*>(r.query);
@@ -662,6 +666,7 @@ hipError_t fsi_launch_retrieve(const RetrieveLaunch& r) {
     ta.scores = st->d_scores;
     ta.stride = st->max_user_facts;
     ta.user_begin = st->d_user_begin;
+    ta.user_count = st->d_user_count;
     ta.num_users = d.num_users;
     ta.user = r.user;
     ta.fact_len = st->d_fact_len;

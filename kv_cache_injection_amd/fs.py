@@ -42,7 +42,8 @@ FS_KV_DEVICE = 0
 FS_KV_PINNED_HOST = 1
 
 EXPORTS = ("fs_create_store", "fs_destroy_store", "fs_retrieve_topk", "fs_inject",
-           "fs_fetch_async", "fs_attend_prefill", "fs_attend_workspace_size", "fs_ivf_build",
+           "fs_fetch_async", "fs_attend_prefill", "fs_attend_workspace_size", "fs_ingest_init",
+           "fs_ingest_facts", "fs_evict_fact", "fs_store_live", "fs_ivf_build",
            "fs_ivf_destroy", "fs_ivf_arrays", "fs_ivf_retrieve_topk", "fs_poll_errors",
            "fs_strerror", "fs_last_error_message")
 
@@ -102,6 +103,10 @@ def _load() -> ctypes.CDLL:
         "fs_attend_prefill": (i32, [P, i32, i32, i32, P, P, P, i32, P, i32, P, P, ctypes.c_float,
                                     P, P, ctypes.c_size_t, P]),
         "fs_attend_workspace_size": (i32, [P, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]),
+        "fs_ingest_init": (i32, [P, P, i64, P]),
+        "fs_ingest_facts": (i32, [P, i32, P, P, P, P, P, P, P, P]),
+        "fs_evict_fact": (i32, [P, i32, P, ctypes.POINTER(i32)]),
+        "fs_store_live": (i32, [P, i32, ctypes.POINTER(i32), ctypes.POINTER(i64)]),
         "fs_ivf_build": (i32, [P, i32, i32, i32, i32, P, ctypes.POINTER(P)]),
         "fs_ivf_destroy": (i32, [P]),
         "fs_ivf_arrays": (i32, [P, ctypes.POINTER(fs_ivf_view)]),
@@ -330,6 +335,66 @@ def fs_attend_workspace_size(store, batch: int, num_q_tokens: int, num_q_heads: 
                                        int(num_q_heads), ctypes.byref(n))
     _check(st, "fs_attend_workspace_size")
     return int(n.value)
+
+
+def fs_ingest_init(store, live_counts, rows_used: int, stream=None) -> None:
+    import numpy as np
+    c = np.ascontiguousarray(live_counts, dtype=np.int32)
+    if c.shape != (store.desc.num_users,):
+        raise ValueError("live_counts must have one entry per user")
+    st = _lib.fs_ingest_init(_handle(store), c.ctypes.data_as(ctypes.c_void_p), int(rows_used),
+                             _stream(stream))
+    _check(st, "fs_ingest_init")
+
+
+def fs_ingest_facts(store, user, k_window: Sequence[torch.Tensor], v_window: Sequence[torch.Tensor],
+                    keep_begin, keep_len, emb: torch.Tensor, stream=None):
+    """Append facts: user/keep_begin/keep_len host sequences of length n;
+    k_window/v_window per-layer device bf16 [rows, H, D]; emb device fp32
+    [n, E].  Returns the new fact ids (numpy int32)."""
+    import numpy as np
+    u = np.ascontiguousarray(user, dtype=np.int32)
+    kb = np.ascontiguousarray(keep_begin, dtype=np.int64)
+    kl = np.ascontiguousarray(keep_len, dtype=np.int32)
+    n = u.size
+    if kb.size != n or kl.size != n:
+        raise ValueError("user, keep_begin and keep_len must have the same length")
+    L = store.desc.num_layers
+    if len(k_window) != L or len(v_window) != L:
+        raise ValueError("one window array per layer")
+    H, D, E = store.desc.num_kv_heads, store.desc.head_dim, store.desc.embed_dim
+    for t in list(k_window) + list(v_window):
+        if t.dim() != 3 or t.shape[1:] != (H, D):
+            raise ValueError(f"window arrays must be [rows, {H}, {D}]")
+        if t.dtype not in (torch.bfloat16, torch.int16) or not t.is_contiguous() or t.device.type != "cuda":
+            raise TypeError("window arrays must be contiguous bf16 device tensors")
+        if np.any(kb + kl > t.shape[0]):
+            raise ValueError("a kept row range runs past the window array")
+    karr = (ctypes.c_void_p * L)(*[t.data_ptr() for t in k_window])
+    varr = (ctypes.c_void_p * L)(*[t.data_ptr() for t in v_window])
+    ids = np.zeros(n, np.int32)
+    st = _lib.fs_ingest_facts(_handle(store), int(n), u.ctypes.data_as(ctypes.c_void_p), karr, varr,
+                              kb.ctypes.data_as(ctypes.c_void_p), kl.ctypes.data_as(ctypes.c_void_p),
+                              _ptr(emb, torch.float32, shape=(n, E), name="emb"), _stream(stream),
+                              ids.ctypes.data_as(ctypes.c_void_p))
+    _check(st, "fs_ingest_facts")
+    return ids
+
+
+def fs_evict_fact(store, fact_id: int, stream=None) -> int:
+    """Evict a live fact; returns the former id of the fact moved into its
+    slot, or -1."""
+    moved = ctypes.c_int32(-1)
+    st = _lib.fs_evict_fact(_handle(store), int(fact_id), _stream(stream), ctypes.byref(moved))
+    _check(st, "fs_evict_fact")
+    return int(moved.value)
+
+
+def fs_store_live(store, user: int):
+    live, rows = ctypes.c_int32(0), ctypes.c_int64(0)
+    _check(_lib.fs_store_live(_handle(store), int(user), ctypes.byref(live), ctypes.byref(rows)),
+           "fs_store_live")
+    return int(live.value), int(rows.value)
 
 
 class Ivf:

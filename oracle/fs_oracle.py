@@ -51,7 +51,8 @@ __all__ = [
     "bf16_to_f64", "f64_to_bf16", "score", "select_topk", "decisive_gap",
     "retrieve", "compose", "segment_rows", "placement", "request_problem",
     "rope_inv_freq", "rope_rotate", "inject_request", "expected_rows",
-    "gather_rows", "causal_attention", "attend_prefill", "ivf_probe",
+    "gather_rows", "causal_attention", "attend_prefill", "ivf_probe", "cwe_window",
+    "capture_rows",
 ]
 
 
@@ -358,3 +359,25 @@ def ivf_probe(emb: np.ndarray, centroids: np.ndarray, list_begin: np.ndarray,
     ids[: order.size] = cand[order]
     sc[: order.size] = s[order]
     return ids, sc
+
+
+# --------------------------------------------------------------------------
+# Context-Window Encoding: which tokens the encoder sees, which rows are kept
+# --------------------------------------------------------------------------
+
+def cwe_window(turn_len: Sequence[int], j: int, w: int) -> Tuple[int, int, int, int]:
+    """Context-Window Encoding of fact j (conversation turn j) with a window
+    of w turns [offline "Encodage de la Fenêtre de Contexte"]: the encoder
+    reads turns max(0, j - w) .. j as one sequence, and only the fact's own
+    tokens are kept.  Returns (first token, end token) of the window in the
+    conversation, and (keep_begin, keep_len) of the fact inside the window."""
+    starts = np.concatenate([[0], np.cumsum(np.asarray(turn_len, np.int64))])
+    a = int(starts[max(0, j - w)])
+    b = int(starts[j + 1])
+    return a, b, int(starts[j]) - a, int(turn_len[j])
+
+
+def capture_rows(window: np.ndarray, keep_begin: int, keep_len: int) -> np.ndarray:
+    """The stored part of a window's pre-RoPE K (or raw V): the fact's rows,
+    bytes unchanged; the context rows are discarded."""
+    return np.array(window[keep_begin:keep_begin + keep_len], copy=True)

@@ -135,7 +135,7 @@ def test_create_rejects_pinned_without_staging():
     dict(ufb=(0, 3, 2)),                 # decreasing
     dict(ufb=(0, 2, 3)),                 # does not end at num_facts
     dict(fl=(10, 10, 0, 20)),            # empty fact
-    dict(fl=(10, 10, 10, 11)),           # lengths do not sum to num_tokens
+    dict(fl=(10, 10, 10, 11)),           # lengths exceed num_tokens
     dict(emb=FAKE + 4),                  # misaligned embeddings
     dict(arenas=[FAKE, FAKE + 8]),       # misaligned arena
     dict(arenas=[FAKE, 0]),              # null arena
