@@ -9,11 +9,13 @@ cache).  Inputs are resident in HBM before the timed region; every step uses
 a different (query, start position, block table) set, cycling through
 --sets pre-drawn sets, so the selected facts change from step to step.
 
-Steps are issued as a serving loop would: retrieval on one stream, injection
-on another, so that step i+1's retrieval (latency-bound, a few MB) overlaps
-step i's injection (bandwidth-bound); step i's injection waits on an event
-after step i's retrieval.  ms_per_step_in_order repeats the steps on one
-stream, strictly one after the other.
+Steps are issued as a serving loop with two lanes would: step i runs its
+retrieval and then its injection on stream i % 2, so step i+1's retrieval
+(latency-bound, a few MB) and the start of its injection overlap step i's
+injection (bandwidth-bound).  Retrievals share the store's scratch, so each
+waits on an event after the previous one; the lanes inject into separate
+cache pools.  ms_per_step_in_order repeats the steps on one stream, strictly
+one after the other.
 
 Prints ONE JSON line:
   value       whole-step algorithmic HBM bytes / step time (GB/s)
@@ -125,28 +127,37 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(total)]
 
-    # two streams at the default priority: retrieval of step i+1 runs while
-    # step i injects (the calls share no scratch; ids have a slot per step)
-    s_ret, s_inj = torch.cuda.Stream(), torch.cuda.Stream()
-    ready = [torch.cuda.Event() for _ in range(total)]
+    # Pipelined steps on two lanes (streams at the default priority): step i
+    # retrieves and injects on lane i % 2, so each inject follows its own
+    # retrieval in stream order, and the other lane's retrieval and inject run
+    # beside it.  Retrievals share the store's score scratch, so retrieval i
+    # waits for retrieval i - 1 (an event); the two lanes write separate cache
+    # pools, as two different requests would.  ids have a slot per step.
+    kc2, vc2 = synth.make_caches(wl, layers, "cuda")
+    caches2 = fs.CacheTable(ds.store, kc2, vc2, nb)
+    lanes = (torch.cuda.Stream(), torch.cuda.Stream())
+    ret_done = [torch.cuda.Event() for _ in range(total)]
 
     # arguments marshalled once per step slot; the timed loops only issue
     # the foreign calls
-    def prep(stream_ret, stream_inj):
+    def prep(stream_ret, stream_inj, cache_of=lambda i: caches):
         rc = [fs.prepare_retrieve_topk(ds.store, B, user, sets[i % len(sets)]["query"], k, ids[i],
-                                       None, ntok[i], stream=stream_ret) for i in range(total)]
+                                       None, ntok[i], stream=stream_ret(i)) for i in range(total)]
         ic = [fs.prepare_inject(ds.store, fs.FS_ALL_LAYERS, B, user, ids[i], k,
                                 sets[i % len(sets)]["block_table"], mb, sets[i % len(sets)]["start_pos"],
-                                caches, stream=stream_inj) for i in range(total)]
+                                cache_of(i), stream=stream_inj(i)) for i in range(total)]
         return rc, ic
-    ret_p, inj_p = prep(s_ret, s_inj)                  # pipelined
+    ret_p, inj_p = prep(lambda i: lanes[i % 2], lambda i: lanes[i % 2],
+                        lambda i: caches if i % 2 == 0 else caches2)            # two lanes
     cur = torch.cuda.current_stream()
-    ret_s, inj_s = prep(cur, cur)                      # one stream, in order
+    ret_s, inj_s = prep(lambda i: cur, lambda i: cur)                          # one stream, in order
 
     def step_pipelined(i):
+        lane = lanes[i % 2]
+        if i > 0:
+            lane.wait_event(ret_done[i - 1])
         ret_p[i]()
-        ready[i].record(s_ret)
-        s_inj.wait_event(ready[i])
+        ret_done[i].record(lane)
         inj_p[i]()
 
     def step_serial(i):
@@ -157,8 +168,8 @@ def main():
     for i in range(args.warmup):
         step_pipelined(i)
     torch.cuda.synchronize()
-    # timed region 1: the whole hot path for every step, retrieval of the
-    # next step overlapping injection of the current one (no timing events)
+    # timed region 1: the whole hot path for every step, each lane's
+    # retrieval and inject overlapping the other lane's (no timing events)
     t0 = time.perf_counter()
     for i in range(args.warmup, total):
         step_pipelined(i)
