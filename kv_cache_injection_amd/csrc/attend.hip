@@ -26,7 +26,11 @@
 // contraction index of P.V maps to positions in the order the score tiles
 // produce them (any order works if both operands agree).  K/V tiles of 64
 // positions are staged in LDS (K row-major, V transposed), with the next
-// tile's global loads in flight while the current one is consumed.
+// tile's global loads in flight while the current one is consumed.  A block's
+// raw Q and first K/V tile are loaded before anything else (the block-table
+// entries of that tile are range-checked where they are read), so their
+// latency overlaps the request check and the (cos, sin) table.  Long contexts
+// are split over several blocks whose partial results a second kernel merges.
 
 #include <hip/hip_runtime.h>
 
@@ -97,8 +101,17 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 1) void fs_attend_kernel(A
     auto sVt = reinterpret_cast<uint16_t(*)[kVPad]>(s_raw + kKT * kKPad * 2);   // [d][pos]
     auto s_cs = reinterpret_cast<double2(*)[kD / 2]>(s_raw);                    // [query][i]
 
-    const int qt = blockIdx.x / a.splits, sp = blockIdx.x - qt * a.splits;
-    const int hk = blockIdx.y, b = blockIdx.z;
+    // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin, so
+    // physical id P runs on XCD P mod 8.  Logical ids are handed out in 8
+    // contiguous chunks, one per XCD: the query tiles of one (request, KV
+    // head) then share their K/V tiles in one XCD's L2.
+    const int nblk = gridDim.x * gridDim.y * gridDim.z;
+    const int pid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int xq = nblk >> 3, xr = nblk & 7, xcd = pid & 7;
+    const int lid = xcd * xq + min(xcd, xr) + (pid >> 3);
+    const int lx = lid % gridDim.x;
+    const int qt = lx / a.splits, sp = lx - qt * a.splits;
+    const int hk = (lid / gridDim.x) % gridDim.y, b = lid / (gridDim.x * gridDim.y);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int col = lane & 15;        // the query this lane's S^T / O^T column holds
@@ -111,11 +124,64 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 1) void fs_attend_kernel(A
     const int jq = j_lo + col;
     const bool q_real = jq < a.tq;
 
+    // ---- raw Q (the lane's 8 + 8 elements of each head slot), issued first
+    uint4 qraw[kHS][4];
+#pragma unroll
+    for (int hs = 0; hs < kHS; ++hs) {
+        const int hw = wave + kWaves * hs;
+        const bool hv = hw < a.group && q_real;
+        const uint16_t* qrow = a.q + ((int64_t(b) * a.tq + (q_real ? jq : 0)) * a.hq + hk * a.group +
+                                      (hw < a.group ? hw : 0)) * kD;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int i = (kk & 1) * 32 + 8 * grp + (kk >> 1) * (kD / 2);
+            qraw[hs][kk] = hv ? *reinterpret_cast<const uint4*>(qrow + i) : make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    // ---- the block's tile range (positions checked in int64 first: the
+    // first tile's loads go out before the block-table check below)
+    const bool pos_ok = c0 >= 0 && c0 <= qp0 && int64_t(qp0) + a.tq - 1 <= int64_t(INT32_MAX);
+    const int j_hi = min(a.tq, j_lo + kQT) - 1;            // last real query of the block
+    const int p_end = pos_ok ? qp0 + j_hi : 0;              // last position any of them reads
+    const int ntiles = pos_ok ? (p_end - c0) / kKT + 1 : 0;
+    const int tps = (ntiles + a.splits - 1) / a.splits;     // tiles per split
+    const int t_begin = sp * tps;
+    const int t_end = min(ntiles, t_begin + tps);
+    const int qpos = qp0 + jq;
+
+    // ---- tile staging: thread -> 16-byte vector lvec of positions 4*lq .. 4*lq+3
+    const int lvec = threadIdx.x & 15;
+    const int lq = threadIdx.x >> 4;
+    uint4 kr[4], vr[4];
+    auto gload_row = [&](int r, int p, int blk) {
+        const int64_t row = (int64_t(blk) << a.log2_block) | (p & bs_mask);
+        const int64_t off = (row * a.hkv + hk) * kD + lvec * 8;
+        kr[r] = *reinterpret_cast<const uint4*>(a.kc + off);
+        vr[r] = *reinterpret_cast<const uint4*>(a.vc + off);
+    };
+    if (t_begin < t_end) {
+        // entries read from the table and range-checked here, since the
+        // request's check has not run yet (a rejected request discards them)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int p = c0 + t_begin * kKT + 4 * lq + r;
+            const int64_t ei = p >> a.log2_block;
+            const int blk = p <= p_end && ei < a.max_blocks ? bt[ei] : -1;
+            if (blk >= 0 && blk < a.num_blocks) {
+                gload_row(r, p, blk);
+            } else {
+                kr[r] = make_uint4(0, 0, 0, 0);
+                vr[r] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
+
     // ---- validation of the request (every block checks, one block reports)
     if (wave == 0) {
         uint32_t bits = 0;
         const int64_t last = int64_t(qp0) + a.tq - 1;
-        if (c0 < 0 || c0 > qp0 || last > int64_t(INT32_MAX)) {
+        if (!pos_ok) {
             bits |= FS_ERR_START_POS;
         } else if ((last >> a.log2_block) >= a.max_blocks) {
             bits |= FS_ERR_BLOCK_SHORT;
@@ -145,14 +211,6 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 1) void fs_attend_kernel(A
         }
         return;
     }
-
-    const int j_hi = min(a.tq, j_lo + kQT) - 1;            // last real query of the block
-    const int p_end = qp0 + j_hi;                           // last position any of them reads
-    const int ntiles = (p_end - c0) / kKT + 1;
-    const int tps = (ntiles + a.splits - 1) / a.splits;     // tiles per split
-    const int t_begin = sp * tps;
-    const int t_end = min(ntiles, t_begin + tps);
-    const int qpos = qp0 + jq;
     if (t_begin >= t_end) {
         // nothing of the context falls in this split: an empty partial
         if (q_real && grp == 0) {
@@ -189,25 +247,18 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 1) void fs_attend_kernel(A
     b8 qf[kHS][4];
 #pragma unroll
     for (int hs = 0; hs < kHS; ++hs) {
-        const int hw = wave + kWaves * hs;
-        const bool hv = hw < a.group && q_real;
-        const uint16_t* qrow = a.q + ((int64_t(b) * a.tq + (q_real ? jq : 0)) * a.hq + hk * a.group +
-                                      (hw < a.group ? hw : 0)) * kD;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
+            const uint32_t* w1 = &qraw[hs][kk].x;
+            const uint32_t* w2 = &qraw[hs][kk + 2].x;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int i = kk * 32 + 8 * grp + e;
-                uint16_t y1 = 0, y2 = 0;
-                if (hv) {
-                    const double x1 = bf16_to_f32(qrow[i]);
-                    const double x2 = bf16_to_f32(qrow[i + kD / 2]);
-                    const double2 cs = s_cs[col][i];
-                    y1 = static_cast<uint16_t>(f64_to_bf16_bits(fma(x1, cs.x, -(x2 * cs.y))));
-                    y2 = static_cast<uint16_t>(f64_to_bf16_bits(fma(x2, cs.x, x1 * cs.y)));
-                }
-                qf[hs][kk][e] = as_bf16(y1);
-                qf[hs][kk + 2][e] = as_bf16(y2);
+                const double x1 = bf16_to_f32(static_cast<uint16_t>(w1[e >> 1] >> (16 * (e & 1))));
+                const double x2 = bf16_to_f32(static_cast<uint16_t>(w2[e >> 1] >> (16 * (e & 1))));
+                const double2 cs = s_cs[col][i];
+                qf[hs][kk][e] = as_bf16(static_cast<uint16_t>(f64_to_bf16_bits(fma(x1, cs.x, -(x2 * cs.y)))));
+                qf[hs][kk + 2][e] = as_bf16(static_cast<uint16_t>(f64_to_bf16_bits(fma(x2, cs.x, x1 * cs.y))));
             }
         }
     }
@@ -224,21 +275,13 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 1) void fs_attend_kernel(A
         for (int dc = 0; dc < 8; ++dc) o[hs][dc] = f4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    // ---- tile staging: thread -> 16-byte vector lvec of positions 4*lq .. 4*lq+3
-    const int lvec = threadIdx.x & 15;
-    const int lq = threadIdx.x >> 4;
-    uint4 kr[4], vr[4];
     auto gload = [&](int t) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int p = c0 + t * kKT + 4 * lq + r;
             if (p <= p_end) {
                 const int64_t ei = p >> a.log2_block;
-                const int blk = bt_cached ? s_bt[ei - e_first] : bt[ei];
-                const int64_t row = (int64_t(blk) << a.log2_block) | (p & bs_mask);
-                const int64_t off = (row * a.hkv + hk) * kD + lvec * 8;
-                kr[r] = *reinterpret_cast<const uint4*>(a.kc + off);
-                vr[r] = *reinterpret_cast<const uint4*>(a.vc + off);
+                gload_row(r, p, bt_cached ? s_bt[ei - e_first] : bt[ei]);
             } else {
                 kr[r] = make_uint4(0, 0, 0, 0);
                 vr[r] = make_uint4(0, 0, 0, 0);
@@ -259,7 +302,6 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 1) void fs_attend_kernel(A
         }
     };
 
-    gload(t_begin);
     for (int t = t_begin; t < t_end; ++t) {
         lstore();
         __syncthreads();                                    // tile t staged
@@ -355,31 +397,44 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 1) void fs_attend_kernel(A
 }
 
 // Merge of the split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
-// with M = max_s m_s.  One thread per (row, d); a NaN max marks a rejected
-// request, whose rows are left unwritten.
+// with M = max_s m_s.  One thread per (row, 4 consecutive d): every split's
+// (max, sum) is loaded at once, then every contributing split's partial, and
+// the sums run in split order.  A NaN max marks a rejected request, whose
+// rows are left unwritten.
 __global__ __launch_bounds__(256) void fs_attend_combine_kernel(AttendArgs a, int64_t rows) {
     const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t row = idx / kD;
+    const int64_t row = idx / (kD / 4);
     if (row >= rows) return;
-    const int d = static_cast<int>(idx - row * kD);
+    const int d = 4 * static_cast<int>(idx - row * (kD / 4));
+    float2 ml[kMaxSplits];
     float mx = -1e30f;
     bool bad = false;
-    for (int s2 = 0; s2 < a.splits; ++s2) {
-        const float2 ml = a.part_ml[int64_t(s2) * rows + row];
-        if (ml.x != ml.x) bad = true;
-        mx = fmaxf(mx, ml.x);
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplits; ++s2) {
+        ml[s2] = s2 < a.splits ? a.part_ml[int64_t(s2) * rows + row] : make_float2(-1e30f, 0.0f);
+        if (ml[s2].x != ml[s2].x) bad = true;
+        mx = fmaxf(mx, ml[s2].x);
     }
     if (bad) return;
-    float num = 0.0f, den = 0.0f;
-    for (int s2 = 0; s2 < a.splits; ++s2) {
-        const float2 ml = a.part_ml[int64_t(s2) * rows + row];
-        const float w = __builtin_amdgcn_exp2f(ml.x - mx);
-        if (w > 0.0f) {                  // empty splits leave no partial output
-            den += w * ml.y;
-            num += w * a.part_o[(int64_t(s2) * rows + row) * kD + d];
+    float w[kMaxSplits];
+    f4 x[kMaxSplits];
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplits; ++s2) {
+        w[s2] = s2 < a.splits ? __builtin_amdgcn_exp2f(ml[s2].x - mx) : 0.0f;
+        // empty splits leave no partial output
+        x[s2] = w[s2] > 0.0f ? *reinterpret_cast<const f4*>(a.part_o + (int64_t(s2) * rows + row) * kD + d)
+                             : f4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    f4 num = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    float den = 0.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplits; ++s2) {
+        if (w[s2] > 0.0f) {
+            den += w[s2] * ml[s2].y;
+            num += w[s2] * x[s2];
         }
     }
-    a.out[row * kD + d] = num / den;
+    *reinterpret_cast<f4*>(a.out + row * kD + d) = num / den;
 }
 
 }  // namespace
@@ -439,6 +494,6 @@ hipError_t fsi_launch_attend(const AttendLaunch& r) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     const int64_t rows = int64_t(r.batch) * r.num_q_tokens * r.num_q_heads;
-    fs_attend_combine_kernel<<<static_cast<unsigned>((rows * kD + 255) / 256), 256, 0, r.stream>>>(a, rows);
+    fs_attend_combine_kernel<<<static_cast<unsigned>((rows * (kD / 4) + 255) / 256), 256, 0, r.stream>>>(a, rows);
     return hipGetLastError();
 }
