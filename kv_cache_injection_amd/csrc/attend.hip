@@ -88,12 +88,19 @@ __device__ __forceinline__ __bf16 as_bf16(uint16_t h) {
     return r;
 }
 
-template <int kHS>                    // head slots per wave: group <= 4 * kHS
-__global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 1) void fs_attend_kernel(AttendArgs a) {
+// kQS sub-tiles of 16 query tokens per block; the 4 waves form kQS teams of
+// kWaves / kQS waves, team qs covering sub-tile qs.  Wave hb of a team holds
+// the query heads hb, hb + kWaves / kQS, ... (kHS head slots): a team covers
+// the whole GQA group when group <= kHS * kWaves / kQS.  A wave's head slots
+// share every K and V fragment it reads from LDS.
+template <int kHS, int kQS>
+__global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(AttendArgs a) {
+    constexpr int kWQ = kWaves / kQS;     // waves per team
+    constexpr int kBQ = kQT * kQS;        // query tokens per block
     // the fp64 (cos, sin) table of the block's queries is only needed before
     // the first tile, so it shares storage with the K/V tiles
     constexpr int kTileBytes = (kKT * kKPad + kD * kVPad) * 2;
-    constexpr int kCSBytes = kQT * (kD / 2) * 16;
+    constexpr int kCSBytes = kBQ * (kD / 2) * 16;
     __shared__ __attribute__((aligned(16))) unsigned char s_raw[kTileBytes > kCSBytes ? kTileBytes : kCSBytes];
     __shared__ int s_bt[kBtCache];
     __shared__ int s_ok;
@@ -113,22 +120,27 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 1) void fs_attend_kernel(A
     const int qt = lx / a.splits, sp = lx - qt * a.splits;
     const int hk = (lid / gridDim.x) % gridDim.y, b = lid / (gridDim.x * gridDim.y);
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches
+    const int qs = wave / kWQ;        // the wave's query sub-tile
+    const int hb = wave - qs * kWQ;   // its first head
     const int col = lane & 15;        // the query this lane's S^T / O^T column holds
     const int grp = lane >> 4;        // 4-row group of the MFMA layouts
     const int c0 = a.ctx_begin[b];
     const int qp0 = a.q_pos[b];
     const int64_t bs_mask = (int64_t(1) << a.log2_block) - 1;
     const int32_t* bt = a.bt + int64_t(b) * a.max_blocks;
-    const int j_lo = qt * kQT;
+    const int jb = qt * kBQ;          // the block's first query
+    const int j_lo = jb + qs * kQT;   // the wave's first query
     const int jq = j_lo + col;
     const bool q_real = jq < a.tq;
+    const bool wave_live = j_lo < a.tq;
+    auto head = [&](int hs) { return hb + kWQ * hs; };
 
     // ---- raw Q (the lane's 8 + 8 elements of each head slot), issued first
     uint4 qraw[kHS][4];
 #pragma unroll
     for (int hs = 0; hs < kHS; ++hs) {
-        const int hw = wave + kWaves * hs;
+        const int hw = head(hs);
         const bool hv = hw < a.group && q_real;
         const uint16_t* qrow = a.q + ((int64_t(b) * a.tq + (q_real ? jq : 0)) * a.hq + hk * a.group +
                                       (hw < a.group ? hw : 0)) * kD;
@@ -142,13 +154,14 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 1) void fs_attend_kernel(A
     // ---- the block's tile range (positions checked in int64 first: the
     // first tile's loads go out before the block-table check below)
     const bool pos_ok = c0 >= 0 && c0 <= qp0 && int64_t(qp0) + a.tq - 1 <= int64_t(INT32_MAX);
-    const int j_hi = min(a.tq, j_lo + kQT) - 1;            // last real query of the block
+    const int j_hi = min(a.tq, jb + kBQ) - 1;               // last real query of the block
     const int p_end = pos_ok ? qp0 + j_hi : 0;              // last position any of them reads
     const int ntiles = pos_ok ? (p_end - c0) / kKT + 1 : 0;
     const int tps = (ntiles + a.splits - 1) / a.splits;     // tiles per split
     const int t_begin = sp * tps;
     const int t_end = min(ntiles, t_begin + tps);
     const int qpos = qp0 + jq;
+    const int wave_last = qp0 + min(a.tq - 1, j_lo + kQT - 1);   // the wave's last query position
 
     // ---- tile staging: thread -> 16-byte vector lvec of positions 4*lq .. 4*lq+3
     const int lvec = threadIdx.x & 15;
@@ -198,30 +211,24 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 1) void fs_attend_kernel(A
         }
     }
     __syncthreads();
-    if (!s_ok) {
-        // a split run marks its partials so the combine writes nothing
-        if (a.splits > 1 && q_real) {
+    auto mark = [&](float2 v) {       // this split's (max, sum) of the wave's rows
+        if (q_real && grp == 0) {
 #pragma unroll
             for (int hs = 0; hs < kHS; ++hs) {
-                const int hw = wave + kWaves * hs;
-                if (hw < a.group && grp == 0)
-                    a.part_ml[((int64_t(sp) * gridDim.z + b) * a.tq + jq) * a.hq + hk * a.group + hw] =
-                        make_float2(__builtin_nanf(""), 0.0f);
+                const int hw = head(hs);
+                if (hw < a.group)
+                    a.part_ml[((int64_t(sp) * gridDim.z + b) * a.tq + jq) * a.hq + hk * a.group + hw] = v;
             }
         }
+    };
+    if (!s_ok) {
+        // a split run marks its partials so the combine writes nothing
+        if (a.splits > 1) mark(make_float2(__builtin_nanf(""), 0.0f));
         return;
     }
     if (t_begin >= t_end) {
         // nothing of the context falls in this split: an empty partial
-        if (q_real && grp == 0) {
-#pragma unroll
-            for (int hs = 0; hs < kHS; ++hs) {
-                const int hw = wave + kWaves * hs;
-                if (hw < a.group)
-                    a.part_ml[((int64_t(sp) * gridDim.z + b) * a.tq + jq) * a.hq + hk * a.group + hw] =
-                        make_float2(-1e30f, 0.0f);
-            }
-        }
+        mark(make_float2(-1e30f, 0.0f));
         return;
     }
 
@@ -232,12 +239,12 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 1) void fs_attend_kernel(A
     if (bt_cached)
         for (int64_t j = e_first + threadIdx.x; j <= e_last; j += kThreads) s_bt[j - e_first] = bt[j];
 
-    // ---- fp64 (cos, sin) of (position of query j_lo + qq) * w_i, shared by the heads
-    for (int e = threadIdx.x; e < kQT * (kD / 2); e += kThreads) {
+    // ---- fp64 (cos, sin) of (position of query jb + qq) * w_i, shared by the heads
+    for (int e = threadIdx.x; e < kBQ * (kD / 2); e += kThreads) {
         const int qq = e / (kD / 2);
         const int i = e - qq * (kD / 2);
         double sv, cv;
-        sincos(static_cast<double>(qp0 + j_lo + qq) * a.inv_freq[i], &sv, &cv);
+        sincos(static_cast<double>(qp0 + jb + qq) * a.inv_freq[i], &sv, &cv);
         s_cs[qq][i] = make_double2(cv, sv);
     }
     __syncthreads();
@@ -256,7 +263,7 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 1) void fs_attend_kernel(A
                 const int i = kk * 32 + 8 * grp + e;
                 const double x1 = bf16_to_f32(static_cast<uint16_t>(w1[e >> 1] >> (16 * (e & 1))));
                 const double x2 = bf16_to_f32(static_cast<uint16_t>(w2[e >> 1] >> (16 * (e & 1))));
-                const double2 cs = s_cs[col][i];
+                const double2 cs = s_cs[qs * kQT + col][i];
                 qf[hs][kk][e] = as_bf16(static_cast<uint16_t>(f64_to_bf16_bits(fma(x1, cs.x, -(x2 * cs.y)))));
                 qf[hs][kk + 2][e] = as_bf16(static_cast<uint16_t>(f64_to_bf16_bits(fma(x2, cs.x, x1 * cs.y))));
             }
@@ -307,56 +314,66 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 1) void fs_attend_kernel(A
         __syncthreads();                                    // tile t staged
         if (t + 1 < t_end) gload(t + 1);                   // in flight during the math
         const int tbase = c0 + t * kKT;
-#pragma unroll
-        for (int hs = 0; hs < kHS; ++hs) {
-            if (wave + kWaves * hs >= a.group) continue;    // uniform over the wave
-            // S^T for 4 sub-tiles of 16 positions: st[sub][i] = S[jq][tbase + 16*sub + 4*grp + i]
-            f4 st[4];
+        // a tile wholly after the wave's queries changes nothing (every weight
+        // is 0), so the wave skips it; so do waves without a real query
+        if (wave_live && tbase <= wave_last) {
+            // S^T for 4 sub-tiles of 16 positions: st[hs][sub][i] = S[jq][tbase + 16*sub + 4*grp + i]
+            f4 st[kHS][4];
 #pragma unroll
             for (int sub = 0; sub < 4; ++sub) {
-                st[sub] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int hs = 0; hs < kHS; ++hs) st[hs][sub] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     const b8 ka = *reinterpret_cast<const b8*>(&sK[16 * sub + col][kk * 32 + 8 * grp]);
-                    st[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[hs][kk], st[sub], 0, 0, 0);
+                    // a slot past the group computes on zero Q and is never
+                    // written: no branch between the matrix instructions
+#pragma unroll
+                    for (int hs = 0; hs < kHS; ++hs)
+                        st[hs][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[hs][kk], st[hs][sub], 0, 0, 0);
                 }
             }
-            // causal mask only where the tile reaches past the block's first
+            // causal mask only where the tile reaches past the wave's first
             // query position; columns of absent queries are never written
             const bool full = tbase + kKT - 1 <= qp0 + j_lo;
-            float tmax = -1e30f;
+            b8 pb[kHS][2];
+            float alpha[kHS];
 #pragma unroll
-            for (int sub = 0; sub < 4; ++sub) {
+            for (int hs = 0; hs < kHS; ++hs) {
+                float tmax = -1e30f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float x = st[sub][i] * a.scale_log2;
-                    if (!full && tbase + 16 * sub + 4 * grp + i > qpos) x = -1e30f;
-                    st[sub][i] = x;
-                    tmax = fmaxf(tmax, x);
+                for (int sub = 0; sub < 4; ++sub) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float x = st[hs][sub][i] * a.scale_log2;
+                        if (!full && tbase + 16 * sub + 4 * grp + i > qpos) x = -1e30f;
+                        st[hs][sub][i] = x;
+                        tmax = fmaxf(tmax, x);
+                    }
                 }
-            }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-            const float m_new = fmaxf(m[hs], tmax);
-            const float alpha = __builtin_amdgcn_exp2f(m[hs] - m_new);
-            m[hs] = m_new;
-            // P^T fragments for the two 32-position halves: k = 8*grp + e maps to
-            // position 32*hh + 16*(e/4) + 4*grp + e%4, the lane's own scores
-            b8 pb[2];
-            float psum = 0.0f;
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+                const float m_new = fmaxf(m[hs], tmax);
+                alpha[hs] = __builtin_amdgcn_exp2f(m[hs] - m_new);
+                m[hs] = m_new;
+                // P^T fragments for the two 32-position halves: k = 8*grp + e maps to
+                // position 32*hh + 16*(e/4) + 4*grp + e%4, the lane's own scores
+                float psum = 0.0f;
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
+                for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float pe = __builtin_amdgcn_exp2f(st[2 * hh + e / 4][e % 4] - m_new);
-                    pb[hh][e] = static_cast<__bf16>(pe);
-                    psum += pe;
+                    for (int e = 0; e < 8; ++e) {
+                        const float pe = __builtin_amdgcn_exp2f(st[hs][2 * hh + e / 4][e % 4] - m_new);
+                        pb[hs][hh][e] = static_cast<__bf16>(pe);
+                        psum += pe;
+                    }
                 }
+                lp[hs] = lp[hs] * alpha[hs] + psum;
             }
-            lp[hs] = lp[hs] * alpha + psum;
 #pragma unroll
             for (int dc = 0; dc < 8; ++dc) {
-                o[hs][dc] *= alpha;
+#pragma unroll
+                for (int hs = 0; hs < kHS; ++hs) o[hs][dc] *= alpha[hs];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     // A = V^T row dc*16 + col, in the position order of pb
@@ -364,7 +381,9 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 1) void fs_attend_kernel(A
                     const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
                     const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
                     const b8 va = __builtin_bit_cast(b8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-                    o[hs][dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hh], o[hs][dc], 0, 0, 0);
+#pragma unroll
+                    for (int hs = 0; hs < kHS; ++hs)
+                        o[hs][dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hs][hh], o[hs][dc], 0, 0, 0);
                 }
             }
         }
@@ -374,7 +393,7 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 1) void fs_attend_kernel(A
     // ---- lane holds O[jq][dc*16 + 4*grp .. +3] (unnormalised)
 #pragma unroll
     for (int hs = 0; hs < kHS; ++hs) {
-        const int hw = wave + kWaves * hs;
+        const int hw = head(hs);
         if (hw >= a.group) continue;
         float l = lp[hs];
         l += __shfl_xor(l, 16, 64);
@@ -439,8 +458,17 @@ __global__ __launch_bounds__(256) void fs_attend_combine_kernel(AttendArgs a, in
 
 }  // namespace
 
-int fsi_attend_splits(const fs_store* st, int32_t batch, int32_t num_q_tokens) {
-    const int64_t base = int64_t((num_q_tokens + kQT - 1) / kQT) * st->desc.num_kv_heads * batch;
+namespace {
+
+// Query sub-tiles per block: two when two waves' head slots hold the whole
+// GQA group and the request has more than one sub-tile of queries.
+int attend_qsub(int group, int32_t num_q_tokens) { return group <= 4 && num_q_tokens > kQT ? 2 : 1; }
+
+}  // namespace
+
+int fsi_attend_splits(const fs_store* st, int32_t batch, int32_t num_q_tokens, int32_t num_q_heads) {
+    const int bq = kQT * attend_qsub(num_q_heads / st->desc.num_kv_heads, num_q_tokens);
+    const int64_t base = int64_t((num_q_tokens + bq - 1) / bq) * st->desc.num_kv_heads * batch;
     int64_t sp = (2 * int64_t(st->num_cus) + base - 1) / base;
     return static_cast<int>(sp < 1 ? 1 : (sp > kMaxSplits ? kMaxSplits : sp));
 }
@@ -474,7 +502,7 @@ hipError_t fsi_launch_attend(const AttendLaunch& r) {
     a.err = st->d_err;
     // split the context when one range per (query tile, KV head, request)
     // would leave the device idle and the workspace holds the partials
-    int splits = fsi_attend_splits(st, r.batch, r.num_q_tokens);
+    int splits = fsi_attend_splits(st, r.batch, r.num_q_tokens, r.num_q_heads);
     while (splits > 1 && fsi_attend_workspace_bytes(splits, r.batch, r.num_q_tokens, r.num_q_heads) >
                              r.workspace_bytes)
         --splits;
@@ -485,12 +513,20 @@ hipError_t fsi_launch_attend(const AttendLaunch& r) {
         a.part_o = static_cast<float*>(r.workspace);
         a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(r.workspace) + size_t(splits) * rows * kD * sizeof(float));
     }
-    const dim3 grid(static_cast<unsigned>((r.num_q_tokens + kQT - 1) / kQT * splits),
+    const int qsub = attend_qsub(a.group, r.num_q_tokens);
+    const int bq = kQT * qsub;
+    const dim3 grid(static_cast<unsigned>((r.num_q_tokens + bq - 1) / bq * splits),
                     static_cast<unsigned>(d.num_kv_heads), static_cast<unsigned>(r.batch));
-    if (a.group <= kWaves)
-        fs_attend_kernel<1><<<grid, kThreads, 0, r.stream>>>(a);
-    else
-        fs_attend_kernel<2><<<grid, kThreads, 0, r.stream>>>(a);
+    if (qsub == 2) {
+        if (a.group <= kWaves / 2)
+            fs_attend_kernel<1, 2><<<grid, kThreads, 0, r.stream>>>(a);
+        else
+            fs_attend_kernel<2, 2><<<grid, kThreads, 0, r.stream>>>(a);
+    } else if (a.group <= kWaves) {
+        fs_attend_kernel<1, 1><<<grid, kThreads, 0, r.stream>>>(a);
+    } else {
+        fs_attend_kernel<2, 1><<<grid, kThreads, 0, r.stream>>>(a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     const int64_t rows = int64_t(r.batch) * r.num_q_tokens * r.num_q_heads;

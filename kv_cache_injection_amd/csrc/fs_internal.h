@@ -116,7 +116,7 @@ struct AttendLaunch {
 };
 hipError_t fsi_launch_attend(const AttendLaunch& a);
 // context splits the launch would use, and the workspace that many need
-int fsi_attend_splits(const fs_store* st, int32_t batch, int32_t num_q_tokens);
+int fsi_attend_splits(const fs_store* st, int32_t batch, int32_t num_q_tokens, int32_t num_q_heads);
 size_t fsi_attend_workspace_bytes(int splits, int32_t batch, int32_t num_q_tokens, int32_t num_q_heads);
 
 // Inverted-file index over one user's facts (approximate retrieval).
