@@ -709,11 +709,17 @@ def recorded_traffic(config: str, layers: int):
 
 def cpu_baseline(wl, ds, layers, n_req, max_host_bytes=16 << 30):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    retrieve + compose + rotate + scatter for ``n_req`` requests, single
-    thread, over the resident layers whose arenas fit ``max_host_bytes`` of
-    host memory (all of them for the Llama-shaped store).  Same
+    retrieve + compose + rotate + scatter for ``n_req`` requests, over the
+    resident layers whose arenas fit ``max_host_bytes`` of host memory (all of
+    them for the Llama-shaped store).  Timed twice: on one thread (BLAS
+    limited to one thread too), and on all the host cores given to the
+    process (at most 16), each request's layers split over a thread pool
+    (numpy releases the interpreter lock inside its array operations).  Same
     algorithmic-bytes accounting."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
+    from threadpoolctl import threadpool_limits
 
     import oracle
     from kv_cache_injection_amd import synth
@@ -729,24 +735,47 @@ def cpu_baseline(wl, ds, layers, n_req, max_host_bytes=16 << 30):
     shape = (nb, s.block_size, s.num_kv_heads, s.head_dim)
     kc = [np.full(shape, synth.SENTINEL_BITS, np.uint16) for _ in use]
     vc = [np.full(shape, synth.SENTINEL_BITS, np.uint16) for _ in use]
-    total_bytes = 0
-    t0 = time.perf_counter()
     sets = synth.request_sets(wl, n_req, seed=wl.seed + 1)   # the bench's first sets
-    for i in range(n_req):
+    u = int(wl.users[0])
+    n_user = int(wl.user_fact_begin[u + 1] - wl.user_fact_begin[u])
+
+    def one_request(i, pool=None, chunks=None):
         r = sets[i]
-        u = int(wl.users[0])
         ids, _ = oracle.retrieve(wl.emb, wl.user_fact_begin, u, r["queries"][0], wl.k)
-        L = oracle.inject_request(kb, vb, kc, vc, ids, wl.fact_len, wl.fact_token_begin,
-                                  int(r["start_pos"][0]), r["block_table"][0], s.block_size,
-                                  s.rope_theta, use)
-        n_user = int(wl.user_fact_begin[u + 1] - wl.user_fact_begin[u])
-        total_bytes += 8 * L * nl * s.num_kv_heads * s.head_dim + 4 * n_user * s.embed_dim
-    dt = time.perf_counter() - t0
+        args = (ids, wl.fact_len, wl.fact_token_begin, int(r["start_pos"][0]), r["block_table"][0],
+                s.block_size, s.rope_theta)
+        if pool is None:
+            L = oracle.inject_request(kb, vb, kc, vc, *args, use)
+        else:
+            futs = [pool.submit(oracle.inject_request, [kb[j] for j in c], [vb[j] for j in c],
+                                [kc[j] for j in c], [vc[j] for j in c], *args, c) for c in chunks]
+            L = [f.result() for f in futs][0]
+        return 8 * L * nl * s.num_kv_heads * s.head_dim + 4 * n_user * s.embed_dim
+
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        total_bytes = sum(one_request(i) for i in range(n_req))
+        dt = time.perf_counter() - t0
+        try:
+            ncore = len(os.sched_getaffinity(0))
+        except AttributeError:
+            ncore = os.cpu_count() or 1
+        nt = max(1, min(16, ncore, nl))
+        chunks = [use[j::nt] for j in range(nt)]
+        with ThreadPoolExecutor(nt) as pool:
+            t1 = time.perf_counter()
+            total_all = sum(one_request(i, pool, chunks) for i in range(n_req))
+            dt_all = time.perf_counter() - t1
     return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s",
             "requests_per_s": round(n_req / dt, 4), "cores": 1, "kind": "oracle",
             "seconds": round(dt, 2),
             "sample": f"{n_req} request(s) of the {s.name} workload (the first request of each "
-                      f"set), {nl} layer(s), k={wl.k}: numpy fp64 oracle, one thread"}
+                      f"set), {nl} layer(s), k={wl.k}: numpy fp64 oracle, one thread",
+            "all_cores": {"value": round(total_all / dt_all / 1e9, 4), "unit": "GB/s",
+                          "requests_per_s": round(n_req / dt_all, 4), "cores": nt,
+                          "seconds": round(dt_all, 2),
+                          "sample": "the same requests, each request's layers split over a pool of "
+                                    f"{nt} threads"}}
 
 
 if __name__ == "__main__":
