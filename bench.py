@@ -20,8 +20,8 @@ one after the other.
 Prints ONE JSON line:
   value       whole-step algorithmic HBM bytes / step time (GB/s)
   roofline    the inject kernel: its algorithmic bytes per launch over its
-              average launch time, measured with HIP events on the launch
-              stream over the timed region, against 8 TB/s
+              average launch time (HIP events on the launch stream around the
+              steps' injects issued back to back), against 8 TB/s
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
 
 Algorithmic bytes: inject = 8 * L * layers * heads * head_dim (K and V, bf16,
@@ -124,8 +124,7 @@ def main():
     total = args.warmup + args.steps
     ids = torch.empty((total, B, k), dtype=torch.int32, device="cuda")   # one slot per step
     ntok = torch.zeros((total, B), dtype=torch.int32, device="cuda")
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(total)]
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
 
     # Pipelined steps on two lanes (streams at the default priority): step i
     # retrieves and injects on lane i % 2, so each inject follows its own
@@ -188,27 +187,28 @@ def main():
     torch.cuda.synchronize()
     u1 = time.perf_counter()
 
-    # timed region 2: the same steps in order with HIP events around each
-    # launch on the launch stream, for the per-kernel durations the roofline
-    # uses
+    # timed region 2: per-kernel average durations for the roofline, from
+    # HIP events on the launch stream: the steps' retrievals back to back
+    # between two events, then their injects back to back between two more
+    # (each inject reads the ids its step's retrieval wrote); the average is
+    # the span over the number of launches
+    e0.record()
     for i in range(args.warmup, total):
-        e0, e1, e2 = ev[i]
-        e0.record()
         ret_s[i]()
-        e1.record()
+    e1.record()
+    for i in range(args.warmup, total):
         inj_s[i]()
-        e2.record()
+    e2.record()
     torch.cuda.synchronize()
 
     wall = t1 - t0
-    timed = range(args.warmup, total)
     row_bytes = 2 * s.num_kv_heads * s.head_dim                      # one token, one layer, K or V
     inject_bytes = 4 * row_bytes * L.sum(axis=1) * nl                # K,V read + write
     n_user = np.diff(wl.user_fact_begin)[wl.users]
     scan_bytes = 4 * int(n_user.sum()) * s.embed_dim
     step_bytes = inject_bytes + scan_bytes
-    inj_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in timed])
-    ret_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in timed])
+    inj_ms = np.full(args.steps, e1.elapsed_time(e2) / args.steps)
+    ret_ms = np.full(args.steps, e0.elapsed_time(e1) / args.steps)
     achieved = float(inject_bytes.sum() / (inj_ms.sum() * 1e-3) / 1e9)
     value = float(step_bytes.sum() / wall / 1e9)
     ms_per_step = wall / args.steps * 1e3
