@@ -225,6 +225,22 @@ FS_API fs_status fs_inject(const fs_store* store, int32_t layer, int32_t batch,
                     int32_t num_blocks, void* stream);
 
 /*
+ * fs_inject_layers — fs_inject over the layers [layer_begin, layer_end) in
+ * one launch (same passages, same per-layer result, same checks and errors).
+ * A layer-pipelined caller injects the first layers alone and the rest in
+ * larger chunks: one launch per chunk instead of one per layer.
+ *   0 <= layer_begin < layer_end <= num_layers, else FS_E_RANGE.  On pinned
+ *   stores every layer of the range reads its own staging slot, so the range
+ *   spans at most staging_layers layers (FS_ERR_STAGING otherwise).
+ */
+FS_API fs_status fs_inject_layers(const fs_store* store, int32_t layer_begin, int32_t layer_end,
+                           int32_t batch, const int32_t* user, const int32_t* ids, int32_t k,
+                           const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* start_pos,
+                           void* const* k_cache, void* const* v_cache,
+                           int32_t num_blocks, void* stream);
+
+/*
  * fs_fetch_async — host-DRAM offload (gist.science summary, "Résultats":
  * the KV store can be offloaded to host DRAM at a small TTFT cost).
  * Pinned stores only.  Gathers the selected facts' K and V rows of layers

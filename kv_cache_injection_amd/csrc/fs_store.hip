@@ -303,15 +303,16 @@ fs_status fs_retrieve_topk(const fs_store* store, int32_t batch, const int32_t* 
     return FS_OK;
 }
 
-fs_status fs_inject(const fs_store* store, int32_t layer, int32_t batch, const int32_t* user,
-                    const int32_t* ids, int32_t k, const int32_t* block_table, int32_t max_blocks,
-                    const int32_t* start_pos, void* const* k_cache, void* const* v_cache,
-                    int32_t num_blocks, void* stream) {
+fs_status fs_inject_layers(const fs_store* store, int32_t layer_begin, int32_t layer_end, int32_t batch,
+                           const int32_t* user, const int32_t* ids, int32_t k, const int32_t* block_table,
+                           int32_t max_blocks, const int32_t* start_pos, void* const* k_cache,
+                           void* const* v_cache, int32_t num_blocks, void* stream) {
     g_msg[0] = 0;
     if (!store) return fail(FS_E_ARG, "null store");
     const fs_store_desc& d = store->desc;
-    if (layer != FS_ALL_LAYERS && (layer < 0 || layer >= d.num_layers))
-        return fail(FS_E_RANGE, "layer %d outside [0, %d)", layer, d.num_layers);
+    if (layer_begin < 0 || layer_end > d.num_layers || layer_begin >= layer_end)
+        return fail(FS_E_RANGE, "layer range [%d, %d) invalid for %d layers", layer_begin, layer_end,
+                    d.num_layers);
     if (batch < 1 || batch > d.max_batch)
         return fail(FS_E_RANGE, "batch %d outside [1, %d]", batch, d.max_batch);
     if (k < 0 || k > d.max_k) return fail(FS_E_RANGE, "k %d outside [0, %d]", k, d.max_k);
@@ -321,19 +322,32 @@ fs_status fs_inject(const fs_store* store, int32_t layer, int32_t batch, const i
         return fail(FS_E_ARG, "int32 argument not 4-byte aligned");
     if (max_blocks < 1) return fail(FS_E_BLOCKTABLE, "max_blocks %d < 1", max_blocks);
     if (num_blocks < 1) return fail(FS_E_BLOCKTABLE, "num_blocks %d < 1", num_blocks);
-    int lb = layer == FS_ALL_LAYERS ? 0 : layer;
-    int le = layer == FS_ALL_LAYERS ? d.num_layers : layer + 1;
-    for (int l = lb; l < le; ++l) {
+    for (int l = layer_begin; l < layer_end; ++l) {
         if (!k_cache[l] || !v_cache[l]) return fail(FS_E_ARG, "layer %d cache pointer is null", l);
         if (!aligned(k_cache[l], 16) || !aligned(v_cache[l], 16))
             return fail(FS_E_ARG, "layer %d cache not 16-byte aligned", l);
     }
     if (k == 0) return FS_OK;
-    InjectLaunch a{store, lb, le, batch, user, ids, k, block_table, max_blocks, start_pos,
+    InjectLaunch a{store, layer_begin, layer_end, batch, user, ids, k, block_table, max_blocks, start_pos,
                    k_cache, v_cache, num_blocks, reinterpret_cast<hipStream_t>(stream)};
     hipError_t e = fsi_launch_inject(a);
     if (e != hipSuccess) return hip_fail(e, "inject launch");
     return FS_OK;
+}
+
+fs_status fs_inject(const fs_store* store, int32_t layer, int32_t batch, const int32_t* user,
+                    const int32_t* ids, int32_t k, const int32_t* block_table, int32_t max_blocks,
+                    const int32_t* start_pos, void* const* k_cache, void* const* v_cache,
+                    int32_t num_blocks, void* stream) {
+    g_msg[0] = 0;
+    if (!store) return fail(FS_E_ARG, "null store");
+    const int32_t L = store->desc.num_layers;
+    if (layer != FS_ALL_LAYERS && (layer < 0 || layer >= L))
+        return fail(FS_E_RANGE, "layer %d outside [0, %d)", layer, L);
+    const int32_t lb = layer == FS_ALL_LAYERS ? 0 : layer;
+    const int32_t le = layer == FS_ALL_LAYERS ? L : layer + 1;
+    return fs_inject_layers(store, lb, le, batch, user, ids, k, block_table, max_blocks, start_pos, k_cache,
+                            v_cache, num_blocks, stream);
 }
 
 fs_status fs_fetch_async(const fs_store* store, int32_t batch, const int32_t* user,

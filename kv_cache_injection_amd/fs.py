@@ -42,7 +42,7 @@ FS_KV_DEVICE = 0
 FS_KV_PINNED_HOST = 1
 
 EXPORTS = ("fs_create_store", "fs_destroy_store", "fs_retrieve_topk", "fs_inject",
-           "fs_fetch_async", "fs_attend_prefill", "fs_attend_workspace_size", "fs_ingest_init",
+           "fs_inject_layers", "fs_fetch_async", "fs_attend_prefill", "fs_attend_workspace_size", "fs_ingest_init",
            "fs_ingest_facts", "fs_evict_fact", "fs_store_live", "fs_ivf_build",
            "fs_ivf_destroy", "fs_ivf_arrays", "fs_ivf_retrieve_topk", "fs_poll_errors",
            "fs_strerror", "fs_last_error_message")
@@ -99,6 +99,7 @@ def _load() -> ctypes.CDLL:
         "fs_destroy_store": (i32, [P]),
         "fs_retrieve_topk": (i32, [P, i32, P, P, i32, P, P, P, P]),
         "fs_inject": (i32, [P, i32, i32, P, P, i32, P, i32, P, P, P, i32, P]),
+        "fs_inject_layers": (i32, [P, i32, i32, i32, P, P, i32, P, i32, P, P, P, i32, P]),
         "fs_fetch_async": (i32, [P, i32, P, P, i32, i32, i32, P]),
         "fs_attend_prefill": (i32, [P, i32, i32, i32, P, P, P, i32, P, i32, P, P, ctypes.c_float,
                                     P, P, ctypes.c_size_t, P]),
@@ -284,6 +285,18 @@ def fs_inject(store, layer: int, batch: int, user: torch.Tensor, ids: torch.Tens
         _ptr(start_pos, torch.int32, shape=(batch,), name="start_pos"),
         table.k, table.v, table.num_blocks, _stream(stream))
     _check(st, "fs_inject")
+
+
+def fs_inject_layers(store, layer_begin: int, layer_end: int, batch: int, user: torch.Tensor,
+                     ids: torch.Tensor, k: int, block_table: torch.Tensor, max_blocks: int,
+                     start_pos: torch.Tensor, caches: "CacheTable", stream=None) -> None:
+    """fs_inject over the layers [layer_begin, layer_end) in one launch."""
+    if not isinstance(caches, CacheTable):
+        raise TypeError("fs_inject_layers takes a CacheTable")
+    if 0 <= layer_begin < layer_end <= len(caches.present) and not all(caches.present[layer_begin:layer_end]):
+        raise ValueError(f"no cache given for some layer of [{layer_begin}, {layer_end})")
+    prepare_inject(store, (layer_begin, layer_end), batch, user, ids, k, block_table, max_blocks,
+                   start_pos, caches, stream=stream)()
 
 
 def fs_fetch_async(store, batch: int, user: torch.Tensor, ids: torch.Tensor, k: int,
@@ -502,19 +515,24 @@ def prepare_retrieve_topk(store, batch: int, user, query, k: int, ids, scores=No
                     (store, user, query, ids, scores, num_tokens))
 
 
-def prepare_inject(store, layer: int, batch: int, user, ids, k: int, block_table,
+def prepare_inject(store, layer, batch: int, user, ids, k: int, block_table,
                    max_blocks: int, start_pos, caches: "CacheTable", stream=None) -> Prepared:
+    """``layer``: one layer, FS_ALL_LAYERS, or a (begin, end) pair for
+    fs_inject_layers."""
     if not isinstance(caches, CacheTable):
         raise TypeError("prepare_inject takes a CacheTable")
-    args = (_handle(store), int(layer), int(batch),
+    if isinstance(layer, tuple):
+        fn, where, lay = _lib.fs_inject_layers, "fs_inject_layers", (int(layer[0]), int(layer[1]))
+    else:
+        fn, where, lay = _lib.fs_inject, "fs_inject", (int(layer),)
+    args = (_handle(store), *lay, int(batch),
             _ptr(user, torch.int32, shape=(batch,), name="user"),
             _ptr(ids, torch.int32, shape=(batch, k), name="ids"), int(k),
             _ptr(block_table, torch.int32, shape=(batch, max_blocks), name="block_table"),
             int(max_blocks),
             _ptr(start_pos, torch.int32, shape=(batch,), name="start_pos"),
             caches.k, caches.v, caches.num_blocks, _stream(stream))
-    return Prepared(_lib.fs_inject, args, "fs_inject",
-                    (store, user, ids, block_table, start_pos, caches))
+    return Prepared(fn, args, where, (store, user, ids, block_table, start_pos, caches))
 
 
 def make_desc(**kw) -> fs_store_desc:

@@ -7,9 +7,9 @@ InferScale injects into the engine's paged cache at serving time and offloads
 the store to host memory when it does not fit the GPU (gist.science summary,
 "Phase En-ligne" and "Résultats").
 
-``LayerInjector`` issues one fs_inject per layer on a side stream and records
-one event per layer; the forward waits on ``wait(l)`` before it reads layer
-l.  ``PinnedLayerInjector`` does the same for stores whose K/V live in pinned
+``LayerInjector`` issues fs_inject launches on a side stream, one per chunk
+of consecutive layers (one layer per chunk by default), and records one event
+per chunk; the forward waits on ``wait(l)`` before it reads layer l.  ``PinnedLayerInjector`` does the same for stores whose K/V live in pinned
 host memory: the fetch of layer l's rows over the host link (fs_fetch_async,
 into staging slot l % staging_layers) runs on a fetch stream, the injection
 of layer l waits for that fetch, and the fetch that refills a slot waits for
@@ -29,7 +29,11 @@ from . import fs
 
 
 class LayerInjector:
-    """Per-layer injection of one batch on a side stream (device stores)."""
+    """Layer-pipelined injection of one batch on a side stream (device
+    stores): one launch per chunk of consecutive layers, one event per chunk.
+    One chunk per layer is the plain per-layer pipeline.  A first chunk of
+    one layer followed by larger chunks keeps what the forward waits for
+    before its first layer small, with fewer launches overall."""
 
     def __init__(self, store, caches: "fs.CacheTable", num_layers: int,
                  stream: Optional[torch.cuda.Stream] = None):
@@ -37,28 +41,55 @@ class LayerInjector:
         self.caches = caches
         self.num_layers = num_layers
         self.stream = stream or torch.cuda.Stream()
-        self.done: List[torch.cuda.Event] = [torch.cuda.Event() for _ in range(num_layers)]
+        self._events: List[torch.cuda.Event] = [torch.cuda.Event() for _ in range(num_layers)]
+        self._event_of: List[Optional[torch.cuda.Event]] = [None] * num_layers
+        self._waited = {}                 # stream -> the chunk event it last waited on
 
     def prepare(self, batch: int, user, ids, k: int, block_table, max_blocks: int, start_pos,
-                layers: Optional[Sequence[int]] = None) -> List["tuple[int, fs.Prepared]"]:
-        """Marshal the per-layer calls once (validated like fs_inject), for
-        batches that reuse the same buffers."""
-        ls = range(self.num_layers) if layers is None else layers
-        return [(l, fs.prepare_inject(self.store, l, batch, user, ids, k, block_table, max_blocks,
-                                      start_pos, self.caches, stream=self.stream)) for l in ls]
+                layers: Optional[Sequence[int]] = None,
+                chunks: Optional[Sequence["tuple[int, int]"]] = None) -> List["tuple[tuple, fs.Prepared]"]:
+        """Marshal the calls once (validated like fs_inject), for batches that
+        reuse the same buffers.  ``chunks``: consecutive (begin, end) layer
+        ranges, each one fs_inject_layers launch; default one per layer (of
+        ``layers``, default all)."""
+        if chunks is None:
+            ls = range(self.num_layers) if layers is None else layers
+            chunks = [(l, l + 1) for l in ls]
+        out = []
+        for b, e in chunks:
+            if not 0 <= b < e <= self.num_layers:
+                raise ValueError(f"layer chunk ({b}, {e}) outside [0, {self.num_layers})")
+            lay = b if e == b + 1 else (b, e)
+            out.append(((b, e), fs.prepare_inject(self.store, lay, batch, user, ids, k, block_table,
+                                                  max_blocks, start_pos, self.caches, stream=self.stream)))
+        return out
 
     def launch(self, calls, after: Optional[torch.cuda.Stream] = None):
-        """Enqueue prepared per-layer calls.  ``after`` (default: the current
-        stream) is the stream whose pending work produced the ids: the side
-        stream waits for it first."""
+        """Enqueue prepared calls.  ``after`` (default: the current stream) is
+        the stream whose pending work produced the ids: the side stream waits
+        for it first."""
         self.stream.wait_stream(after or torch.cuda.current_stream())
-        for l, call in calls:
+        self._waited.clear()
+        for i, ((b, e), call) in enumerate(calls):
             call()
-            self.done[l].record(self.stream)
+            ev = self._events[i]
+            ev.record(self.stream)
+            for l in range(b, e):
+                self._event_of[l] = ev
 
     def wait(self, layer: int, stream: Optional[torch.cuda.Stream] = None):
-        """Make ``stream`` (default: current) wait until ``layer`` is injected."""
-        (stream or torch.cuda.current_stream()).wait_event(self.done[layer])
+        """Make ``stream`` (default: current) wait until ``layer`` is injected.
+        A stream waits on each chunk's event once: the later layers of a
+        chunk it has already waited for add no wait (every cross-stream wait
+        costs the waiting queue a few microseconds)."""
+        ev = self._event_of[layer]
+        if ev is None:
+            raise RuntimeError(f"layer {layer} was not launched")
+        st = stream or torch.cuda.current_stream()
+        if self._waited.get(st) is ev:
+            return
+        st.wait_event(ev)
+        self._waited[st] = ev
 
 
 class PinnedLayerInjector:

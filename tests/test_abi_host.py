@@ -152,6 +152,7 @@ def test_null_store_is_rejected_everywhere():
     assert L.fs_retrieve_topk(None, 1, FAKE, FAKE, 1, FAKE, None, None, None) == fs.FS_E_ARG
     arr = (ctypes.c_void_p * 1)(FAKE)
     assert L.fs_inject(None, 0, 1, FAKE, FAKE, 1, FAKE, 4, FAKE, arr, arr, 4, None) == fs.FS_E_ARG
+    assert L.fs_inject_layers(None, 0, 1, 1, FAKE, FAKE, 1, FAKE, 4, FAKE, arr, arr, 4, None) == fs.FS_E_ARG
     assert L.fs_fetch_async(None, 1, FAKE, FAKE, 1, 0, 1, None) == fs.FS_E_ARG
     assert L.fs_poll_errors(None, None, ctypes.byref(flags)) == fs.FS_E_ARG
     assert L.fs_destroy_store(None) == fs.FS_OK
