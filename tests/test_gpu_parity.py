@@ -304,6 +304,46 @@ def test_head_dims_and_block_sizes(D, H, bs):
     ds2.close()
 
 
+def _random_shape(case: int):
+    """A seeded random layout: heads, head dim, block size, theta, users,
+    batch, k, fact lengths and start positions drawn per case."""
+    import dataclasses
+    r = np.random.default_rng(9000 + case)
+    H = int(r.choice([1, 2, 4, 8, 16]))
+    D = int(r.choice([64, 128, 256]))
+    bs = int(r.choice([1, 2, 4, 8, 16, 32, 64]))
+    users = int(r.integers(1, 6))
+    batch = int(r.integers(1, users + 1))
+    k = int(r.integers(1, 65))
+    lo = int(r.integers(1, 20))
+    hi = int(r.integers(lo, 61))
+    start_hi = int(r.integers(1, 3000))
+    per_req = -(-(start_hi - 1 + k * hi) // bs)
+    return dataclasses.replace(
+        synth.CONFIGS["concurrent"], name=f"rand{case}", num_layers=2, num_kv_heads=H, head_dim=D,
+        rope_theta=float(r.choice([1e4, 5e5, 1e6])), embed_dim=int(r.choice([16, 64, 384])),
+        num_users=users, facts_per_user=int(r.integers(1, 200)), len_lo=lo, len_hi=hi, batch=batch, k=k,
+        start_lo=0, start_hi=start_hi, block_size=bs, pool_blocks=batch * per_req + int(r.integers(0, 50)),
+        table="shared_pool")
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_layouts(case):
+    """Seeded random shapes (k may exceed a user's fact count), both layers
+    compared row by row with the oracle and every other byte with the
+    sentinel."""
+    shape = _random_shape(case)
+    wl = synth.make_workload(shape, seed=9100 + case)
+    say(f"random layout {case}: H={shape.num_kv_heads} D={shape.head_dim} bs={shape.block_size} "
+        f"users={shape.num_users} B={shape.batch} k={shape.k} len=[{shape.len_lo},{shape.len_hi}] "
+        f"start<{shape.start_hi} facts/user={shape.facts_per_user}")
+    ds, req, ids, scores, ntok, kc, vc = _run(wl, [0, 1])
+    o = check_retrieval(wl, _host(ids), _host(scores), _host(ntok), range(shape.batch), wl.k)
+    check_injection(wl, ds, kc, vc, o, [0, 1])
+    check_sentinel(kc, vc, written_mask(wl, o, kc[0].shape[0]), [0, 1])
+    ds.close()
+
+
 def test_multi_user_batch_small():
     wl = synth.make_workload("concurrent", num_users=12, facts_per_user=150, batch=12)
     ds, req, ids, scores, ntok, kc, vc = _run(wl, [0, 5])
