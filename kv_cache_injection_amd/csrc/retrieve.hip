@@ -43,11 +43,9 @@ constexpr int kScoreWaves = 4;
 constexpr int kScoreRowsPerWave = 2;
 constexpr int kScoreRowsPerBlock = kScoreWaves * kScoreRowsPerWave;
 constexpr int kScoreGroup = 8;       // queries of one user scored per block
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kTopkSmallN = 4096;     // up to this many scores a 256-thread block selects
 constexpr int kBins = 2048;          // value bins of the threshold search
 constexpr int kCandMax = 2048;       // largest candidate set ranked directly
-constexpr int kKeep = 4;             // scores per thread kept in registers
 
 __device__ __forceinline__ uint64_t order_key(double x) {
     uint64_t u = (x == 0.0) ? 0ull : static_cast<uint64_t>(__double_as_longlong(x));
@@ -264,7 +262,14 @@ struct TopkArgs {
     const int32_t* idmap;
 };
 
-__global__ __launch_bounds__(kTopkThreads) void fs_topk_kernel(TopkArgs a) {
+// kT threads: 256 for stores of up to kTopkSmallN scores per request (a
+// small block starts sooner beside a running inject and syncs faster),
+// 1024 above.
+template <int kT>
+__global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
+    constexpr int kTopkThreads = kT;
+    constexpr int kTopkWaves = kT / 64;
+    constexpr int kKeep = 4096 / kT;       // scores per thread kept in registers
     __shared__ int hist[256];
     __shared__ uint64_t cand_key[fsi::kMaxK];
     __shared__ int32_t cand_idx[fsi::kMaxK];
@@ -372,11 +377,16 @@ __global__ __launch_bounds__(kTopkThreads) void fs_topk_kernel(TopkArgs a) {
                 if (tid + j * kTopkThreads < n) atomicAdd(&s_bin[value_bin(xv[j], lo, scale)], 1);
             for (int i = tail0; i < n; i += kTopkThreads) atomicAdd(&s_bin[value_bin(sc[i], lo, scale)], 1);
             __syncthreads();
-            // suffix counts from the top bin down: thread tid owns the two
-            // bins at descending positions 2*tid and 2*tid + 1
-            const int hb0 = kBins - 1 - 2 * tid, hb1 = hb0 - 1;
-            const int c0 = s_bin[hb0], c1 = s_bin[hb1];
-            const int local = c0 + c1;
+            // suffix counts from the top bin down: thread tid owns the kBPT
+            // bins at descending positions kBPT*tid .. kBPT*tid + kBPT - 1
+            constexpr int kBPT = kBins / kTopkThreads;
+            int cb[kBPT];
+            int local = 0;
+#pragma unroll
+            for (int j = 0; j < kBPT; ++j) {
+                cb[j] = s_bin[kBins - 1 - (kBPT * tid + j)];
+                local += cb[j];
+            }
             int incl = local;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -389,12 +399,16 @@ __global__ __launch_bounds__(kTopkThreads) void fs_topk_kernel(TopkArgs a) {
             for (int w = 0; w < wave; ++w) before += s_wsum[w];
             // the k-th best score lies in the bin where the count of scores
             // above it first reaches kk
-            if (before < kk && kk <= before + c0) {
-                s_t = hb0;
-                s_C = before + c0;
-            } else if (before + c0 < kk && kk <= before + local) {
-                s_t = hb1;
-                s_C = before + local;
+            {
+                int cum = before;
+#pragma unroll
+                for (int j = 0; j < kBPT; ++j) {
+                    if (cum < kk && kk <= cum + cb[j]) {
+                        s_t = kBins - 1 - (kBPT * tid + j);
+                        s_C = cum + cb[j];
+                    }
+                    cum += cb[j];
+                }
             }
             __syncthreads();
             const int t = s_t, C = s_C;
@@ -642,6 +656,19 @@ outputs:
 
 }  // namespace
 
+
+namespace {
+
+// One block per request; n_max bounds the scores any request of the launch has.
+void launch_topk(int64_t n_max, dim3 grid, size_t lds, hipStream_t stream, const TopkArgs& a) {
+    if (n_max <= kTopkSmallN)
+        fs_topk_kernel<256><<<grid, 256, lds, stream>>>(a);
+    else
+        fs_topk_kernel<1024><<<grid, 1024, lds, stream>>>(a);
+}
+
+}  // namespace
+
 hipError_t fsi_launch_retrieve(const RetrieveLaunch& r) {
     const fs_store* st = r.st;
     const fs_store_desc& d = st->desc;
@@ -677,7 +704,7 @@ hipError_t fsi_launch_retrieve(const RetrieveLaunch& r) {
     ta.err = st->d_err;
     const int lds_keys = st->max_user_facts < fsi::kTopkLdsKeys ? st->max_user_facts : fsi::kTopkLdsKeys;
     size_t lds = sizeof(uint64_t) * size_t(lds_keys);
-    fs_topk_kernel<<<dim3(r.batch), kTopkThreads, lds, r.stream>>>(ta);
+    launch_topk(st->max_user_facts, dim3(r.batch), lds, r.stream, ta);
     return hipGetLastError();
 }
 
@@ -714,7 +741,7 @@ hipError_t fsi_launch_ivf_probe(const IvfProbeLaunch& r) {
     t1.ids = ix->d_chosen;          // row stride nprobe: written as [B][nprobe]
     t1.err = st->d_err;
     const int lds1 = ix->nlist < fsi::kTopkLdsKeys ? ix->nlist : fsi::kTopkLdsKeys;
-    fs_topk_kernel<<<dim3(r.batch), kTopkThreads, sizeof(uint64_t) * size_t(lds1), r.stream>>>(t1);
+    launch_topk(ix->nlist, dim3(r.batch), sizeof(uint64_t) * size_t(lds1), r.stream, t1);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -751,6 +778,6 @@ hipError_t fsi_launch_ivf_probe(const IvfProbeLaunch& r) {
     t2.err = st->d_err;
     t2.counts = ix->d_counts;
     t2.idmap = ix->d_cand_ids;
-    fs_topk_kernel<<<dim3(r.batch), kTopkThreads, 0, r.stream>>>(t2);
+    launch_topk(int64_t(r.nprobe) * ix->max_list, dim3(r.batch), 0, r.stream, t2);
     return hipGetLastError();
 }
