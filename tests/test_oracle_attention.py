@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import oracle
-from _decoder import Decoder
+from _decoder import Decoder, rope_complex
 
 
 def _masked_softmax_attention(q, k, v, qpos, kpos, scale):
@@ -109,3 +109,40 @@ def test_theorem3_needs_the_intended_positions():
     _, mem_kv = dec.prefill(mem, np.arange(lm))
     h_bad = dec.prefill_over_injected(qry, start + lm + np.arange(tq), mem_kv, start - 1 + np.arange(lm))
     assert not np.allclose(h_bad, h_full[lm:], atol=1e-6)
+
+
+# ---- encode once, inject anywhere -------------------------------------------
+
+@pytest.mark.parametrize("shift", [1, 37, 4096])
+def test_encode_once_inject_anywhere(shift):
+    """The pages store each fact's pre-RoPE K once and place it at any
+    position later (gist.science summary, "Phase Hors-ligne" and "Rotation
+    Dynamique").  That rests on translation invariance: a RoPE decoder fed the
+    same tokens at positions shifted by s computes the same pre-RoPE K and V in
+    every layer, and its post-RoPE keys are the stored keys rotated to the new
+    positions, which is what the oracle's Chunked RoPE computes."""
+    rng = np.random.default_rng(shift)
+    dec = Decoder(rng, layers=3)
+    lm = 13
+    x = rng.standard_normal((lm, 24))
+    _, kv0 = dec.prefill(x, np.arange(lm))
+    pos = shift + np.arange(lm)
+    _, kvs = dec.prefill(x, pos)
+    for (k0, v0), (ks, vs) in zip(kv0, kvs):
+        assert np.allclose(ks, k0, rtol=0, atol=1e-10)
+        assert np.allclose(vs, v0, rtol=0, atol=1e-10)
+        post = rope_complex(ks, pos, dec.theta)
+        assert np.allclose(oracle.rope_rotate(k0, pos[:, None], dec.theta), post, rtol=0, atol=1e-10)
+
+
+def test_absolute_positions_break_encode_once():
+    # with an absolute position signal in the input, the stored K would depend
+    # on where the fact was encoded: the invariance above is not automatic
+    rng = np.random.default_rng(8)
+    dec = Decoder(rng, layers=2)
+    lm = 9
+    x = rng.standard_normal((lm, 24))
+    p_emb = lambda p: np.sin(np.outer(p, np.arange(1, 25)) * 0.01)
+    _, kv0 = dec.prefill(x + p_emb(np.arange(lm)), np.arange(lm))
+    _, kvs = dec.prefill(x + p_emb(50 + np.arange(lm)), 50 + np.arange(lm))
+    assert not np.allclose(kvs[1][0], kv0[1][0], atol=1e-6)
