@@ -25,8 +25,9 @@
 // the running maximum is reduced across lanes, once per 64 positions.  The
 // contraction index of P.V maps to positions in the order the score tiles
 // produce them (any order works if both operands agree).  K/V tiles of 64
-// positions are staged in LDS (K row-major, V transposed), with the next
-// tile's global loads in flight while the current one is consumed.  A block's
+// positions are staged in LDS, both row-major, with the next tile's global
+// loads in flight while the current one is consumed; the V^T operand comes
+// from gfx950's transposing LDS reads.  A block's
 // raw Q and first K/V tile are loaded before anything else (the block-table
 // entries of that tile are range-checked where they are read), so their
 // latency overlaps the request check and the (cos, sin) table.  Long contexts
@@ -48,7 +49,7 @@ constexpr int kKT = 64;               // cache positions per tile
 constexpr int kThreads = 256;         // 4 waves
 constexpr int kWaves = kThreads / 64;
 constexpr int kKPad = kD + 8;         // sK row: 272 bytes, 16-byte aligned, spreads banks
-constexpr int kVPad = kKT + 4;        // sVt row: 136 bytes, 8-byte aligned, spreads banks
+constexpr int kVPad = kD + 16;        // sV row: 288 bytes (32 mod 256): transposing reads hit distinct banks
 
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -88,6 +89,21 @@ __device__ __forceinline__ __bf16 as_bf16(uint16_t h) {
     return r;
 }
 
+typedef short s4 __attribute__((ext_vector_type(4)));
+
+// gfx950's transposing LDS read (ds_read_b64_tr_b16): each group of 16 lanes
+// supplies 16 chunks of 4 consecutive 16-bit values, R[c][0..3] at lane c's
+// address, and lane i receives R[i/4 + 4e][i % 4] for e = 0..3.  When lane c
+// points at V[p0 + c/4][d0 + 4*(c%4)], lane i receives V[p0 + e][d0 + i]:
+// four consecutive positions of column d0 + i.  Two reads, 16 positions
+// apart, give the 8 positions of one lane's A = V^T fragment.
+__device__ __forceinline__ b8 tr_v(const uint16_t* p, int second) {
+    const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(p));
+    const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(p + second));
+    struct { s4 a, b; } v{lo, hi};
+    return __builtin_bit_cast(b8, v);
+}
+
 // kQS sub-tiles of 16 query tokens per block; the 4 waves form kQS teams of
 // kWaves / kQS waves, team qs covering sub-tile qs.  Wave hb of a team holds
 // the query heads hb, hb + kWaves / kQS, ... (kHS head slots): a team covers
@@ -99,13 +115,13 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(A
     constexpr int kBQ = kQT * kQS;        // query tokens per block
     // the fp64 (cos, sin) table of the block's queries is only needed before
     // the first tile, so it shares storage with the K/V tiles
-    constexpr int kTileBytes = (kKT * kKPad + kD * kVPad) * 2;
+    constexpr int kTileBytes = (kKT * kKPad + kKT * kVPad) * 2;
     constexpr int kCSBytes = kBQ * (kD / 2) * 16;
     __shared__ __attribute__((aligned(16))) unsigned char s_raw[kTileBytes > kCSBytes ? kTileBytes : kCSBytes];
     __shared__ int s_bt[kBtCache];
     __shared__ int s_ok;
     auto sK = reinterpret_cast<uint16_t(*)[kKPad]>(s_raw);                       // [pos][d]
-    auto sVt = reinterpret_cast<uint16_t(*)[kVPad]>(s_raw + kKT * kKPad * 2);   // [d][pos]
+    auto sV = reinterpret_cast<uint16_t(*)[kVPad]>(s_raw + kKT * kKPad * 2);    // [pos][d]
     auto s_cs = reinterpret_cast<double2(*)[kD / 2]>(s_raw);                    // [query][i]
 
     // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin, so
@@ -297,15 +313,9 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(A
     };
     auto lstore = [&]() {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4*>(&sK[4 * lq + r][lvec * 8]) = kr[r];
-        // V transposed: for each d of the vector, the 4 positions side by side
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const uint32_t x0 = (&vr[0].x)[w], x1 = (&vr[1].x)[w], x2 = (&vr[2].x)[w], x3 = (&vr[3].x)[w];
-            const uint2 lo = make_uint2((x0 & 0xFFFFu) | (x1 << 16), (x2 & 0xFFFFu) | (x3 << 16));
-            const uint2 hi = make_uint2((x0 >> 16) | (x1 & 0xFFFF0000u), (x2 >> 16) | (x3 & 0xFFFF0000u));
-            *reinterpret_cast<uint2*>(&sVt[lvec * 8 + 2 * w][4 * lq]) = lo;
-            *reinterpret_cast<uint2*>(&sVt[lvec * 8 + 2 * w + 1][4 * lq]) = hi;
+        for (int r = 0; r < 4; ++r) {
+            *reinterpret_cast<uint4*>(&sK[4 * lq + r][lvec * 8]) = kr[r];
+            *reinterpret_cast<uint4*>(&sV[4 * lq + r][lvec * 8]) = vr[r];
         }
     };
 
@@ -340,12 +350,14 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(A
             float alpha[kHS];
 #pragma unroll
             for (int hs = 0; hs < kHS; ++hs) {
+                // raw scores; the scale (> 0) is applied to the maximum and
+                // inside each exponent, fl(max(s) c) being max(fl(s c))
                 float tmax = -1e30f;
 #pragma unroll
                 for (int sub = 0; sub < 4; ++sub) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        float x = st[hs][sub][i] * a.scale_log2;
+                        float x = st[hs][sub][i];
                         if (!full && tbase + 16 * sub + 4 * grp + i > qpos) x = -1e30f;
                         st[hs][sub][i] = x;
                         tmax = fmaxf(tmax, x);
@@ -353,7 +365,7 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(A
                 }
                 tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
                 tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-                const float m_new = fmaxf(m[hs], tmax);
+                const float m_new = fmaxf(m[hs], tmax * a.scale_log2);
                 alpha[hs] = __builtin_amdgcn_exp2f(m[hs] - m_new);
                 m[hs] = m_new;
                 // P^T fragments for the two 32-position halves: k = 8*grp + e maps to
@@ -363,7 +375,7 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(A
                 for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float pe = __builtin_amdgcn_exp2f(st[hs][2 * hh + e / 4][e % 4] - m_new);
+                        const float pe = __builtin_amdgcn_exp2f(fmaf(st[hs][2 * hh + e / 4][e % 4], a.scale_log2, -m_new));
                         pb[hs][hh][e] = static_cast<__bf16>(pe);
                         psum += pe;
                     }
@@ -376,11 +388,9 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(A
                 for (int hs = 0; hs < kHS; ++hs) o[hs][dc] *= alpha[hs];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    // A = V^T row dc*16 + col, in the position order of pb
-                    const uint16_t* vrow = &sVt[dc * 16 + col][32 * hh + 4 * grp];
-                    const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
-                    const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
-                    const b8 va = __builtin_bit_cast(b8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+                    // A = V^T row dc*16 + col, in the position order of pb,
+                    // by two transposing LDS reads of row-major V (see tr_v)
+                    const b8 va = tr_v(&sV[32 * hh + 4 * grp + (col >> 2)][dc * 16 + 4 * (col & 3)], 16 * kVPad);
 #pragma unroll
                     for (int hs = 0; hs < kHS; ++hs)
                         o[hs][dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hs][hh], o[hs][dc], 0, 0, 0);
