@@ -34,7 +34,9 @@
  *     ring, so they must not overlap one another or an fs_fetch_async.  On
  *     device stores fs_inject uses no scratch, so one stream may inject
  *     while another retrieves for a later request (the caller orders each
- *     inject after the retrieval that produced its ids, e.g. with an event).
+ *     inject after the retrieval that produced its ids, e.g. with an event),
+ *     and injects on different streams may overlap when they write disjoint
+ *     cache blocks.
  *   - Errors: a call returns a status.  Host-checkable errors return before
  *     anything is enqueued and nothing is written.  Conditions only the GPU
  *     can see set bits in the store's device error word (fs_poll_errors) and
