@@ -7,6 +7,8 @@ staging slots."""
 
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -102,3 +104,63 @@ def test_pinned_layer_pipeline_two_batches_match_device_store():
         assert torch.equal(_bits(vc[l]), _bits(rv[l])), f"layer {l} V"
     pin.close()
     dev.close()
+
+
+def test_two_lane_steps_match_one_stream():
+    """The bench's serving loop: step i retrieves then injects on stream
+    i % 2, each retrieval after the previous one (an event), the lanes writing
+    separate cache pools, so consecutive injects run side by side.  Every
+    step's ids and cache pool must equal the same step run alone on one
+    stream (which the parity tests compare with the oracle), and one step is
+    checked against the oracle directly."""
+    wl = synth.make_workload("llama", seed=1007)
+    s = wl.shape
+    layers = [0, 1, 2, 3]
+    B, k = s.batch, wl.k
+    mb = wl.block_table.shape[1]
+    say("two lanes: building store")
+    ds = build_store(wl, layers)
+    sets = [request_tensors(wl, queries=r["queries"], start_pos=r["start_pos"],
+                            block_table=r["block_table"])
+            for r in synth.request_sets(wl, 6, seed=wl.seed + 13)]
+    n = len(sets)
+    lanes = [torch.cuda.Stream(), torch.cuda.Stream()]
+    done = [torch.cuda.Event() for _ in range(n)]
+    ids = [torch.full((B, k), -7, dtype=torch.int32, device="cuda") for _ in range(n)]
+    ntok = [torch.zeros((B,), dtype=torch.int32, device="cuda") for _ in range(n)]
+    scores = [torch.zeros((B, k), dtype=torch.float64, device="cuda") for _ in range(n)]
+    pools = [synth.make_caches(wl, layers, "cuda") for _ in range(n)]
+    say("two lanes: 6 pipelined steps")
+    for i, r in enumerate(sets):
+        lane = lanes[i % 2]
+        if i > 0:
+            lane.wait_event(done[i - 1])
+        fs.fs_retrieve_topk(ds.store, B, r["user"], r["query"], k, ids[i], scores[i], ntok[i], stream=lane)
+        done[i].record(lane)
+        kc, vc = pools[i]
+        fs.fs_inject(ds.store, fs.FS_ALL_LAYERS, B, r["user"], ids[i], k, r["block_table"], mb,
+                     r["start_pos"], kc, vc, kc[0].shape[0], stream=lane)
+    torch.cuda.synchronize()
+    assert fs.fs_poll_errors(ds.store) == 0
+    say("two lanes: the same steps one by one on one stream")
+    for i, r in enumerate(sets):
+        rid = torch.empty((B, k), dtype=torch.int32, device="cuda")
+        rnt = torch.empty((B,), dtype=torch.int32, device="cuda")
+        fs.fs_retrieve_topk(ds.store, B, r["user"], r["query"], k, rid, None, rnt)
+        rk, rv = synth.make_caches(wl, layers, "cuda")
+        fs.fs_inject(ds.store, fs.FS_ALL_LAYERS, B, r["user"], rid, k, r["block_table"], mb,
+                     r["start_pos"], rk, rv, rk[0].shape[0])
+        torch.cuda.synchronize()
+        assert torch.equal(ids[i], rid) and torch.equal(ntok[i], rnt), f"step {i} retrieval"
+        kc, vc = pools[i]
+        for l in range(len(layers)):
+            assert torch.equal(_bits(kc[l]), _bits(rk[l])), f"step {i} layer {l} K"
+            assert torch.equal(_bits(vc[l]), _bits(rv[l])), f"step {i} layer {l} V"
+    assert fs.fs_poll_errors(ds.store) == 0
+    # step 0 against the oracle, through the same helpers as the parity tests
+    wl0 = dataclasses.replace(wl, queries=sets[0]["query"].cpu().numpy(),
+                              start_pos=sets[0]["start_pos"].cpu().numpy(),
+                              block_table=sets[0]["block_table"].cpu().numpy())
+    o = check_retrieval(wl0, ids[0].cpu().numpy(), scores[0].cpu().numpy(), ntok[0].cpu().numpy(), [0], k)
+    check_injection(wl0, ds, pools[0][0], pools[0][1], o, [0, 3])
+    ds.close()
