@@ -36,7 +36,9 @@
  *     while another retrieves for a later request (the caller orders each
  *     inject after the retrieval that produced its ids, e.g. with an event),
  *     and injects on different streams may overlap when they write disjoint
- *     cache blocks.
+ *     cache blocks.  Several stores may be created over the same arenas and
+ *     embeddings (each with its own scratch, e.g. one per stream) while none
+ *     of them ingests or evicts: each keeps its own copy of the metadata.
  *   - Errors: a call returns a status.  Host-checkable errors return before
  *     anything is enqueued and nothing is written.  Conditions only the GPU
  *     can see set bits in the store's device error word (fs_poll_errors) and
