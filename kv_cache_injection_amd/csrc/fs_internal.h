@@ -18,6 +18,11 @@ constexpr int kMaxK = FS_MAX_K;
 // Top-k keeps a request's keys in LDS when the user has at most this many
 // facts (48 KiB of uint64 keys); larger users are re-read from global memory.
 constexpr int kTopkLdsKeys = 6144;
+// users with more facts than kTopkChunkedN are selected in two phases: the
+// top k of every chunk of kTopkChunk scores (one block each), then the top k
+// of those candidates
+constexpr int kTopkChunkedN = 65536;
+constexpr int kTopkChunk = 16384;
 
 }  // namespace fsi
 
@@ -38,6 +43,10 @@ struct fs_store {
     double* d_inv_freq = nullptr;      // [head_dim/2] theta^(-2i/D)
     uint32_t* d_err = nullptr;         // device error word
     double* d_scores = nullptr;        // [max_batch][max_user_facts] score scratch
+    int32_t topk_chunks = 0;           // chunks of the largest user (0: one-phase selection)
+    int32_t* d_tk_ids = nullptr;       // [max_batch][topk_chunks * max_k] per-chunk winners
+    double* d_tk_scores = nullptr;     // [max_batch][topk_chunks * max_k]
+    int32_t* d_tk_counts = nullptr;    // [max_batch]
     const void** d_src_k = nullptr;    // [L] device-visible arena pointers
     const void** d_src_v = nullptr;
     // inject plan scratch (written by the plan kernel, read by the inject kernel)

@@ -46,7 +46,8 @@ void free_store(fs_store* s) {
     if (!s) return;
     void* bufs[] = {s->d_fact_begin, s->d_fact_len, s->d_user_begin, s->d_user_count,
                     s->d_ingest_items, s->d_inv_freq, s->d_err,
-                    s->d_scores, (void*)s->d_src_k, (void*)s->d_src_v, s->d_tok_src,
+                    s->d_scores, s->d_tk_ids, s->d_tk_scores, s->d_tk_counts,
+                    (void*)s->d_src_k, (void*)s->d_src_v, s->d_tok_src,
                     s->d_tok_dst, s->d_req_len, s->d_stage_k,
                     s->d_stage_v, s->d_stage_ids, s->d_stage_meta};
     for (void* p : bufs)
@@ -198,6 +199,9 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
         inv[i] = std::pow(d.rope_theta, -2.0 * double(i) / double(d.head_dim));
 
     const int H = d.num_kv_heads, D = d.head_dim;
+    st->topk_chunks = max_user > fsi::kTopkChunkedN
+                          ? static_cast<int32_t>((max_user + fsi::kTopkChunk - 1) / fsi::kTopkChunk) : 0;
+    const size_t tk_elems = size_t(d.max_batch) * size_t(st->topk_chunks > 0 ? st->topk_chunks : 1) * size_t(d.max_k);
     struct { void** p; size_t bytes; const char* what; } allocs[] = {
         {(void**)&st->d_fact_begin, sizeof(int64_t) * (d.num_facts + 1), "fact offsets"},
         {(void**)&st->d_fact_len, sizeof(int32_t) * d.num_facts, "fact lengths"},
@@ -207,6 +211,9 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
         {(void**)&st->d_inv_freq, sizeof(double) * (D / 2), "frequency table"},
         {(void**)&st->d_err, sizeof(uint32_t), "error word"},
         {(void**)&st->d_scores, sizeof(double) * size_t(d.max_batch) * size_t(max_user > 0 ? max_user : 1), "score scratch"},
+        {(void**)&st->d_tk_ids, sizeof(int32_t) * tk_elems, "top-k chunk scratch"},
+        {(void**)&st->d_tk_scores, sizeof(double) * tk_elems, "top-k chunk scratch"},
+        {(void**)&st->d_tk_counts, sizeof(int32_t) * size_t(d.max_batch), "top-k chunk scratch"},
         {(void**)&st->d_src_k, sizeof(void*) * d.num_layers, "arena table"},
         {(void**)&st->d_src_v, sizeof(void*) * d.num_layers, "arena table"},
         {(void**)&st->d_tok_src, sizeof(int64_t) * size_t(d.max_batch) * size_t(st->seg_tokens), "segment plan"},

@@ -260,6 +260,14 @@ struct TopkArgs {
     // lower fact id
     const int32_t* counts;
     const int32_t* idmap;
+    // chunk mode (first phase of a large user's selection): block
+    // (request b, chunk c) selects the top k of the user's scores
+    // [c * chunk, (c + 1) * chunk) and writes them, by global fact id, to
+    // ids / out_scores at row b * nchunks + c; the request's last chunk
+    // writes the number of candidates to out_counts[b]
+    int32_t chunk;
+    int32_t nchunks;
+    int32_t* out_counts;
 };
 
 // kT threads: 256 for stores of up to kTopkSmallN scores per request (a
@@ -278,7 +286,9 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
     __shared__ int s_rem, s_done, s_ncand, s_tokens;
     extern __shared__ uint64_t keys_lds[];
 
-    const int b = blockIdx.x;
+    const bool chunked = a.chunk > 0;
+    const int b = chunked ? blockIdx.x / a.nchunks : blockIdx.x;
+    const int cidx = chunked ? blockIdx.x - b * a.nchunks : 0;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -286,16 +296,26 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
     const bool mapped = a.counts != nullptr;
     const int u = mapped ? 0 : a.user[b];
     const bool bad_user = !mapped && (u < 0 || u >= a.num_users);
-    const int64_t base = (mapped || bad_user) ? 0 : a.user_begin[u];
-    const int32_t n = mapped ? a.counts[b]
-                             : (bad_user ? 0 : (a.user_count ? a.user_count[u]
-                                                            : static_cast<int32_t>(a.user_begin[u + 1] - base)));
+    const int64_t ubase = (mapped || bad_user) ? 0 : a.user_begin[u];
+    const int32_t n_all = mapped ? a.counts[b]
+                                 : (bad_user ? 0 : (a.user_count ? a.user_count[u]
+                                                                : static_cast<int32_t>(a.user_begin[u + 1] - ubase)));
+    const int32_t c0 = cidx * a.chunk;              // first score of this block's chunk
+    const int32_t n = chunked ? max(0, min(a.chunk, n_all - c0)) : n_all;
+    const int64_t base = ubase + c0;
     const int kk = n < k ? n : k;
+    if (chunked && tid == 0) {
+        // the request's last non-empty chunk (or chunk 0 of an empty user)
+        // reports how many candidates the chunks hold
+        const int last = n_all > 0 ? (n_all - 1) / a.chunk : 0;
+        if (cidx == last) a.out_counts[b] = n_all > 0 ? last * k + min(k, n_all - last * a.chunk) : 0;
+    }
     const int32_t* imap = mapped ? a.idmap + int64_t(b) * a.stride : nullptr;
     // the id a candidate is ranked and reported by
     auto cand_id = [&](int i) -> int32_t { return mapped ? imap[i] : i; };
 
-    if (bad_user && tid == 0) atomicOr(a.err, FS_ERR_USER);
+    if (bad_user && tid == 0 && cidx == 0) atomicOr(a.err, FS_ERR_USER);
+    if (chunked && kk == 0) return;
     if (kk == 0) {
         for (int j = tid; j < k; j += blockDim.x) {
             a.ids[int64_t(b) * k + j] = -1;
@@ -305,7 +325,7 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
         return;
     }
 
-    const double* sc = a.scores + int64_t(b) * a.stride;
+    const double* sc = a.scores + int64_t(b) * a.stride + c0;
 
     bool tokens_known = false;           // the fast path sums the lengths itself
 
@@ -633,6 +653,14 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
 
 outputs:
     // ---- outputs -----------------------------------------------------------
+    if (chunked) {
+        const int64_t row = (int64_t(b) * a.nchunks + cidx) * k;
+        for (int j = tid; j < kk; j += blockDim.x) {
+            a.ids[row + j] = static_cast<int32_t>(base + cand_idx[j]);
+            a.out_scores[row + j] = key_value(cand_key[j]);
+        }
+        return;
+    }
     int my_tokens = 0;
     for (int j = tid; j < k; j += blockDim.x) {
         int32_t id = -1;
@@ -702,6 +730,30 @@ hipError_t fsi_launch_retrieve(const RetrieveLaunch& r) {
     ta.out_scores = r.scores;
     ta.num_tokens = r.num_tokens;
     ta.err = st->d_err;
+    if (st->topk_chunks > 0 && r.k > 0) {
+        // large users: the top k of every chunk, one block each, then the top
+        // k of those candidates by (score desc, fact id asc).  Every fact of
+        // the true top k is among its own chunk's top k, so this is exact.
+        TopkArgs t1 = ta;
+        t1.fact_len = nullptr;
+        t1.num_tokens = nullptr;
+        t1.ids = st->d_tk_ids;
+        t1.out_scores = st->d_tk_scores;
+        t1.chunk = fsi::kTopkChunk;
+        t1.nchunks = st->topk_chunks;
+        t1.out_counts = st->d_tk_counts;
+        launch_topk(fsi::kTopkChunk, dim3(static_cast<unsigned>(r.batch) * st->topk_chunks),
+                    sizeof(uint64_t) * size_t(fsi::kTopkLdsKeys), r.stream, t1);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        TopkArgs t2 = ta;
+        t2.scores = st->d_tk_scores;
+        t2.stride = st->topk_chunks * r.k;
+        t2.counts = st->d_tk_counts;
+        t2.idmap = st->d_tk_ids;
+        launch_topk(int64_t(t2.stride), dim3(r.batch), 0, r.stream, t2);
+        return hipGetLastError();
+    }
     const int lds_keys = st->max_user_facts < fsi::kTopkLdsKeys ? st->max_user_facts : fsi::kTopkLdsKeys;
     size_t lds = sizeof(uint64_t) * size_t(lds_keys);
     launch_topk(st->max_user_facts, dim3(r.batch), lds, r.stream, ta);

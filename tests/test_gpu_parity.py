@@ -23,7 +23,7 @@ import pytest
 import torch
 
 import oracle
-from _parity import (SCORE_ABS_TOL, bf16_ulp_distance, check_injection, check_retrieval,
+from _parity import (CERT_GAP, SCORE_ABS_TOL, bf16_ulp_distance, check_injection, check_retrieval,
                      check_sentinel, gpu_retrieve, say, table_mask, written_mask)
 from kv_cache_injection_amd import fs, synth
 from kv_cache_injection_amd.workload import build_store, make_desc, request_tensors
@@ -142,6 +142,55 @@ def test_retrieval_ties_padding_and_empty_user():
     ids = torch.empty((4, 3), dtype=torch.int32, device="cuda")
     fs.fs_retrieve_topk(st, 4, user_t, q_t, 3, ids, None, None)
     assert list(_host(ids)[0][:2]) == [12, 17]
+    st.close()
+
+
+@pytest.mark.parametrize("k", [1, 50, 1024])
+def test_large_user_two_phase_selection(k):
+    """A user above 65,536 facts is selected in two phases (the top k of
+    every 16,384-score chunk, then the top k of those).  Exact duplicates of
+    the best rows sit in different chunks, at chunk edges and in the short last
+    chunk: the lower fact id must win every tie, across chunks too.  A small
+    user and an empty user share the store."""
+    rng = np.random.default_rng(31)
+    E, n_big = 64, 200_003
+    ufb = np.array([0, 1000, 1000, 1000 + n_big], np.int64)   # user 1 has no facts
+    F = int(ufb[-1])
+    emb = rng.standard_normal((F, E)).astype(np.float32)
+    emb /= np.linalg.norm(emb, axis=1, keepdims=True)
+    q_big = emb[1000 + 5000].copy()
+    for off in (16383, 16384, 50_000, 131_071, 196_607, n_big - 1):   # copies of the user's row 5000
+        emb[1000 + off] = q_big
+    fl = rng.integers(1, 4, F).astype(np.int32)
+    st, _, _ = _small_store(emb, ufb, fl, H=1, D=64, max_k=1024, max_batch=4)
+    users = np.array([2, 0, 2, 1], np.int32)
+    q = np.stack([q_big, emb[17], rng.standard_normal(E).astype(np.float32), q_big]).astype(np.float32)
+    q[2] /= np.linalg.norm(q[2])
+    ids = torch.full((4, k), -7, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((4, k), dtype=torch.float64, device="cuda")
+    nt = torch.full((4,), -7, dtype=torch.int32, device="cuda")
+    say(f"two-phase selection: {n_big} facts, k={k}")
+    fs.fs_retrieve_topk(st, 4, torch.from_numpy(users).cuda(), torch.from_numpy(q).cuda(), k, ids, sc, nt)
+    assert fs.fs_poll_errors(st) == 0
+    g, gs, gn = _host(ids), _host(sc), _host(nt)
+    for b in range(4):
+        u = users[b]
+        o_ids, o_sc = oracle.retrieve(emb, ufb, u, q[b], k)
+        kk = min(k, int(ufb[u + 1] - ufb[u]))
+        s_all = oracle.score(emb[ufb[u]:ufb[u + 1]], q[b]) if kk else np.zeros(0)
+        if kk and oracle.decisive_gap(s_all, k) <= CERT_GAP:
+            # besides the exact copies, a decisive gap this small would leave
+            # the order to rounding: then only validity is checked
+            assert set(g[b][:kk].tolist()) <= set(range(int(ufb[u]), int(ufb[u + 1])))
+            say(f"request {b}: near-tie, validity checked")
+        else:
+            assert np.array_equal(g[b].astype(np.int64), o_ids), (b, g[b][:8], o_ids[:8])
+            assert gn[b] == oracle.compose(o_ids, fl)[1]
+        assert np.all(np.abs(gs[b][:kk] - o_sc[:kk]) <= SCORE_ABS_TOL)
+        assert np.all(g[b][kk:] == -1) and np.all(np.isneginf(gs[b][kk:]))
+    # the copies of the query row tie exactly and come out in id order
+    top = g[0][:7].tolist()
+    assert top == sorted(top) and top[0] == 1000 + 5000
     st.close()
 
 
