@@ -336,9 +336,11 @@ FS_API fs_status fs_attend_workspace_size(const fs_store* store, int32_t batch,
  * injection see live facts only.  Arena rows are handed out in order from
  * rows_used and are not reused after an eviction (rebuild the store to
  * compact).  An inverted-file index is not updated: rebuild it after ingest
- * or eviction.  These calls write the caller's embedding matrix and arenas,
- * synchronise `stream` before they return, and must not overlap any other
- * call on the store.
+ * or eviction.  These calls write the caller's embedding matrix and arenas
+ * and must not overlap any other call on the store.  fs_ingest_init and
+ * fs_evict_fact synchronise `stream` before they return; fs_ingest_facts is
+ * asynchronous on `stream` like the compute calls, so the caller orders any
+ * later call on the store after it (the same stream, or an event).
  */
 
 /*
@@ -359,9 +361,11 @@ FS_API fs_status fs_ingest_init(fs_store* store, const int32_t* live_counts, int
  * keep_begin[i] + keep_len[i] - 1 (host arrays; 1 <= keep_len <= the longest
  * fact at creation), the rest of its window is discarded.  emb: device fp32
  * [n][embed_dim], fact i's embedding.  fact_ids (host [n], out): the ids
- * given.  All-or-nothing: a host-checked error (no free slot, arenas full, a
- * length out of range) writes nothing.  Errors: FS_E_ARG, FS_E_RANGE,
- * FS_E_HIP.
+ * given, assigned at once (fs_store_live counts them on return).  The window
+ * arrays and emb must stay valid until `stream` has run the call.
+ * All-or-nothing: a host-checked error (no free slot, arenas full, a length
+ * out of range) writes nothing.  Errors: FS_E_ARG, FS_E_RANGE, FS_E_NOMEM
+ * (host staging of the first call), FS_E_HIP.
  */
 FS_API fs_status fs_ingest_facts(fs_store* store, int32_t n, const int32_t* user,
                                  const void* const* k_window, const void* const* v_window,

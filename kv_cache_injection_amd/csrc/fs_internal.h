@@ -68,6 +68,9 @@ struct fs_store {
     std::vector<int32_t> h_fact_len;       // [F]
     int64_t next_row = 0;                  // first arena row never handed out
     void* d_ingest_items = nullptr;        // [kIngestMax] per-call fact descriptors
+    void* h_ingest_items = nullptr;        // pinned host staging of the descriptors (first ingest)
+    int32_t* h_ingest_counts = nullptr;    // pinned host staging of the live counts [U]
+    hipEvent_t ingest_copied = nullptr;    // recorded after the last ingest's host-to-device copies
 
     // caller-owned, referenced
     const float* emb = nullptr;

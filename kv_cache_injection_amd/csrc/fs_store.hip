@@ -52,6 +52,9 @@ void free_store(fs_store* s) {
                     s->d_stage_v, s->d_stage_ids, s->d_stage_meta};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
+    if (s->ingest_copied) (void)hipEventDestroy(s->ingest_copied);
+    if (s->h_ingest_items) (void)hipHostFree(s->h_ingest_items);
+    if (s->h_ingest_counts) (void)hipHostFree(s->h_ingest_counts);
     delete s;
 }
 
@@ -495,15 +498,35 @@ fs_status fs_ingest_facts(fs_store* store, int32_t n, const int32_t* user, const
         max_len = std::max(max_len, keep_len[i]);
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(store->d_ingest_items, items.data(), sizeof(IngestItem) * n,
-                                  hipMemcpyHostToDevice, s);
+    // descriptors and counts go through pinned host buffers, so the copies
+    // are asynchronous; a buffer is refilled only after the previous call's
+    // copies out of it have completed
+    hipError_t e = hipSuccess;
+    if (!store->h_ingest_items) {
+        e = hipHostMalloc(&store->h_ingest_items, sizeof(IngestItem) * kIngestMax, hipHostMallocDefault);
+        if (e == hipSuccess)
+            e = hipHostMalloc(reinterpret_cast<void**>(&store->h_ingest_counts), sizeof(int32_t) * d.num_users,
+                              hipHostMallocDefault);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&store->ingest_copied, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(FS_E_NOMEM, "ingest staging: %s", hipGetErrorString(e));
+        }
+    } else {
+        e = hipEventSynchronize(store->ingest_copied);
+        if (e != hipSuccess) return hip_fail(e, "ingest staging wait");
+    }
+    std::memcpy(store->h_ingest_items, items.data(), sizeof(IngestItem) * n);
+    std::memcpy(store->h_ingest_counts, count.data(), sizeof(int32_t) * d.num_users);
+    e = hipMemcpyAsync(store->d_ingest_items, store->h_ingest_items, sizeof(IngestItem) * n,
+                       hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(ingest descriptors)");
     IngestLaunch a{store, n, max_len, k_window, v_window, emb, s};
     e = fsi_launch_ingest(a);
     if (e != hipSuccess) return hip_fail(e, "ingest launch");
-    e = hipMemcpyAsync(store->d_user_count, count.data(), sizeof(int32_t) * d.num_users,
+    e = hipMemcpyAsync(store->d_user_count, store->h_ingest_counts, sizeof(int32_t) * d.num_users,
                        hipMemcpyHostToDevice, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);   // host descriptors and counts are consumed
+    if (e == hipSuccess) e = hipEventRecord(store->ingest_copied, s);
     if (e != hipSuccess) return hip_fail(e, "ingest");
     for (int i = 0; i < n; ++i) {
         store->h_fact_begin[items[i].slot] = items[i].dst_row;

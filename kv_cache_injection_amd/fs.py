@@ -376,12 +376,15 @@ def fs_ingest_facts(store, user, k_window: Sequence[torch.Tensor], v_window: Seq
     if len(k_window) != L or len(v_window) != L:
         raise ValueError("one window array per layer")
     H, D, E = store.desc.num_kv_heads, store.desc.head_dim, store.desc.embed_dim
-    for t in list(k_window) + list(v_window):
-        if t.dim() != 3 or t.shape[1:] != (H, D):
+    need = int((kb + kl).max()) if n else 0          # rows every window array must hold
+    bf, i16 = torch.bfloat16, torch.int16
+    for t in (*k_window, *v_window):
+        sh = t.shape
+        if len(sh) != 3 or sh[1] != H or sh[2] != D:
             raise ValueError(f"window arrays must be [rows, {H}, {D}]")
-        if t.dtype not in (torch.bfloat16, torch.int16) or not t.is_contiguous() or t.device.type != "cuda":
+        if (t.dtype is not bf and t.dtype is not i16) or not t.is_cuda or not t.is_contiguous():
             raise TypeError("window arrays must be contiguous bf16 device tensors")
-        if np.any(kb + kl > t.shape[0]):
+        if sh[0] < need:
             raise ValueError("a kept row range runs past the window array")
     karr = (ctypes.c_void_p * L)(*[t.data_ptr() for t in k_window])
     varr = (ctypes.c_void_p * L)(*[t.data_ptr() for t in v_window])
