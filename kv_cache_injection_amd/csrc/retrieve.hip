@@ -16,7 +16,12 @@
 //                block, which reads its rows once for all their queries: a
 //                batch of one user's requests scans the table once, not once
 //                per request.
-// top-k kernel   one 1024-thread block per request.  First try: the min and
+// top-k kernel   one block per request: 256 threads when no request of the
+//                launch has more than 4,096 scores (a small block starts
+//                sooner beside a running inject), 1,024 above.  Users above
+//                65,536 facts are selected in two phases: the top k of every
+//                16,384-score chunk (one block each), then the top k of those
+//                candidates, which is exact.  First try: the min and
 //                max of the request's scores define 2048 equal-width value
 //                bins (the bin is a monotone function of the score, so equal
 //                scores share a bin); an LDS histogram and a block suffix scan
