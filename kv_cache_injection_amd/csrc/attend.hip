@@ -14,8 +14,10 @@
 // w_i = theta^(-2i/D)) in fp64 and rounds once to bf16, as the injection does
 // for keys, so Q and K carry the same rounding.
 //
-// One block = 16 query tokens x one KV head (all the query heads of its GQA
-// group, one per wave, two per wave for groups of 5..8).  Scores and P.V run
+// One block = one KV head and 16 or 32 query tokens (all the query heads of
+// its GQA group): for groups up to 4 and more than 16 tokens, two 16-token
+// sub-tiles with two heads per wave; otherwise 16 tokens with one head per
+// wave, two per wave for groups of 5..8.  Scores and P.V run
 // on the matrix cores (gfx950 16x16x32 bf16 MFMA, fp32 accumulation);
 // softmax is online in fp32 (exp2); the weights are rounded to bf16 for P.V
 // and summed unrounded for the normaliser.  Both products are computed transposed,
@@ -27,8 +29,8 @@
 // produce them (any order works if both operands agree).  K/V tiles of 64
 // positions are staged in LDS, both row-major, with the next tile's global
 // loads in flight while the current one is consumed; the V^T operand comes
-// from gfx950's transposing LDS reads.  A block's
-// raw Q and first K/V tile are loaded before anything else (the block-table
+// from gfx950's transposing LDS reads.  A block's raw Q and first K/V tile
+// are loaded before anything else (the block-table
 // entries of that tile are range-checked where they are read), so their
 // latency overlaps the request check and the (cos, sin) table.  Long contexts
 // are split over several blocks whose partial results a second kernel merges.
