@@ -9,7 +9,7 @@
 // raw V into free arena rows, then records the fact's rows and length in its
 // slot and copies its embedding row.  The context rows are discarded.
 //
-// Grid (row group, fact, layer); 64-thread blocks copy 16-byte vectors, a
+// Grid (row group, fact, layer); 256-thread blocks copy 16-byte vectors, a
 // whole K and V row per token; block (0, f, 0) writes fact f's metadata.
 
 #include <hip/hip_runtime.h>
