@@ -194,13 +194,25 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(A
     if (t_begin < t_end) {
         // entries read from the table and range-checked here, since the
         // request's check has not run yet (a rejected request discards them)
+        // the four entries are read first (clamped in range, so the reads
+        // need no branch), then the eight K/V loads: no load waits behind
+        // another row's K/V
+        int blk[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t ei = int64_t(c0 + t_begin * kKT + 4 * lq + r) >> a.log2_block;
+            blk[r] = __builtin_nontemporal_load(bt + (ei < a.max_blocks ? ei : a.max_blocks - 1));
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int p = c0 + t_begin * kKT + 4 * lq + r;
-            const int64_t ei = p >> a.log2_block;
-            const int blk = p <= p_end && ei < a.max_blocks ? bt[ei] : -1;
-            if (blk >= 0 && blk < a.num_blocks) {
-                gload_row(r, p, blk);
+            if (p > p_end || (int64_t(p) >> a.log2_block) >= a.max_blocks) blk[r] = -1;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int p = c0 + t_begin * kKT + 4 * lq + r;
+            if (blk[r] >= 0 && blk[r] < a.num_blocks) {
+                gload_row(r, p, blk[r]);
             } else {
                 kr[r] = make_uint4(0, 0, 0, 0);
                 vr[r] = make_uint4(0, 0, 0, 0);
@@ -257,12 +269,15 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(A
     if (bt_cached)
         for (int64_t j = e_first + threadIdx.x; j <= e_last; j += kThreads) s_bt[j - e_first] = bt[j];
 
-    // ---- fp64 (cos, sin) of (position of query jb + qq) * w_i, shared by the heads
+    // ---- fp64 (cos, sin) of (position of query jb + qq) * w_i, shared by the
+    // heads; a thread's frequency index is the same in every iteration
+    static_assert(kThreads % (kD / 2) == 0, "one frequency per thread");
+    const double w_i = a.inv_freq[threadIdx.x % (kD / 2)];
     for (int e = threadIdx.x; e < kBQ * (kD / 2); e += kThreads) {
         const int qq = e / (kD / 2);
         const int i = e - qq * (kD / 2);
         double sv, cv;
-        sincos(static_cast<double>(qp0 + jb + qq) * a.inv_freq[i], &sv, &cv);
+        sincos(static_cast<double>(qp0 + jb + qq) * w_i, &sv, &cv);
         s_cs[qq][i] = make_double2(cv, sv);
     }
     __syncthreads();
@@ -300,13 +315,29 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(A
         for (int dc = 0; dc < 8; ++dc) o[hs][dc] = f4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
+    // the block ids of the four rows first (LDS or global, one uniform
+    // branch), then the eight K/V loads: a load's wait for its block id must
+    // not also wait for the rows issued before it
     auto gload = [&](int t) {
+        int blk[4];
+        if (bt_cached) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int p = c0 + t * kKT + 4 * lq + r;
+                blk[r] = p <= p_end ? s_bt[(int64_t(p) >> a.log2_block) - e_first] : -1;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int p = c0 + t * kKT + 4 * lq + r;
+                blk[r] = p <= p_end ? bt[int64_t(p) >> a.log2_block] : -1;
+            }
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int p = c0 + t * kKT + 4 * lq + r;
-            if (p <= p_end) {
-                const int64_t ei = p >> a.log2_block;
-                gload_row(r, p, bt_cached ? s_bt[ei - e_first] : bt[ei]);
+            if (blk[r] >= 0) {
+                gload_row(r, p, blk[r]);
             } else {
                 kr[r] = make_uint4(0, 0, 0, 0);
                 vr[r] = make_uint4(0, 0, 0, 0);
