@@ -74,6 +74,7 @@ struct PlanArgs {
     const int64_t* user_begin;
     const int32_t* user_count;      // live facts per user (from user_begin[u])
     int32_t num_users;
+    int64_t num_facts;
     int32_t layer_begin, layer_end, heads;
     const int32_t* stage_ids;       // non-null for pinned stores
     const int32_t* stage_meta;
@@ -129,11 +130,15 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 // the segment length and the number of real (non-pad) ids.
 __device__ uint32_t plan_request(const int32_t* user, const int32_t* ids, int k,
                                  const int64_t* user_begin, const int32_t* user_count, int num_users,
-                                 const int32_t* fact_len, const int64_t* fact_begin, int b,
+                                 int64_t num_facts, const int32_t* fact_len, const int64_t* fact_begin, int b,
                                  int32_t* off, int64_t* row0, int* L_out, int* nf_out) {
     const int lane = threadIdx.x & 63;
     uint32_t bits = 0;
+    // the user and the first 64 ids are read together; the user's range and
+    // each id's length and first row then together (an id outside the fact
+    // table reads fact 0 and is rejected below): two dependent rounds
     const int u = user[b];
+    const int id0 = lane < k ? ids[int64_t(b) * k + lane] : 0;
     const bool bad_user = (u < 0 || u >= num_users);
     if (bad_user) bits |= FS_ERR_USER;
     const int64_t ub0 = bad_user ? 0 : user_begin[u];
@@ -144,9 +149,12 @@ __device__ uint32_t plan_request(const int32_t* user, const int32_t* ids, int k,
     int carry = 0, first_pad = k, last_real = -1;
     for (int c0 = 0; c0 < k; c0 += 64) {
         const int j = c0 + lane;
+        const int id = c0 == 0 ? id0 : (j < k ? ids[int64_t(b) * k + j] : 0);
+        const int64_t idc = id >= 0 && id < num_facts ? id : 0;
+        const int len_any = j < k ? fact_len[idc] : 0;
+        const int64_t r0_any = j < k ? fact_begin[idc] : 0;
         int len = 0;
         int64_t r0 = 0;
-        const int id = j < k ? ids[int64_t(b) * k + j] : 0;
         first_pad = wave_min(min(first_pad, (j < k && id < 0) ? j : k));
         if (j < k) {
             if (id < 0 || j > first_pad) {
@@ -157,8 +165,8 @@ __device__ uint32_t plan_request(const int32_t* user, const int32_t* ids, int k,
                 } else if (id < ub0 || id >= ub1) {
                     bits |= FS_ERR_FACT_ID;
                 } else {
-                    len = fact_len[id];
-                    r0 = fact_begin[id];
+                    len = len_any;
+                    r0 = r0_any;
                 }
             }
         }
@@ -210,6 +218,7 @@ struct FetchArgs {
     const int64_t* user_begin;
     const int32_t* user_count;      // live facts per user (from user_begin[u])
     int32_t num_users;
+    int64_t num_facts;
     int32_t heads;
     int32_t layer_begin, layer_end, layers_per_block;
     const void* const* src_k;       // device table of device-visible host addresses
@@ -283,7 +292,7 @@ __global__ __launch_bounds__(kPlanThreads) void fs_plan_kernel(PlanArgs a) {
     const int b = blockIdx.x;
     if (threadIdx.x < 64) {
         int L = 0, nf = 0;
-        uint32_t bits = plan_request(a.user, a.ids, a.k, a.user_begin, a.user_count, a.num_users, a.fact_len,
+        uint32_t bits = plan_request(a.user, a.ids, a.k, a.user_begin, a.user_count, a.num_users, a.num_facts, a.fact_len,
                                      a.fact_begin, b, off, row0, &L, &nf);
         bits |= check_request(a, b, L);
         bits = wave_or(bits);
@@ -358,7 +367,7 @@ __global__ __launch_bounds__(kInjectThreads, kInjectOcc) void fs_inject_kernel(I
         }
     } else if (wave == 0) {
         int Lr = 0, nf = 0;
-        const uint32_t bits = plan_request(pa.user, pa.ids, pa.k, pa.user_begin, pa.user_count, pa.num_users,
+        const uint32_t bits = plan_request(pa.user, pa.ids, pa.k, pa.user_begin, pa.user_count, pa.num_users, pa.num_facts,
                                            pa.fact_len, pa.fact_begin, b, off, row0, &Lr, &nf);
         const uint32_t any = wave_or(bits);
         if (lane == 0) {
@@ -367,13 +376,18 @@ __global__ __launch_bounds__(kInjectThreads, kInjectOcc) void fs_inject_kernel(I
             s_bits = any;
         }
     }
-    const int cs_begin = kPlanned ? 0 : 64;  // threads filling the table
+    constexpr int kCsBegin = kPlanned ? 0 : 64;             // threads filling the table
+    constexpr int kCsStride = kInjectThreads - kCsBegin;
+    // when the stride is a multiple of D/2 a thread meets one frequency only:
+    // it is loaded once, not before every sincos
+    constexpr bool kOneFreq = kCsStride % (D / 2) == 0;
     if (kPlanned || wave > 0) {
-        for (int e = threadIdx.x - cs_begin; e < kCS; e += kInjectThreads - cs_begin) {
+        const double w_own = kOneFreq ? a.inv_freq[(threadIdx.x - kCsBegin) % (D / 2)] : 0.0;
+        for (int e = threadIdx.x - kCsBegin; e < kCS; e += kCsStride) {
             const int tt = e / (D / 2);
             const int i = e - tt * (D / 2);
             double sv, cv;
-            sincos(static_cast<double>(p0 + tt) * a.inv_freq[i], &sv, &cv);
+            sincos(static_cast<double>(p0 + tt) * (kOneFreq ? w_own : a.inv_freq[i]), &sv, &cv);
             s_cs[e] = make_double2(cv, sv);
         }
     }
@@ -457,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void fs_fetch_kernel(FetchArgs a) {
     const int b = blockIdx.y;
     const int lane = threadIdx.x;
     int L = 0, nf = 0;
-    uint32_t bits = plan_request(a.user, a.ids, a.k, a.user_begin, a.user_count, a.num_users, a.fact_len,
+    uint32_t bits = plan_request(a.user, a.ids, a.k, a.user_begin, a.user_count, a.num_users, a.num_facts, a.fact_len,
                                  a.fact_begin, b, off, row0, &L, &nf);
     bits = wave_or(bits);
     const int l0 = a.layer_begin + blockIdx.z * a.layers_per_block;
@@ -554,6 +568,7 @@ hipError_t launch_inject(const InjectLaunch& r) {
     pa.user_begin = st->d_user_begin;
     pa.user_count = st->d_user_count;
     pa.num_users = d.num_users;
+    pa.num_facts = d.num_facts;
     pa.layer_begin = r.layer_begin;
     pa.layer_end = r.layer_end;
     pa.heads = d.num_kv_heads;
@@ -624,6 +639,7 @@ hipError_t launch_fetch(const FetchLaunch& r) {
     a.user_begin = st->d_user_begin;
     a.user_count = st->d_user_count;
     a.num_users = d.num_users;
+    a.num_facts = d.num_facts;
     a.heads = d.num_kv_heads;
     a.layer_begin = r.layer_begin;
     a.layer_end = r.layer_end;
