@@ -260,9 +260,15 @@ __device__ uint32_t check_request(const PlanArgs& a, int b, int L) {
         if (last >= a.max_blocks) {
             bits |= FS_ERR_BLOCK_SHORT;
         } else {
-            for (int j = first + lane; j <= last; j += 64) {
-                const int e = bt[j];
-                if (e < 0 || e >= a.num_blocks) bits |= FS_ERR_BLOCK_ID;
+            // four entries per lane in flight at a time (indices clamped to
+            // the range, so the loads need no branch and no wait between them)
+            for (int j0 = first + lane; j0 <= last; j0 += 256) {
+                int e[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) e[q] = bt[min(j0 + 64 * q, last)];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (j0 + 64 * q <= last && (e[q] < 0 || e[q] >= a.num_blocks)) bits |= FS_ERR_BLOCK_ID;
             }
         }
     }
@@ -398,11 +404,6 @@ __global__ __launch_bounds__(kInjectThreads, kInjectOcc) void fs_inject_kernel(I
         if (t < L) {
             const int j = find_fact(off, s_nf, t);
             src_row = row0[j] + (t - off[j]);
-            const int64_t p = p0 + team;
-            const int64_t bi = p >> pa.log2_block;
-            int blk = 0;
-            if (p >= 0 && bi < pa.max_blocks) blk = pa.block_table[int64_t(b) * pa.max_blocks + bi];
-            dst_row = (int64_t(blk) << pa.log2_block) | (p & ((1 << pa.log2_block) - 1));
         }
     }
     const bool act = t < L;
@@ -429,6 +430,16 @@ __global__ __launch_bounds__(kInjectThreads, kInjectOcc) void fs_inject_kernel(I
         }
     };
     load_head(wave);                         // in flight across the barrier
+    // the token's cache slot: its block-table entry is read after the K/V
+    // loads are out, by every thread (index clamped in range, so no branch
+    // forces a wait on it here; a bad entry or a short table rejects the
+    // request below, before any store)
+    int blk_raw = 0;
+    const int64_t p_tok = p0 + team;
+    const int64_t bi_tok = p_tok >> pa.log2_block;
+    if (!kPlanned)
+        blk_raw = pa.block_table[int64_t(b) * pa.max_blocks +
+                                 (p_tok >= 0 && bi_tok < pa.max_blocks ? bi_tok : 0)];
     if (!kPlanned && wave == 0) {
         const uint32_t bits = wave_or(check_request(pa, b, L)) | s_bits;
         if (lane == 0) {
@@ -439,6 +450,7 @@ __global__ __launch_bounds__(kInjectThreads, kInjectOcc) void fs_inject_kernel(I
     __syncthreads();                         // reached by every thread still here
     if (!kPlanned && s_bits) return;
     if (!act) return;
+    if (!kPlanned) dst_row = (int64_t(blk_raw) << pa.log2_block) | (p_tok & ((1 << pa.log2_block) - 1));
     FS_GLOBAL u32x4* kd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.kc[l]) + dst_row * row_elems);
     FS_GLOBAL u32x4* vd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.vc[l]) + dst_row * row_elems);
     double c[8], sn[8];
