@@ -24,7 +24,10 @@
 // S^T = K Q^T and O^T += V^T P^T: a lane's scores are then exactly the P^T
 // entries it supplies, and the O^T column it accumulates is the query whose
 // softmax state it holds, so rescaling and normalising need no shuffles; only
-// the running maximum is reduced across lanes, once per 64 positions.  The
+// the running maximum is reduced across lanes (lane-swap moves), once per 64
+// positions.  The maximum is raised only when a column's grows by more than
+// 2^8, so unnormalised weights stay below 256 and O is rescaled on few
+// tiles; the masked pass runs only on tiles that cross the diagonal.  The
 // contraction index of P.V maps to positions in the order the score tiles
 // produce them (any order works if both operands agree).  K/V tiles of 64
 // positions are staged in LDS, both row-major, with the next tile's global
@@ -92,6 +95,20 @@ __device__ __forceinline__ __bf16 as_bf16(uint16_t h) {
 }
 
 typedef short s4 __attribute__((ext_vector_type(4)));
+
+// maximum over the four lanes l, l^16, l^32, l^48 (the rows of one S^T
+// column), by gfx950's lane-swap moves instead of LDS permutes: the first
+// swap pairs 16-lane rows 0-1 and 2-3, the second the two halves
+__device__ __forceinline__ float colmax(float x) {
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
+// the running maximum (log2 units) is raised only when a tile's exceeds it
+// by more than this, so unnormalised weights stay below 2^kLazy
+constexpr float kLazy = 8.0f;
 
 // gfx950's transposing LDS read (ds_read_b64_tr_b16): each group of 16 lanes
 // supplies 16 chunks of 4 consecutive 16-bit values, R[c][0..3] at lane c's
@@ -376,31 +393,50 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(A
                         st[hs][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[hs][kk], st[hs][sub], 0, 0, 0);
                 }
             }
-            // causal mask only where the tile reaches past the wave's first
-            // query position; columns of absent queries are never written
-            const bool full = tbase + kKT - 1 <= qp0 + j_lo;
+            // causal mask only on tiles that reach past the wave's first
+            // query position (a uniform branch); columns of absent queries
+            // are never written
+            if (tbase + kKT - 1 > qp0 + j_lo) {
+#pragma unroll
+                for (int hs = 0; hs < kHS; ++hs)
+#pragma unroll
+                    for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (tbase + 16 * sub + 4 * grp + i > qpos) st[hs][sub][i] = -1e30f;
+                __asm__ volatile("" ::: "memory");
+            }
             b8 pb[kHS][2];
-            float alpha[kHS];
+            bool rescale = false;
+            float m_new[kHS];
 #pragma unroll
             for (int hs = 0; hs < kHS; ++hs) {
                 // raw scores; the scale (> 0) is applied to the maximum and
                 // inside each exponent, fl(max(s) c) being max(fl(s c))
                 float tmax = -1e30f;
 #pragma unroll
-                for (int sub = 0; sub < 4; ++sub) {
+                for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float x = st[hs][sub][i];
-                        if (!full && tbase + 16 * sub + 4 * grp + i > qpos) x = -1e30f;
-                        st[hs][sub][i] = x;
-                        tmax = fmaxf(tmax, x);
-                    }
+                    for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, st[hs][sub][i]);
+                tmax = colmax(tmax);
+                m_new[hs] = fmaxf(m[hs], tmax * a.scale_log2);
+                rescale |= m_new[hs] > m[hs] + kLazy;
+            }
+            // the running maximum moves only when some column's grows by
+            // more than kLazy: weights stay below 2^kLazy, and the rescale of
+            // O and the sums is skipped on most tiles
+            if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
+#pragma unroll
+                for (int hs = 0; hs < kHS; ++hs) {
+                    const float alpha = __builtin_amdgcn_exp2f(m[hs] - m_new[hs]);
+                    m[hs] = m_new[hs];
+                    lp[hs] *= alpha;
+#pragma unroll
+                    for (int dc = 0; dc < 8; ++dc) o[hs][dc] *= alpha;
                 }
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-                const float m_new = fmaxf(m[hs], tmax * a.scale_log2);
-                alpha[hs] = __builtin_amdgcn_exp2f(m[hs] - m_new);
-                m[hs] = m_new;
+            }
+#pragma unroll
+            for (int hs = 0; hs < kHS; ++hs) {
                 // P^T fragments for the two 32-position halves: k = 8*grp + e maps to
                 // position 32*hh + 16*(e/4) + 4*grp + e%4, the lane's own scores
                 float psum = 0.0f;
@@ -408,17 +444,15 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(A
                 for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float pe = __builtin_amdgcn_exp2f(fmaf(st[hs][2 * hh + e / 4][e % 4], a.scale_log2, -m_new));
+                        const float pe = __builtin_amdgcn_exp2f(fmaf(st[hs][2 * hh + e / 4][e % 4], a.scale_log2, -m[hs]));
                         pb[hs][hh][e] = static_cast<__bf16>(pe);
                         psum += pe;
                     }
                 }
-                lp[hs] = lp[hs] * alpha[hs] + psum;
+                lp[hs] += psum;
             }
 #pragma unroll
             for (int dc = 0; dc < 8; ++dc) {
-#pragma unroll
-                for (int hs = 0; hs < kHS; ++hs) o[hs][dc] *= alpha[hs];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     // A = V^T row dc*16 + col, in the position order of pb,
