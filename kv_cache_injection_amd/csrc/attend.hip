@@ -30,13 +30,15 @@
 // tiles; the masked pass runs only on tiles that cross the diagonal.  The
 // contraction index of P.V maps to positions in the order the score tiles
 // produce them (any order works if both operands agree).  K/V tiles of 64
-// positions are staged in LDS, both row-major, with the next tile's global
-// loads in flight while the current one is consumed; the V^T operand comes
-// from gfx950's transposing LDS reads.  A block's raw Q and first K/V tile
-// are loaded before anything else (the block-table
-// entries of that tile are range-checked where they are read), so their
-// latency overlaps the request check and the (cos, sin) table.  Long contexts
-// are split over several blocks whose partial results a second kernel merges.
+// positions go from global memory straight into LDS (gfx950's direct loads,
+// no registers or LDS stores on the way), row-major with swizzled 16-byte
+// chunks, into two buffers: the next tile lands in one while the current one
+// is consumed from the other, with one barrier per tile.  The V^T operand
+// comes from gfx950's transposing LDS reads.  A block's raw Q and first K/V
+// tile are loaded before anything else (the block-table entries of that tile
+// are range-checked where they are read), so their latency overlaps the
+// request check and the (cos, sin) table.  Long contexts are split over
+// several blocks whose partial results a second kernel merges.
 
 #include <hip/hip_runtime.h>
 
@@ -53,8 +55,16 @@ constexpr int kQT = 16;               // query tokens per block
 constexpr int kKT = 64;               // cache positions per tile
 constexpr int kThreads = 256;         // 4 waves
 constexpr int kWaves = kThreads / 64;
-constexpr int kKPad = kD + 8;         // sK row: 272 bytes, 16-byte aligned, spreads banks
-constexpr int kVPad = kD + 16;        // sV row: 288 bytes (32 mod 256): transposing reads hit distinct banks
+constexpr int kRowB = kD * 2;         // one K or V row in LDS: 256 bytes, unpadded
+constexpr int kHalfB = kKT * kRowB;   // the K (or V) half of a tile buffer
+constexpr int kBufB = 2 * kHalfB;     // one tile buffer, K then V
+// The direct loads fill 1 KB (four rows) per wave instruction, so rows cannot
+// be padded; 16-byte chunks are XOR-swizzled within a row instead.  K chunk c
+// of row r sits in slot c ^ (r & 15): the 16 rows a score fragment reads hit
+// 16 different slots.  V chunk c sits in slot c ^ 2(r & 7): the 8 rows of a
+// half-wave's transposing reads hit 8 different slot pairs.
+__device__ __forceinline__ int k_slot(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((r & 7) << 1); }
 
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -69,6 +79,7 @@ struct AttendArgs {
     const int32_t* ctx_begin;         // [B]
     const int32_t* q_pos;             // [B]
     const double* inv_freq;           // [D/2]
+    const void* zero_row;             // 256+ bytes of zeros
     float scale_log2;                 // softmax scale * log2(e)
     float* out;                       // [B][Tq][Hq][D] fp32
     uint32_t* err;
@@ -77,7 +88,8 @@ struct AttendArgs {
     float2* part_ml;                  // [splits][B][Tq][Hq] (running max, weight sum)
 };
 
-constexpr int kBtCache = 1024;        // block-table entries a block caches in LDS
+constexpr int kBtCache = 1024;
+constexpr unsigned kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters untouched        // block-table entries a block caches in LDS
 constexpr int kMaxSplits = 16;
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
@@ -129,19 +141,24 @@ __device__ __forceinline__ b8 tr_v(const uint16_t* p, int second) {
 // the whole GQA group when group <= kHS * kWaves / kQS.  A wave's head slots
 // share every K and V fragment it reads from LDS.
 template <int kHS, int kQS>
-__global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(AttendArgs a) {
+// Two tile buffers (64 KB) and the block-table cache hold two blocks per CU.
+__global__ __launch_bounds__(kThreads, 2) void fs_attend_kernel(AttendArgs a) {
     constexpr int kWQ = kWaves / kQS;     // waves per team
     constexpr int kBQ = kQT * kQS;        // query tokens per block
     // the fp64 (cos, sin) table of the block's queries is only needed before
     // the first tile, so it shares storage with the K/V tiles
-    constexpr int kTileBytes = (kKT * kKPad + kKT * kVPad) * 2;
     constexpr int kCSBytes = kBQ * (kD / 2) * 16;
-    __shared__ __attribute__((aligned(16))) unsigned char s_raw[kTileBytes > kCSBytes ? kTileBytes : kCSBytes];
+    static_assert(kCSBytes <= kBufB, "the (cos, sin) table fits one tile buffer");
+    // two tile buffers as separate objects: the compiler then knows that
+    // reads of one need not wait for the direct loads into the other
+    __shared__ __attribute__((aligned(16))) unsigned char s_buf0[kBufB];
+    __shared__ __attribute__((aligned(16))) unsigned char s_buf1[kBufB];
     __shared__ int s_bt[kBtCache];
     __shared__ int s_ok;
-    auto sK = reinterpret_cast<uint16_t(*)[kKPad]>(s_raw);                       // [pos][d]
-    auto sV = reinterpret_cast<uint16_t(*)[kVPad]>(s_raw + kKT * kKPad * 2);    // [pos][d]
-    auto s_cs = reinterpret_cast<double2(*)[kD / 2]>(s_raw);                    // [query][i]
+    // the fp64 (cos, sin) table of the block's queries is needed only
+    // before the first tile: it lives in buffer 1, which the first tile
+    // does not use
+    auto s_cs = reinterpret_cast<double2(*)[kD / 2]>(s_buf1);                   // [query][i]
 
     // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin, so
     // physical id P runs on XCD P mod 8.  Logical ids are handed out in 8
@@ -198,43 +215,47 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(A
     const int qpos = qp0 + jq;
     const int wave_last = qp0 + min(a.tq - 1, j_lo + kQT - 1);   // the wave's last query position
 
-    // ---- tile staging: thread -> 16-byte vector lvec of positions 4*lq .. 4*lq+3
-    const int lvec = threadIdx.x & 15;
-    const int lq = threadIdx.x >> 4;
-    uint4 kr[4], vr[4];
-    auto gload_row = [&](int r, int p, int blk) {
-        const int64_t row = (int64_t(blk) << a.log2_block) | (p & bs_mask);
-        const int64_t off = (row * a.hkv + hk) * kD + lvec * 8;
-        kr[r] = *reinterpret_cast<const uint4*>(a.kc + off);
-        vr[r] = *reinterpret_cast<const uint4*>(a.vc + off);
+    // ---- tile staging by direct loads: wave w fills rows 16w .. 16w+15 of
+    // a tile, four rows (1 KB) per instruction; lane l of instruction i holds
+    // row 16w + 4i + l/16, slot l % 16.  A row past the block's last
+    // position or with a block id out of range reads the zero row.
+    const int slot = lane & 15;
+    const uint16_t* zrow = static_cast<const uint16_t*>(a.zero_row) + 8 * slot;
+    auto dma_tile = [&](unsigned char* buf, int t, const int (&blk)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * wave + 4 * i + (lane >> 4);
+            const int p = c0 + t * kKT + r;
+            const uint16_t* ks = zrow;
+            const uint16_t* vs = zrow;
+            if (blk[i] >= 0) {
+                const int64_t row = (int64_t(blk[i]) << a.log2_block) | (p & bs_mask);
+                const int64_t off = (row * a.hkv + hk) * kD;
+                ks = a.kc + off + 8 * k_slot(r, slot);
+                vs = a.vc + off + 8 * v_slot(r, slot);
+            }
+            __builtin_amdgcn_global_load_lds(ks, (__attribute__((address_space(3))) void*)(buf + (16 * wave + 4 * i) * kRowB), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vs, (__attribute__((address_space(3))) void*)(buf + kHalfB + (16 * wave + 4 * i) * kRowB), 16, 0, 0);
+        }
     };
     if (t_begin < t_end) {
         // entries read from the table and range-checked here, since the
-        // request's check has not run yet (a rejected request discards them)
-        // the four entries are read first (clamped in range, so the reads
-        // need no branch), then the eight K/V loads: no load waits behind
-        // another row's K/V
+        // request's check has not run yet (a rejected request discards the
+        // tile); the four entries are read first (clamped in range, so the
+        // reads need no branch), then the eight direct loads
         int blk[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t ei = int64_t(c0 + t_begin * kKT + 4 * lq + r) >> a.log2_block;
-            blk[r] = __builtin_nontemporal_load(bt + (ei < a.max_blocks ? ei : a.max_blocks - 1));
+        for (int i = 0; i < 4; ++i) {
+            const int64_t ei = int64_t(c0 + t_begin * kKT + 16 * wave + 4 * i + (lane >> 4)) >> a.log2_block;
+            blk[i] = __builtin_nontemporal_load(bt + (ei < a.max_blocks ? ei : a.max_blocks - 1));
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int p = c0 + t_begin * kKT + 4 * lq + r;
-            if (p > p_end || (int64_t(p) >> a.log2_block) >= a.max_blocks) blk[r] = -1;
+        for (int i = 0; i < 4; ++i) {
+            const int p = c0 + t_begin * kKT + 16 * wave + 4 * i + (lane >> 4);
+            if (p > p_end || (int64_t(p) >> a.log2_block) >= a.max_blocks || blk[i] < 0 || blk[i] >= a.num_blocks)
+                blk[i] = -1;
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int p = c0 + t_begin * kKT + 4 * lq + r;
-            if (blk[r] >= 0 && blk[r] < a.num_blocks) {
-                gload_row(r, p, blk[r]);
-            } else {
-                kr[r] = make_uint4(0, 0, 0, 0);
-                vr[r] = make_uint4(0, 0, 0, 0);
-            }
-        }
+        dma_tile(s_buf0, t_begin, blk);
     }
 
     // ---- validation of the request (every block checks, one block reports)
@@ -271,6 +292,7 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(A
     if (!s_ok) {
         // a split run marks its partials so the combine writes nothing
         if (a.splits > 1) mark(make_float2(__builtin_nanf(""), 0.0f));
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);               // no direct load outlives the block
         return;
     }
     if (t_begin >= t_end) {
@@ -319,7 +341,6 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(A
             }
         }
     }
-    __syncthreads();                                        // the table's storage becomes tiles
 
     // O^T chunks: o[hs][dc][i] = O[jq][dc*16 + 4*grp + i]
     f4 o[kHS][8];
@@ -333,46 +354,26 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(A
     }
 
     // the block ids of the four rows first (LDS or global, one uniform
-    // branch), then the eight K/V loads: a load's wait for its block id must
-    // not also wait for the rows issued before it
-    auto gload = [&](int t) {
+    // branch), then the eight direct loads
+    auto load_tile = [&](unsigned char* buf, int t) {
         int blk[4];
         if (bt_cached) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int p = c0 + t * kKT + 4 * lq + r;
-                blk[r] = p <= p_end ? s_bt[(int64_t(p) >> a.log2_block) - e_first] : -1;
+            for (int i = 0; i < 4; ++i) {
+                const int p = c0 + t * kKT + 16 * wave + 4 * i + (lane >> 4);
+                blk[i] = p <= p_end ? s_bt[(int64_t(p) >> a.log2_block) - e_first] : -1;
             }
         } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int p = c0 + t * kKT + 4 * lq + r;
-                blk[r] = p <= p_end ? bt[int64_t(p) >> a.log2_block] : -1;
+            for (int i = 0; i < 4; ++i) {
+                const int p = c0 + t * kKT + 16 * wave + 4 * i + (lane >> 4);
+                blk[i] = p <= p_end ? bt[int64_t(p) >> a.log2_block] : -1;
             }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int p = c0 + t * kKT + 4 * lq + r;
-            if (blk[r] >= 0) {
-                gload_row(r, p, blk[r]);
-            } else {
-                kr[r] = make_uint4(0, 0, 0, 0);
-                vr[r] = make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto lstore = [&]() {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            *reinterpret_cast<uint4*>(&sK[4 * lq + r][lvec * 8]) = kr[r];
-            *reinterpret_cast<uint4*>(&sV[4 * lq + r][lvec * 8]) = vr[r];
-        }
+        dma_tile(buf, t, blk);
     };
 
-    for (int t = t_begin; t < t_end; ++t) {
-        lstore();
-        __syncthreads();                                    // tile t staged
-        if (t + 1 < t_end) gload(t + 1);                   // in flight during the math
+    auto tile_math = [&](int t, const unsigned char* buf) {
         const int tbase = c0 + t * kKT;
         // a tile wholly after the wave's queries changes nothing (every weight
         // is 0), so the wave skips it; so do waves without a real query
@@ -385,7 +386,7 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(A
                 for (int hs = 0; hs < kHS; ++hs) st[hs][sub] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const b8 ka = *reinterpret_cast<const b8*>(&sK[16 * sub + col][kk * 32 + 8 * grp]);
+                    const b8 ka = *reinterpret_cast<const b8*>(buf + (16 * sub + col) * kRowB + 16 * k_slot(col, 4 * kk + grp));
                     // a slot past the group computes on zero Q and is never
                     // written: no branch between the matrix instructions
 #pragma unroll
@@ -457,14 +458,28 @@ __global__ __launch_bounds__(kThreads, kHS == 1 ? 3 : 2) void fs_attend_kernel(A
                 for (int hh = 0; hh < 2; ++hh) {
                     // A = V^T row dc*16 + col, in the position order of pb,
                     // by two transposing LDS reads of row-major V (see tr_v)
-                    const b8 va = tr_v(&sV[32 * hh + 4 * grp + (col >> 2)][dc * 16 + 4 * (col & 3)], 16 * kVPad);
+                    const int vr = 32 * hh + 4 * grp + (col >> 2);
+                    const b8 va = tr_v(reinterpret_cast<const uint16_t*>(buf + kHalfB + vr * kRowB + 16 * v_slot(vr, 2 * dc + ((col & 3) >> 1))) + 4 * (col & 1),
+                                       16 * kD);
 #pragma unroll
                     for (int hs = 0; hs < kHS; ++hs)
                         o[hs][dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hs][hh], o[hs][dc], 0, 0, 0);
                 }
             }
         }
-        __syncthreads();                                    // tile t consumed
+    };
+    // one barrier per tile: after it, tile t has landed in its buffer (each
+    // wave waited for its own direct loads first) and every wave is done
+    // with the other buffer, which then takes tile t + 1
+    auto step = [&](int t, const unsigned char* cur, unsigned char* nxt) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __syncthreads();
+        if (t + 1 < t_end) load_tile(nxt, t + 1);
+        tile_math(t, cur);
+    };
+    for (int t = t_begin; t < t_end; t += 2) {
+        step(t, s_buf0, s_buf1);
+        if (t + 1 < t_end) step(t + 1, s_buf1, s_buf0);
     }
 
     // ---- lane holds O[jq][dc*16 + 4*grp .. +3] (unnormalised)
@@ -574,6 +589,7 @@ hipError_t fsi_launch_attend(const AttendLaunch& r) {
     a.ctx_begin = r.ctx_begin;
     a.q_pos = r.q_pos;
     a.inv_freq = st->d_inv_freq;
+    a.zero_row = st->d_zero_row;
     a.scale_log2 = r.scale * 1.4426950408889634f;
     a.out = r.out;
     a.err = st->d_err;

@@ -41,6 +41,7 @@ struct fs_store {
     int64_t* d_user_begin = nullptr;   // [U+1] first fact slot of each user
     int32_t* d_user_count = nullptr;   // [U] live facts of each user: slots user_begin[u] .. + count
     double* d_inv_freq = nullptr;      // [head_dim/2] theta^(-2i/D)
+    void* d_zero_row = nullptr;        // kZeroRowBytes of zeros (rows past a tile's end read it)
     uint32_t* d_err = nullptr;         // device error word
     double* d_scores = nullptr;        // [max_batch][max_user_facts] score scratch
     int32_t topk_chunks = 0;           // chunks of the largest user (0: one-phase selection)
@@ -109,6 +110,7 @@ struct InjectLaunch {
 };
 hipError_t fsi_launch_inject(const InjectLaunch& a);
 
+constexpr size_t kZeroRowBytes = 512;
 struct AttendLaunch {
     const fs_store* st;
     int32_t batch, num_q_tokens, num_q_heads;

@@ -45,7 +45,7 @@ int ilog2(int64_t x) {
 void free_store(fs_store* s) {
     if (!s) return;
     void* bufs[] = {s->d_fact_begin, s->d_fact_len, s->d_user_begin, s->d_user_count,
-                    s->d_ingest_items, s->d_inv_freq, s->d_err,
+                    s->d_ingest_items, s->d_inv_freq, s->d_zero_row, s->d_err,
                     s->d_scores, s->d_tk_ids, s->d_tk_scores, s->d_tk_counts,
                     (void*)s->d_src_k, (void*)s->d_src_v, s->d_tok_src,
                     s->d_tok_dst, s->d_req_len, s->d_stage_k,
@@ -212,6 +212,7 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
         {(void**)&st->d_user_count, sizeof(int32_t) * d.num_users, "user counts"},
         {(void**)&st->d_ingest_items, sizeof(IngestItem) * kIngestMax, "ingest descriptors"},
         {(void**)&st->d_inv_freq, sizeof(double) * (D / 2), "frequency table"},
+        {(void**)&st->d_zero_row, kZeroRowBytes, "zero row"},
         {(void**)&st->d_err, sizeof(uint32_t), "error word"},
         {(void**)&st->d_scores, sizeof(double) * size_t(d.max_batch) * size_t(max_user > 0 ? max_user : 1), "score scratch"},
         {(void**)&st->d_tk_ids, sizeof(int32_t) * tk_elems, "top-k chunk scratch"},
@@ -258,6 +259,7 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
     st->next_row = total;                     // rows past the facts are free for ingest
     std::vector<int32_t> meta_init(4 * size_t(pinned ? d.staging_layers : 0), -1);
     uint32_t zero = 0;
+    const std::vector<unsigned char> zero_row(kZeroRowBytes, 0);
     struct { void* dst; const void* src; size_t bytes; } cps[] = {
         {st->d_fact_begin, fb.data(), sizeof(int64_t) * fb.size()},
         {st->d_fact_len, fact_len, sizeof(int32_t) * d.num_facts},
@@ -265,6 +267,7 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
         {st->d_user_count, st->h_user_count.data(), sizeof(int32_t) * d.num_users},
         {st->d_inv_freq, inv.data(), sizeof(double) * inv.size()},
         {st->d_err, &zero, sizeof(uint32_t)},
+        {st->d_zero_row, zero_row.data(), kZeroRowBytes},
         {(void*)st->d_src_k, st->src_k.data(), sizeof(void*) * d.num_layers},
         {(void*)st->d_src_v, st->src_v.data(), sizeof(void*) * d.num_layers},
         {st->d_stage_meta, meta_init.data(), sizeof(int32_t) * meta_init.size()},
