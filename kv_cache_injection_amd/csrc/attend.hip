@@ -163,12 +163,15 @@ __global__ __launch_bounds__(kThreads, 2) void fs_attend_kernel(AttendArgs a) {
     // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin, so
     // physical id P runs on XCD P mod 8.  Logical ids are handed out in 8
     // contiguous chunks, one per XCD: the query tiles of one (request, KV
-    // head) then share their K/V tiles in one XCD's L2.
+    // head) then share their K/V tiles in one XCD's L2.  Within a (request,
+    // KV head), the last query tiles go first: under the causal mask they
+    // have the longest context, and starting the longest blocks first
+    // shortens the tail of the launch.
     const int nblk = gridDim.x * gridDim.y * gridDim.z;
     const int pid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
     const int xq = nblk >> 3, xr = nblk & 7, xcd = pid & 7;
     const int lid = xcd * xq + min(xcd, xr) + (pid >> 3);
-    const int lx = lid % gridDim.x;
+    const int lx = gridDim.x - 1 - lid % gridDim.x;
     const int qt = lx / a.splits, sp = lx - qt * a.splits;
     const int hk = (lid / gridDim.x) % gridDim.y, b = lid / (gridDim.x * gridDim.y);
     const int lane = threadIdx.x & 63;
