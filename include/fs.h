@@ -296,9 +296,12 @@ FS_API fs_status fs_fetch_async(const fs_store* store, int32_t batch,
  *                  bytes for the full split.  A smaller workspace splits less,
  *                  NULL not at all; the result is the same up to rounding.
  *                  Calls that share a workspace must not overlap.
- * head_dim must be 128 (else FS_E_UNSUPPORTED).  Precision: Q, K, V bf16;
- * scores and accumulation fp32 on the matrix cores; the softmax weights are
- * rounded to bf16 before they multiply V (the normaliser sums them in fp32).  Device-checked (the request's output rows are then not written):
+ * head_dim must be 128, one cache position (num_kv_heads * 256 bytes) below
+ * 16 MiB and one cache block below 4 GiB (else FS_E_UNSUPPORTED).
+ * Precision: Q, K, V bf16; scores and accumulation fp32 on the matrix cores;
+ * the softmax weights are rounded to bf16 before they multiply V (the
+ * normaliser sums them in fp32).  Device-checked (the request's output rows
+ * are then not written):
  * FS_ERR_START_POS (ctx_begin < 0, ctx_begin > q_pos, or q_pos + Tq past
  * INT32_MAX), FS_ERR_BLOCK_SHORT, FS_ERR_BLOCK_ID.  Errors: FS_E_ARG
  * (null or misaligned: q, caches and out 16-byte aligned), FS_E_RANGE,

@@ -223,20 +223,35 @@ __global__ __launch_bounds__(kThreads, 2) void fs_attend_kernel(AttendArgs a) {
     // row 16w + 4i + l/16, slot l % 16.  A row past the block's last
     // position or with a block id out of range reads the zero row.
     const int slot = lane & 15;
-    const uint16_t* zrow = static_cast<const uint16_t*>(a.zero_row) + 8 * slot;
+    const unsigned char* zrow = static_cast<const unsigned char*>(a.zero_row) + 16 * slot;
+    // tile-invariant parts of the addresses: each of the lane's four rows,
+    // and the byte offset of its K and V chunk within a cache position
+    // (head hk, swizzled slot); a cache block is below 4 GiB (checked on
+    // the host), so only the block's base needs 64-bit arithmetic
+    const uint32_t row_b = uint32_t(a.hkv) * (kD * 2);
+    const uint32_t blk_b = row_b << a.log2_block;
+    const int pmask = (1 << a.log2_block) - 1;
+    int rr[4];
+    uint32_t ko[4], vo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        rr[i] = 16 * wave + 4 * i + (lane >> 4);
+        ko[i] = uint32_t(hk) * (kD * 2) + 16 * k_slot(rr[i], slot);
+        vo[i] = uint32_t(hk) * (kD * 2) + 16 * v_slot(rr[i], slot);
+    }
+    const unsigned char* kc_b = reinterpret_cast<const unsigned char*>(a.kc);
+    const unsigned char* vc_b = reinterpret_cast<const unsigned char*>(a.vc);
+    const int64_t dkv = vc_b - kc_b;
     auto dma_tile = [&](unsigned char* buf, int t, const int (&blk)[4]) {
+        const uint32_t tb = uint32_t(c0) + uint32_t(t) * kKT;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = 16 * wave + 4 * i + (lane >> 4);
-            const int p = c0 + t * kKT + r;
-            const uint16_t* ks = zrow;
-            const uint16_t* vs = zrow;
-            if (blk[i] >= 0) {
-                const int64_t row = (int64_t(blk[i]) << a.log2_block) | (p & bs_mask);
-                const int64_t off = (row * a.hkv + hk) * kD;
-                ks = a.kc + off + 8 * k_slot(r, slot);
-                vs = a.vc + off + 8 * v_slot(r, slot);
-            }
+            // position within its cache block (< 1024) times the position
+            // stride (< 2^24, checked on the host): a 24-bit product
+            const uint32_t in_blk = __umul24((tb + rr[i]) & pmask, row_b);
+            const unsigned char* kb = kc_b + uint64_t(uint32_t(blk[i])) * blk_b;
+            const unsigned char* ks = blk[i] >= 0 ? kb + (in_blk + ko[i]) : zrow;
+            const unsigned char* vs = blk[i] >= 0 ? kb + dkv + (in_blk + vo[i]) : zrow;
             __builtin_amdgcn_global_load_lds(ks, (__attribute__((address_space(3))) void*)(buf + (16 * wave + 4 * i) * kRowB), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(vs, (__attribute__((address_space(3))) void*)(buf + kHalfB + (16 * wave + 4 * i) * kRowB), 16, 0, 0);
         }
@@ -249,12 +264,12 @@ __global__ __launch_bounds__(kThreads, 2) void fs_attend_kernel(AttendArgs a) {
         int blk[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t ei = int64_t(c0 + t_begin * kKT + 16 * wave + 4 * i + (lane >> 4)) >> a.log2_block;
+            const int64_t ei = int64_t(c0 + t_begin * kKT + rr[i]) >> a.log2_block;
             blk[i] = __builtin_nontemporal_load(bt + (ei < a.max_blocks ? ei : a.max_blocks - 1));
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int p = c0 + t_begin * kKT + 16 * wave + 4 * i + (lane >> 4);
+            const int p = c0 + t_begin * kKT + rr[i];
             if (p > p_end || (int64_t(p) >> a.log2_block) >= a.max_blocks || blk[i] < 0 || blk[i] >= a.num_blocks)
                 blk[i] = -1;
         }
@@ -358,19 +373,25 @@ __global__ __launch_bounds__(kThreads, 2) void fs_attend_kernel(AttendArgs a) {
 
     // the block ids of the four rows first (LDS or global, one uniform
     // branch), then the eight direct loads
+    // entry indices are clamped to the block's range and read without a
+    // branch; rows past the block's last position then take -1
+    const int e_first32 = static_cast<int>(e_first), e_span = static_cast<int>(e_last - e_first);
     auto load_tile = [&](unsigned char* buf, int t) {
         int blk[4];
+        const uint32_t tb = uint32_t(c0) + uint32_t(t) * kKT;
         if (bt_cached) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int p = c0 + t * kKT + 16 * wave + 4 * i + (lane >> 4);
-                blk[i] = p <= p_end ? s_bt[(int64_t(p) >> a.log2_block) - e_first] : -1;
+                const uint32_t p = tb + rr[i];
+                const int v = s_bt[min(static_cast<int>(p >> a.log2_block) - e_first32, e_span)];
+                blk[i] = p <= uint32_t(p_end) ? v : -1;
             }
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int p = c0 + t * kKT + 16 * wave + 4 * i + (lane >> 4);
-                blk[i] = p <= p_end ? bt[int64_t(p) >> a.log2_block] : -1;
+                const uint32_t p = tb + rr[i];
+                const int v = bt[min(static_cast<int>(p >> a.log2_block), e_first32 + e_span)];
+                blk[i] = p <= uint32_t(p_end) ? v : -1;
             }
         }
         dma_tile(buf, t, blk);

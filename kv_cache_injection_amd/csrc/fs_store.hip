@@ -405,6 +405,10 @@ fs_status fs_attend_prefill(const fs_store* store, int32_t batch, int32_t num_q_
                     d.num_kv_heads);
     if (num_q_heads / d.num_kv_heads > 8)
         return fail(FS_E_UNSUPPORTED, "more than 8 query heads per KV head");
+    if (uint64_t(d.num_kv_heads) * d.head_dim * 2 >= (uint64_t(1) << 24) ||
+        uint64_t(d.num_kv_heads) * d.head_dim * 2 * uint64_t(d.block_size) >= (uint64_t(1) << 32))
+        return fail(FS_E_UNSUPPORTED, "a cache position (%d KV heads) reaches 16 MiB or a block of %d reaches 4 GiB",
+                    d.num_kv_heads, d.block_size);
     if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(FS_E_ARG, "scale must be finite and > 0");
     if (!q || !k_cache || !v_cache || !block_table || !ctx_begin || !q_pos || !out)
         return fail(FS_E_ARG, "null pointer argument");

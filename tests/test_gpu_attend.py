@@ -67,6 +67,7 @@ def _tolerance(vc_bits, table, bs, ctx_begin, q_pos, tq, group):
     (8, 8, 1, 1, 0, 0),            # one token attending to itself only
     (4, 1, 64, 20, 100, 300),      # one KV head, large blocks, late context start
     (16, 2, 8, 33, 0, 1000),       # 8 query heads per KV head
+    (8, 2, 256, 40, 70, 600),      # blocks longer than a 64-position tile
 ])
 def test_attend_matches_oracle(hq, hkv, bs, tq, c0, q0, split):
     theta = 5e5
@@ -138,6 +139,22 @@ def test_attend_device_errors_write_nothing(split):
                          torch.tensor([14, 0], dtype=torch.int32, device="cuda"), 0.1, out, ws)
     assert fs.fs_poll_errors(st) == fs.FS_ERR_BLOCK_ID
     assert torch.all(out.cpu()[0] == -7.0)
+    st.close()
+
+
+def test_attend_rejects_cache_positions_of_16_mib():
+    """A cache position of 65,536 KV heads x 128 x bf16 is 16 MiB: the
+    kernel's 24-bit offset arithmetic does not cover it, so the call is
+    rejected before any launch."""
+    hkv = 65536
+    one = [torch.zeros((1, hkv, D), dtype=torch.bfloat16, device="cuda")]
+    st = _store(hkv, 1, 1e4, facts=np.array([1], np.int32), k_pre=one, v=[one[0].clone()])
+    q = torch.zeros((1, 1, hkv, D), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((1, 1, hkv, D), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((1, 1, hkv, D), device="cuda")
+    zero = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    with pytest.raises(fs.FsError, match="16 MiB"):
+        fs.fs_attend_prefill(st, 1, q, kc, kc.clone(), zero.reshape(1, 1), 1, zero, zero, 0.1, out)
     st.close()
 
 
