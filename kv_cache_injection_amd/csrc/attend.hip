@@ -88,8 +88,8 @@ struct AttendArgs {
     float2* part_ml;                  // [splits][B][Tq][Hq] (running max, weight sum)
 };
 
-constexpr int kBtCache = 1024;
-constexpr unsigned kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters untouched        // block-table entries a block caches in LDS
+constexpr int kBtCache = 1024;        // block-table entries a block caches in LDS
+constexpr unsigned kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters untouched
 constexpr int kMaxSplits = 16;
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
