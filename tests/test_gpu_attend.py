@@ -68,6 +68,7 @@ def _tolerance(vc_bits, table, bs, ctx_begin, q_pos, tq, group):
     (4, 1, 64, 20, 100, 300),      # one KV head, large blocks, late context start
     (16, 2, 8, 33, 0, 1000),       # 8 query heads per KV head
     (8, 2, 256, 40, 70, 600),      # blocks longer than a 64-position tile
+    (8, 4, 16, 24, 3, 100),        # 2 query heads per KV head: one head per wave, two query sub-tiles
 ])
 def test_attend_matches_oracle(hq, hkv, bs, tq, c0, q0, split):
     theta = 5e5
