@@ -582,10 +582,20 @@ int attend_qsub(int group, int32_t num_q_tokens) { return group <= 4 && num_q_to
 
 }  // namespace
 
-int fsi_attend_splits(const fs_store* st, int32_t batch, int32_t num_q_tokens, int32_t num_q_heads) {
+int fsi_attend_splits(const fs_store* st, int32_t batch, int32_t num_q_tokens, int32_t num_q_heads,
+                      int32_t max_blocks) {
     const int bq = kQT * attend_qsub(num_q_heads / st->desc.num_kv_heads, num_q_tokens);
     const int64_t base = int64_t((num_q_tokens + bq - 1) / bq) * st->desc.num_kv_heads * batch;
+    // two blocks per CU (what LDS allows) ...
     int64_t sp = (2 * int64_t(st->num_cus) + base - 1) / base;
+    if (max_blocks > 0) {
+        // ... unless a split would then cover fewer than 4 tiles of the
+        // longest context the block table can hold: one block per CU with
+        // twice the tiles is then faster (the prologue and the combine are
+        // paid once per split)
+        const int64_t tiles = ((int64_t(max_blocks) << st->log2_block) + kKT - 1) / kKT;
+        if (tiles < 4 * sp) sp = int64_t(st->num_cus) / base > 1 ? int64_t(st->num_cus) / base : 1;
+    }
     return static_cast<int>(sp < 1 ? 1 : (sp > kMaxSplits ? kMaxSplits : sp));
 }
 
@@ -619,7 +629,7 @@ hipError_t fsi_launch_attend(const AttendLaunch& r) {
     a.err = st->d_err;
     // split the context when one range per (query tile, KV head, request)
     // would leave the device idle and the workspace holds the partials
-    int splits = fsi_attend_splits(st, r.batch, r.num_q_tokens, r.num_q_heads);
+    int splits = fsi_attend_splits(st, r.batch, r.num_q_tokens, r.num_q_heads, r.max_blocks);
     while (splits > 1 && fsi_attend_workspace_bytes(splits, r.batch, r.num_q_tokens, r.num_q_heads) >
                              r.workspace_bytes)
         --splits;

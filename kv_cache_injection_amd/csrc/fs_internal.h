@@ -130,7 +130,9 @@ struct AttendLaunch {
 };
 hipError_t fsi_launch_attend(const AttendLaunch& a);
 // context splits the launch would use, and the workspace that many need
-int fsi_attend_splits(const fs_store* st, int32_t batch, int32_t num_q_tokens, int32_t num_q_heads);
+// max_blocks: the block table's width (the context bound), or 0 when unknown
+int fsi_attend_splits(const fs_store* st, int32_t batch, int32_t num_q_tokens, int32_t num_q_heads,
+                      int32_t max_blocks);
 size_t fsi_attend_workspace_bytes(int splits, int32_t batch, int32_t num_q_tokens, int32_t num_q_heads);
 
 // Inverted-file index over one user's facts (approximate retrieval).

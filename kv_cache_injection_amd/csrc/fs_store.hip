@@ -433,7 +433,7 @@ fs_status fs_attend_workspace_size(const fs_store* store, int32_t batch, int32_t
     if (!store || !bytes) return fail(FS_E_ARG, "null pointer argument");
     if (batch < 1 || num_q_tokens < 1 || num_q_heads < 1)
         return fail(FS_E_RANGE, "batch, num_q_tokens and num_q_heads must be >= 1");
-    *bytes = fsi_attend_workspace_bytes(fsi_attend_splits(store, batch, num_q_tokens, num_q_heads), batch,
+    *bytes = fsi_attend_workspace_bytes(fsi_attend_splits(store, batch, num_q_tokens, num_q_heads, 0), batch,
                                         num_q_tokens, num_q_heads);
     return FS_OK;
 }
