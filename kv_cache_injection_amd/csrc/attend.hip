@@ -586,15 +586,21 @@ int fsi_attend_splits(const fs_store* st, int32_t batch, int32_t num_q_tokens, i
                       int32_t max_blocks) {
     const int bq = kQT * attend_qsub(num_q_heads / st->desc.num_kv_heads, num_q_tokens);
     const int64_t base = int64_t((num_q_tokens + bq - 1) / bq) * st->desc.num_kv_heads * batch;
-    // two blocks per CU (what LDS allows) ...
-    int64_t sp = (2 * int64_t(st->num_cus) + base - 1) / base;
-    if (max_blocks > 0) {
-        // ... unless a split would then cover fewer than 4 tiles of the
-        // longest context the block table can hold: one block per CU with
-        // twice the tiles is then faster (the prologue and the combine are
-        // paid once per split)
+    // at most two blocks per CU (what LDS allows): more would queue a
+    // second round of blocks
+    const int64_t cus = st->num_cus;
+    const int64_t two = 2 * cus / base > 1 ? 2 * cus / base : 1;
+    const int64_t one = cus / base > 1 ? cus / base : 1;
+    int64_t sp = two;
+    if (two == 2 && 4 * base >= 3 * cus) {
+        // one block per CU and no combine beats two per CU and a combine
+        sp = 1;
+    } else if (max_blocks > 0) {
+        // a split shorter than 4 tiles of the longest context the block
+        // table can hold: one block per CU with twice the tiles is faster
+        // (the prologue and the combine are paid once per split)
         const int64_t tiles = ((int64_t(max_blocks) << st->log2_block) + kKT - 1) / kKT;
-        if (tiles < 4 * sp) sp = int64_t(st->num_cus) / base > 1 ? int64_t(st->num_cus) / base : 1;
+        if (tiles < 4 * two) sp = one;
     }
     return static_cast<int>(sp < 1 ? 1 : (sp > kMaxSplits ? kMaxSplits : sp));
 }
