@@ -327,15 +327,25 @@ __global__ __launch_bounds__(kThreads, 2) void fs_attend_kernel(AttendArgs a) {
         for (int64_t j = e_first + threadIdx.x; j <= e_last; j += kThreads) s_bt[j - e_first] = bt[j];
 
     // ---- fp64 (cos, sin) of (position of query jb + qq) * w_i, shared by the
-    // heads; a thread's frequency index is the same in every iteration
+    // heads.  A thread keeps one frequency i and takes every kStep-th query:
+    // one sincos for its first query and one for the step angle, then the
+    // angle-addition recurrence (at most kBQ / kStep - 1 steps, each adding
+    // a few fp64 roundings, far below the bf16 rounding that follows)
     static_assert(kThreads % (kD / 2) == 0, "one frequency per thread");
-    const double w_i = a.inv_freq[threadIdx.x % (kD / 2)];
-    for (int e = threadIdx.x; e < kBQ * (kD / 2); e += kThreads) {
-        const int qq = e / (kD / 2);
-        const int i = e - qq * (kD / 2);
-        double sv, cv;
+    {
+        constexpr int kStep = kThreads / (kD / 2);
+        const int i = threadIdx.x % (kD / 2);
+        const double w_i = a.inv_freq[i];
+        int qq = threadIdx.x / (kD / 2);
+        double sv, cv, ds, dc;
         sincos(static_cast<double>(qp0 + jb + qq) * w_i, &sv, &cv);
-        s_cs[qq][i] = make_double2(cv, sv);
+        sincos(static_cast<double>(kStep) * w_i, &ds, &dc);
+        for (; qq < kBQ; qq += kStep) {
+            s_cs[qq][i] = make_double2(cv, sv);
+            const double cn = fma(cv, dc, -(sv * ds));
+            sv = fma(sv, dc, cv * ds);
+            cv = cn;
+        }
     }
     __syncthreads();
 
