@@ -202,6 +202,21 @@ def main():
     e2.record()
     torch.cuda.synchronize()
 
+    # timed region 3 (reported beside, never value): each inject alone after
+    # a 1 GiB write that evicts the MALL and L2, between its own HIP events
+    # (an event pair adds ~2 us to one launch), for median and p10/p90
+    n_cold = min(args.steps, 50)
+    flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
+    cold = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_cold)]
+    for j, (ca, cb) in enumerate(cold):
+        flush.fill_(j)
+        ca.record()
+        inj_s[args.warmup + j]()
+        cb.record()
+    torch.cuda.synchronize()
+    del flush
+    cold_ms = np.array([ca.elapsed_time(cb) for ca, cb in cold])
+
     wall = t1 - t0
     row_bytes = 2 * s.num_kv_heads * s.head_dim                      # one token, one layer, K or V
     inject_bytes = 4 * row_bytes * L.sum(axis=1) * nl                # K,V read + write
@@ -259,6 +274,13 @@ def main():
         },
         "kernels_ms": {"retrieve_avg": round(float(ret_ms.mean()), 5),
                        "inject_avg": round(float(inj_ms.mean()), 5)},
+        "inject_cold": {
+            "note": "each inject alone after a 1 GiB write that evicts the MALL and L2, own HIP events",
+            "launches": n_cold,
+            "ms_median": round(float(np.median(cold_ms)), 5),
+            "ms_p10": round(float(np.percentile(cold_ms, 10)), 5),
+            "ms_p90": round(float(np.percentile(cold_ms, 90)), 5),
+            "GBps_median": round(float(np.median(inject_bytes[:n_cold] / (cold_ms * 1e-3) / 1e9)), 1)},
         "roofline": {"bound": "hbm", "kernel": "fs_inject_kernel<128>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
