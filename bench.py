@@ -751,6 +751,18 @@ def recorded_traffic(config: str, layers: int):
     return rec.get("traffic_bytes_per_launch")
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, ds, layers, n_req, max_host_bytes=16 << 30):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     retrieve + compose + rotate + scatter for ``n_req`` requests, over the
@@ -815,6 +827,7 @@ def cpu_baseline(wl, ds, layers, n_req, max_host_bytes=16 << 30):
             "seconds": round(dt, 2),
             "sample": f"{n_req} request(s) of the {s.name} workload (the first request of each "
                       f"set), {nl} layer(s), k={wl.k}: numpy fp64 oracle, one thread",
+            "cpu_model": host_cpu_model(),
             "all_cores": {"value": round(total_all / dt_all / 1e9, 4), "unit": "GB/s",
                           "requests_per_s": round(n_req / dt_all, 4), "cores": nt,
                           "seconds": round(dt_all, 2),
