@@ -245,6 +245,44 @@ FS_API fs_status fs_inject_layers(const fs_store* store, int32_t layer_begin, in
                            int32_t num_blocks, void* stream);
 
 /*
+ * fs_plan_inject, fs_inject_planned — fs_inject in two calls, with the
+ * composition and validation (the segment of ids[b] laid from start_pos[b],
+ * same passages as fs_inject) written once into a caller-owned plan instead
+ * of being recomputed by the injecting blocks.  A serving loop plans request
+ * i + 1 (a small launch, one block per request) while request i injects on
+ * another stream, and each inject then starts moving bytes at once.  The
+ * result of fs_plan_inject followed by fs_inject_planned equals fs_inject_layers
+ * with the same arguments, bit for bit.  Device stores only
+ * (FS_E_UNSUPPORTED otherwise).
+ *
+ * fs_inject_plan_size: bytes of a plan for `batch` requests (1 .. max_batch).
+ * The plan holds per request its segment length (0 when rejected) and start
+ * position, and every segment token's arena row and cache slot.
+ *
+ * fs_plan_inject: arguments as fs_inject's; plan is device memory of at least
+ *   fs_inject_plan_size(batch) bytes, 16-byte aligned (else FS_E_RANGE /
+ *   FS_E_ARG), owned by the caller.  Device-checked as fs_inject
+ *   (FS_ERR_USER, FS_ERR_FACT_ID, FS_ERR_START_POS, FS_ERR_BLOCK_SHORT,
+ *   FS_ERR_BLOCK_ID): a rejected request's length is 0, so no inject from
+ *   the plan writes anything for it.  k = 0 enqueues nothing.
+ *
+ * fs_inject_planned: the layers [layer_begin, layer_end) from a plan that
+ *   fs_plan_inject wrote earlier in stream order (or after an event) with the
+ *   same batch and k; k_cache and v_cache as fs_inject's, each holding at
+ *   least the num_blocks the plan was checked against.  A plan may be used
+ *   for any number of layer ranges; it must not be rewritten while an inject
+ *   reads it.  Errors: FS_E_ARG, FS_E_RANGE, FS_E_UNSUPPORTED, FS_E_HIP.
+ */
+FS_API fs_status fs_inject_plan_size(const fs_store* store, int32_t batch, size_t* bytes);
+FS_API fs_status fs_plan_inject(const fs_store* store, int32_t batch, const int32_t* user,
+                                const int32_t* ids, int32_t k, const int32_t* block_table,
+                                int32_t max_blocks, const int32_t* start_pos, int32_t num_blocks,
+                                void* plan, size_t plan_bytes, void* stream);
+FS_API fs_status fs_inject_planned(const fs_store* store, int32_t layer_begin, int32_t layer_end,
+                                   int32_t batch, int32_t k, const void* plan, size_t plan_bytes,
+                                   void* const* k_cache, void* const* v_cache, void* stream);
+
+/*
  * fs_fetch_async — host-DRAM offload (gist.science summary, "Résultats":
  * the KV store can be offloaded to host DRAM at a small TTFT cost).
  * Pinned stores only.  Gathers the selected facts' K and V rows of layers

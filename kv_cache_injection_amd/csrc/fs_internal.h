@@ -107,8 +107,33 @@ struct InjectLaunch {
     void* const* v_cache;
     int32_t num_blocks;
     hipStream_t stream;
+    // caller-owned plans (device stores): plan_out set = compose and
+    // validate into it and launch nothing else; plan_in set = inject from it
+    // (user, ids, block_table, start_pos unused)
+    void* plan_out = nullptr;
+    const void* plan_in = nullptr;
 };
 hipError_t fsi_launch_inject(const InjectLaunch& a);
+
+// Layout of a caller-owned inject plan for `batch` requests: segment length
+// (0 if rejected) and start position per request, padded to 16 bytes, then
+// each segment token's arena row and cache slot, seg_tokens per request.
+struct PlanView {
+    int32_t* req_len;
+    int32_t* start;
+    int64_t* tok_src;
+    int64_t* tok_dst;
+};
+inline size_t fsi_plan_header_bytes(int32_t batch) { return (size_t(batch) * 8 + 15) / 16 * 16; }
+inline size_t fsi_plan_bytes(const fs_store* st, int32_t batch) {
+    return fsi_plan_header_bytes(batch) + 2 * sizeof(int64_t) * size_t(batch) * size_t(st->seg_tokens);
+}
+inline PlanView fsi_plan_view(const fs_store* st, int32_t batch, const void* plan) {
+    char* p = static_cast<char*>(const_cast<void*>(plan));
+    int64_t* rows = reinterpret_cast<int64_t*>(p + fsi_plan_header_bytes(batch));
+    const size_t n = size_t(batch) * size_t(st->seg_tokens);
+    return PlanView{reinterpret_cast<int32_t*>(p), reinterpret_cast<int32_t*>(p) + batch, rows, rows + n};
+}
 
 constexpr size_t kZeroRowBytes = 512;
 struct AttendLaunch {

@@ -348,6 +348,80 @@ fs_status fs_inject_layers(const fs_store* store, int32_t layer_begin, int32_t l
     return FS_OK;
 }
 
+fs_status fs_inject_plan_size(const fs_store* store, int32_t batch, size_t* bytes) {
+    g_msg[0] = 0;
+    if (!store || !bytes) return fail(FS_E_ARG, "null argument");
+    if (batch < 1 || batch > store->desc.max_batch)
+        return fail(FS_E_RANGE, "batch %d outside [1, %d]", batch, store->desc.max_batch);
+    *bytes = fsi_plan_bytes(store, batch);
+    return FS_OK;
+}
+
+namespace {
+
+// the checks a plan buffer must pass in both halves of the planned path
+fs_status check_plan(const fs_store* store, int32_t batch, int32_t k, const void* plan, size_t plan_bytes) {
+    const fs_store_desc& d = store->desc;
+    if (d.kv_location != FS_KV_DEVICE) return fail(FS_E_UNSUPPORTED, "planned injection needs a device store");
+    if (batch < 1 || batch > d.max_batch) return fail(FS_E_RANGE, "batch %d outside [1, %d]", batch, d.max_batch);
+    if (k < 0 || k > d.max_k) return fail(FS_E_RANGE, "k %d outside [0, %d]", k, d.max_k);
+    if (!plan) return fail(FS_E_ARG, "null plan");
+    if (!aligned(plan, 16)) return fail(FS_E_ARG, "plan not 16-byte aligned");
+    if (plan_bytes < fsi_plan_bytes(store, batch))
+        return fail(FS_E_RANGE, "plan of %zu bytes, %zu needed for %d requests", plan_bytes,
+                    fsi_plan_bytes(store, batch), batch);
+    return FS_OK;
+}
+
+}  // namespace
+
+fs_status fs_plan_inject(const fs_store* store, int32_t batch, const int32_t* user, const int32_t* ids, int32_t k,
+                         const int32_t* block_table, int32_t max_blocks, const int32_t* start_pos,
+                         int32_t num_blocks, void* plan, size_t plan_bytes, void* stream) {
+    g_msg[0] = 0;
+    if (!store) return fail(FS_E_ARG, "null store");
+    const fs_status c = check_plan(store, batch, k, plan, plan_bytes);
+    if (c != FS_OK) return c;
+    if (!user || !ids || !block_table || !start_pos) return fail(FS_E_ARG, "null pointer argument");
+    if (!aligned(user, 4) || !aligned(ids, 4) || !aligned(block_table, 4) || !aligned(start_pos, 4))
+        return fail(FS_E_ARG, "int32 argument not 4-byte aligned");
+    if (max_blocks < 1) return fail(FS_E_BLOCKTABLE, "max_blocks %d < 1", max_blocks);
+    if (num_blocks < 1) return fail(FS_E_BLOCKTABLE, "num_blocks %d < 1", num_blocks);
+    if (k == 0) return FS_OK;
+    InjectLaunch a{store, 0, store->desc.num_layers, batch, user, ids, k, block_table, max_blocks, start_pos,
+                   nullptr, nullptr, num_blocks, reinterpret_cast<hipStream_t>(stream)};
+    a.plan_out = plan;
+    hipError_t e = fsi_launch_inject(a);
+    if (e != hipSuccess) return hip_fail(e, "plan launch");
+    return FS_OK;
+}
+
+fs_status fs_inject_planned(const fs_store* store, int32_t layer_begin, int32_t layer_end, int32_t batch, int32_t k,
+                            const void* plan, size_t plan_bytes, void* const* k_cache, void* const* v_cache,
+                            void* stream) {
+    g_msg[0] = 0;
+    if (!store) return fail(FS_E_ARG, "null store");
+    const fs_status c = check_plan(store, batch, k, plan, plan_bytes);
+    if (c != FS_OK) return c;
+    const fs_store_desc& d = store->desc;
+    if (layer_begin < 0 || layer_end > d.num_layers || layer_begin >= layer_end)
+        return fail(FS_E_RANGE, "layer range [%d, %d) invalid for %d layers", layer_begin, layer_end,
+                    d.num_layers);
+    if (!k_cache || !v_cache) return fail(FS_E_ARG, "null pointer argument");
+    for (int l = layer_begin; l < layer_end; ++l) {
+        if (!k_cache[l] || !v_cache[l]) return fail(FS_E_ARG, "layer %d cache pointer is null", l);
+        if (!aligned(k_cache[l], 16) || !aligned(v_cache[l], 16))
+            return fail(FS_E_ARG, "layer %d cache not 16-byte aligned", l);
+    }
+    if (k == 0) return FS_OK;
+    InjectLaunch a{store, layer_begin, layer_end, batch, nullptr, nullptr, k, nullptr, 0, nullptr,
+                   k_cache, v_cache, 0, reinterpret_cast<hipStream_t>(stream)};
+    a.plan_in = plan;
+    hipError_t e = fsi_launch_inject(a);
+    if (e != hipSuccess) return hip_fail(e, "inject launch");
+    return FS_OK;
+}
+
 fs_status fs_inject(const fs_store* store, int32_t layer, int32_t batch, const int32_t* user,
                     const int32_t* ids, int32_t k, const int32_t* block_table, int32_t max_blocks,
                     const int32_t* start_pos, void* const* k_cache, void* const* v_cache,

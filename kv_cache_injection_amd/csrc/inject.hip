@@ -83,6 +83,7 @@ struct PlanArgs {
     int64_t* tok_src;
     int64_t* tok_dst;
     int32_t* req_len;
+    int32_t* start_out;             // a caller-owned plan's copy of start_pos, or null
     uint32_t* err;
 };
 
@@ -307,6 +308,7 @@ __global__ __launch_bounds__(kPlanThreads) void fs_plan_kernel(PlanArgs a) {
             s_len = bits ? 0 : L;
             s_nf = nf;
             a.req_len[b] = bits ? 0 : L;
+            if (a.start_out) a.start_out[b] = a.start_pos[b];
         }
     }
     __syncthreads();
@@ -597,6 +599,16 @@ hipError_t launch_inject(const InjectLaunch& r) {
     pa.req_len = st->d_req_len;
     pa.err = st->d_err;
     const size_t plan_lds = sizeof(int64_t) * (size_t(r.k) + (size_t(r.k) + 2) / 2);
+    if (r.plan_out) {
+        // compose and validate into the caller's plan, nothing else
+        const PlanView v = fsi_plan_view(st, r.batch, r.plan_out);
+        pa.tok_src = v.tok_src;
+        pa.tok_dst = v.tok_dst;
+        pa.req_len = v.req_len;
+        pa.start_out = v.start;
+        fs_plan_kernel<<<dim3(r.batch), kPlanThreads, plan_lds, r.stream>>>(pa);
+        return hipGetLastError();
+    }
 
     InjectArgs a{};
     a.start_pos = r.start_pos;
@@ -627,7 +639,16 @@ hipError_t launch_inject(const InjectLaunch& r) {
     const int64_t groups = std::max<int64_t>(1, (int64_t(r.k) * st->max_fact_len + kTok - 1) / kTok);
     const dim3 grid(static_cast<unsigned>(groups), static_cast<unsigned>(r.batch),
                     static_cast<unsigned>(r.layer_end - r.layer_begin));
-    if (d.kv_location == FS_KV_PINNED_HOST) {
+    if (r.plan_in) {
+        // inject from the caller's plan: the blocks read their tokens' rows
+        // and slots instead of planning
+        const PlanView v = fsi_plan_view(st, r.batch, r.plan_in);
+        a.start_pos = v.start;
+        a.tok_src = v.tok_src;
+        a.tok_dst = v.tok_dst;
+        a.req_len = v.req_len;
+        fs_inject_kernel<D, true><<<grid, kInjectThreads, 0, r.stream>>>(a, pa);
+    } else if (d.kv_location == FS_KV_PINNED_HOST) {
         fs_plan_kernel<<<dim3(r.batch), kPlanThreads, plan_lds, r.stream>>>(pa);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -42,7 +42,7 @@ FS_KV_DEVICE = 0
 FS_KV_PINNED_HOST = 1
 
 EXPORTS = ("fs_create_store", "fs_destroy_store", "fs_retrieve_topk", "fs_inject",
-           "fs_inject_layers", "fs_fetch_async", "fs_attend_prefill", "fs_attend_workspace_size", "fs_ingest_init",
+           "fs_inject_layers", "fs_inject_plan_size", "fs_plan_inject", "fs_inject_planned", "fs_fetch_async", "fs_attend_prefill", "fs_attend_workspace_size", "fs_ingest_init",
            "fs_ingest_facts", "fs_evict_fact", "fs_store_live", "fs_ivf_build",
            "fs_ivf_destroy", "fs_ivf_arrays", "fs_ivf_retrieve_topk", "fs_poll_errors",
            "fs_strerror", "fs_last_error_message")
@@ -100,6 +100,9 @@ def _load() -> ctypes.CDLL:
         "fs_retrieve_topk": (i32, [P, i32, P, P, i32, P, P, P, P]),
         "fs_inject": (i32, [P, i32, i32, P, P, i32, P, i32, P, P, P, i32, P]),
         "fs_inject_layers": (i32, [P, i32, i32, i32, P, P, i32, P, i32, P, P, P, i32, P]),
+        "fs_inject_plan_size": (i32, [P, i32, ctypes.POINTER(ctypes.c_size_t)]),
+        "fs_plan_inject": (i32, [P, i32, P, P, i32, P, i32, P, i32, P, ctypes.c_size_t, P]),
+        "fs_inject_planned": (i32, [P, i32, i32, i32, i32, P, ctypes.c_size_t, P, P, P]),
         "fs_fetch_async": (i32, [P, i32, P, P, i32, i32, i32, P]),
         "fs_attend_prefill": (i32, [P, i32, i32, i32, P, P, P, i32, P, i32, P, P, ctypes.c_float,
                                     P, P, ctypes.c_size_t, P]),
@@ -297,6 +300,55 @@ def fs_inject_layers(store, layer_begin: int, layer_end: int, batch: int, user: 
         raise ValueError(f"no cache given for some layer of [{layer_begin}, {layer_end})")
     prepare_inject(store, (layer_begin, layer_end), batch, user, ids, k, block_table, max_blocks,
                    start_pos, caches, stream=stream)()
+
+
+def fs_inject_plan_size(store, batch: int) -> int:
+    """Bytes of a caller-owned plan for ``batch`` requests."""
+    n = ctypes.c_size_t(0)
+    _check(_lib.fs_inject_plan_size(_handle(store), int(batch), ctypes.byref(n)), "fs_inject_plan_size")
+    return int(n.value)
+
+
+def new_inject_plan(store, batch: int) -> torch.Tensor:
+    """A device buffer for an inject plan of ``batch`` requests."""
+    return torch.empty((fs_inject_plan_size(store, batch),), dtype=torch.uint8, device="cuda")
+
+
+def prepare_plan_inject(store, batch: int, user, ids, k: int, block_table, max_blocks: int,
+                        start_pos, num_blocks: int, plan: torch.Tensor, stream=None) -> Prepared:
+    """fs_plan_inject: compose and validate the requests into ``plan``."""
+    args = (_handle(store), int(batch),
+            _ptr(user, torch.int32, shape=(batch,), name="user"),
+            _ptr(ids, torch.int32, shape=(batch, k), name="ids"), int(k),
+            _ptr(block_table, torch.int32, shape=(batch, max_blocks), name="block_table"),
+            int(max_blocks),
+            _ptr(start_pos, torch.int32, shape=(batch,), name="start_pos"), int(num_blocks),
+            _ptr(plan, torch.uint8, name="plan"), ctypes.c_size_t(plan.numel()), _stream(stream))
+    return Prepared(_lib.fs_plan_inject, args, "fs_plan_inject", (store, user, ids, block_table, start_pos, plan))
+
+
+def prepare_inject_planned(store, layers, batch: int, k: int, plan: torch.Tensor,
+                           caches: "CacheTable", stream=None) -> Prepared:
+    """fs_inject_planned over ``layers`` (FS_ALL_LAYERS or a (begin, end) pair)."""
+    if not isinstance(caches, CacheTable):
+        raise TypeError("prepare_inject_planned takes a CacheTable")
+    lb, le = (0, len(caches.present)) if layers == FS_ALL_LAYERS else (int(layers[0]), int(layers[1]))
+    if 0 <= lb < le <= len(caches.present) and not all(caches.present[lb:le]):
+        raise ValueError(f"no cache given for some layer of [{lb}, {le})")
+    args = (_handle(store), lb, le, int(batch), int(k), _ptr(plan, torch.uint8, name="plan"),
+            ctypes.c_size_t(plan.numel()), caches.k, caches.v, _stream(stream))
+    return Prepared(_lib.fs_inject_planned, args, "fs_inject_planned", (store, plan, caches))
+
+
+def fs_plan_inject(store, batch: int, user, ids, k: int, block_table, max_blocks: int, start_pos,
+                   num_blocks: int, plan: torch.Tensor, stream=None) -> None:
+    prepare_plan_inject(store, batch, user, ids, k, block_table, max_blocks, start_pos, num_blocks,
+                        plan, stream)()
+
+
+def fs_inject_planned(store, layers, batch: int, k: int, plan: torch.Tensor, caches: "CacheTable",
+                      stream=None) -> None:
+    prepare_inject_planned(store, layers, batch, k, plan, caches, stream)()
 
 
 def fs_fetch_async(store, batch: int, user: torch.Tensor, ids: torch.Tensor, k: int,

@@ -280,9 +280,10 @@ def test_host_checked_errors_enqueue_nothing():
 
 # --------------------------------------------------------- device-checked faults
 
+@pytest.mark.parametrize("path", ["fused", "planned"])
 @pytest.mark.parametrize("fault", ["block_short", "block_id", "start_pos", "pos_overflow",
                                    "fact_id", "pad_then_id", "user"])
-def test_device_checked_fault_writes_nothing(fault):
+def test_device_checked_fault_writes_nothing(fault, path):
     wl = synth.make_workload("tiny", seed=91)
     s = wl.shape
     B = 2
@@ -313,10 +314,16 @@ def test_device_checked_fault_writes_nothing(fault):
     elif fault == "user":
         users[1] = 1
     kc, vc = synth.make_caches(wl, [0], "cuda")
-    say(f"fault {fault}")
-    fs.fs_inject(ds.store, fs.FS_ALL_LAYERS, B, torch.from_numpy(users).cuda(),
-                 torch.from_numpy(ids).cuda(), wl.k, torch.from_numpy(table).cuda(), mb,
-                 torch.from_numpy(sp).cuda(), kc, vc, s.pool_blocks)
+    say(f"fault {fault}, {path}")
+    args = (torch.from_numpy(users).cuda(), torch.from_numpy(ids).cuda(), wl.k,
+            torch.from_numpy(table).cuda(), mb, torch.from_numpy(sp).cuda())
+    if path == "fused":
+        fs.fs_inject(ds.store, fs.FS_ALL_LAYERS, B, *args, kc, vc, s.pool_blocks)
+    else:
+        plan = fs.new_inject_plan(ds.store, B)
+        fs.fs_plan_inject(ds.store, B, *args, s.pool_blocks, plan)
+        fs.fs_inject_planned(ds.store, fs.FS_ALL_LAYERS, B, wl.k, plan,
+                             fs.CacheTable(ds.store, kc, vc, s.pool_blocks))
     assert fs.fs_poll_errors(ds.store) == expect
     # request 0 is fine and written; request 1 wrote nothing
     w0 = {0: ids[0].astype(np.int64)}

@@ -164,3 +164,85 @@ def test_two_lane_steps_match_one_stream():
     o = check_retrieval(wl0, ids[0].cpu().numpy(), scores[0].cpu().numpy(), ntok[0].cpu().numpy(), [0], k)
     check_injection(wl0, ds, pools[0][0], pools[0][1], o, [0, 3])
     ds.close()
+
+
+def test_planned_inject_equals_fused_inject():
+    """fs_plan_inject + fs_inject_planned against fs_inject, bit for bit: all
+    layers at once, one plan reused for two layer ranges, and the bench's two
+    lanes with a plan per lane (each lane plans step i + 1 while the other
+    injects step i).  Step 0 is also checked against the oracle."""
+    wl = synth.make_workload("llama", seed=1011)
+    s = wl.shape
+    layers = [0, 1, 2, 3]
+    B, k = s.batch, wl.k
+    mb = wl.block_table.shape[1]
+    say("planned: building store")
+    ds = build_store(wl, layers)
+    sets = [request_tensors(wl, queries=r["queries"], start_pos=r["start_pos"],
+                            block_table=r["block_table"])
+            for r in synth.request_sets(wl, 6, seed=wl.seed + 17)]
+    n = len(sets)
+    ids = [torch.empty((B, k), dtype=torch.int32, device="cuda") for _ in range(n)]
+    for i, r in enumerate(sets):
+        fs.fs_retrieve_topk(ds.store, B, r["user"], r["query"], k, ids[i], None, None)
+    torch.cuda.synchronize()
+    nb = synth.make_caches(wl, layers, "cuda")[0][0].shape[0]
+    with pytest.raises(fs.FsError) as e:                     # a plan too small
+        fs.fs_plan_inject(ds.store, B, sets[0]["user"], ids[0], k, sets[0]["block_table"], mb,
+                          sets[0]["start_pos"], nb, torch.empty(64, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == fs.FS_E_RANGE
+    say("planned: all layers, then a reused plan over two layer ranges")
+    for i in (0, 1):
+        r = sets[i]
+        rk, rv = synth.make_caches(wl, layers, "cuda")
+        fs.fs_inject(ds.store, fs.FS_ALL_LAYERS, B, r["user"], ids[i], k, r["block_table"], mb,
+                     r["start_pos"], rk, rv, nb)
+        plan = fs.new_inject_plan(ds.store, B)
+        fs.fs_plan_inject(ds.store, B, r["user"], ids[i], k, r["block_table"], mb, r["start_pos"], nb, plan)
+        kc, vc = synth.make_caches(wl, layers, "cuda")
+        tb = fs.CacheTable(ds.store, kc, vc, nb)
+        if i == 0:
+            fs.fs_inject_planned(ds.store, fs.FS_ALL_LAYERS, B, k, plan, tb)
+        else:
+            fs.fs_inject_planned(ds.store, (0, 1), B, k, plan, tb)
+            fs.fs_inject_planned(ds.store, (1, 4), B, k, plan, tb)
+        torch.cuda.synchronize()
+        for l in range(len(layers)):
+            assert torch.equal(_bits(kc[l]), _bits(rk[l])), f"set {i} layer {l} K"
+            assert torch.equal(_bits(vc[l]), _bits(rv[l])), f"set {i} layer {l} V"
+    say("planned: two lanes, a plan per lane")
+    lanes = [torch.cuda.Stream(), torch.cuda.Stream()]
+    plans = [fs.new_inject_plan(ds.store, B) for _ in lanes]
+    done = [torch.cuda.Event() for _ in range(n)]
+    pools = [synth.make_caches(wl, layers, "cuda") for _ in range(n)]
+    for i, r in enumerate(sets):
+        lane = lanes[i % 2]
+        # the lane's previous inject read this plan: stream order keeps the
+        # rewrite after it
+        fs.fs_plan_inject(ds.store, B, r["user"], ids[i], k, r["block_table"], mb, r["start_pos"], nb,
+                          plans[i % 2], stream=lane)
+        kc, vc = pools[i]
+        fs.fs_inject_planned(ds.store, fs.FS_ALL_LAYERS, B, k, plans[i % 2],
+                             fs.CacheTable(ds.store, kc, vc, nb), stream=lane)
+        done[i].record(lane)
+    torch.cuda.synchronize()
+    assert fs.fs_poll_errors(ds.store) == 0
+    for i, r in enumerate(sets):
+        rk, rv = synth.make_caches(wl, layers, "cuda")
+        fs.fs_inject(ds.store, fs.FS_ALL_LAYERS, B, r["user"], ids[i], k, r["block_table"], mb,
+                     r["start_pos"], rk, rv, nb)
+        torch.cuda.synchronize()
+        kc, vc = pools[i]
+        for l in range(len(layers)):
+            assert torch.equal(_bits(kc[l]), _bits(rk[l])), f"step {i} layer {l} K"
+            assert torch.equal(_bits(vc[l]), _bits(rv[l])), f"step {i} layer {l} V"
+    wl0 = dataclasses.replace(wl, queries=sets[0]["query"].cpu().numpy(),
+                              start_pos=sets[0]["start_pos"].cpu().numpy(),
+                              block_table=sets[0]["block_table"].cpu().numpy())
+    scores = torch.empty((B, k), dtype=torch.float64, device="cuda")
+    ntok = torch.empty((B,), dtype=torch.int32, device="cuda")
+    rid = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    fs.fs_retrieve_topk(ds.store, B, sets[0]["user"], sets[0]["query"], k, rid, scores, ntok)
+    o = check_retrieval(wl0, rid.cpu().numpy(), scores.cpu().numpy(), ntok.cpu().numpy(), [0], k)
+    check_injection(wl0, ds, pools[0][0], pools[0][1], o, [0, 3])
+    ds.close()
