@@ -125,7 +125,8 @@ def main():
     total = args.warmup + args.steps
     ids = torch.empty((total, B, k), dtype=torch.int32, device="cuda")   # one slot per step
     ntok = torch.zeros((total, B), dtype=torch.int32, device="cuda")
-    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    plans = [fs.new_inject_plan(ds.store, B) for _ in range(total)]     # one plan per step
+    e0, e1, e2, e3, e4 = (torch.cuda.Event(enable_timing=True) for _ in range(5))
 
     # Pipelined steps on two lanes (streams at the default priority): step i
     # retrieves and injects on lane i % 2, so each inject follows its own
@@ -133,6 +134,10 @@ def main():
     # beside it.  Retrievals share the store's score scratch, so retrieval i
     # waits for retrieval i - 1 (an event); the two lanes write separate cache
     # pools, as two different requests would.  ids have a slot per step.
+    # (Planning each step into its own plan, fs_plan_inject, and injecting
+    # from it gives the same step time here: the two lanes already overlap
+    # each inject's planning with the other lane's work.  Region 2 times the
+    # planned kernels too.)
     kc2, vc2 = synth.make_caches(wl, layers, "cuda")
     caches2 = fs.CacheTable(ds.store, kc2, vc2, nb)
     lanes = (torch.cuda.Stream(), torch.cuda.Stream())
@@ -146,11 +151,16 @@ def main():
         ic = [fs.prepare_inject(ds.store, fs.FS_ALL_LAYERS, B, user, ids[i], k,
                                 sets[i % len(sets)]["block_table"], mb, sets[i % len(sets)]["start_pos"],
                                 cache_of(i), stream=stream_inj(i)) for i in range(total)]
-        return rc, ic
-    ret_p, inj_p = prep(lambda i: lanes[i % 2], lambda i: lanes[i % 2],
-                        lambda i: caches if i % 2 == 0 else caches2)            # two lanes
+        pc = [fs.prepare_plan_inject(ds.store, B, user, ids[i], k, sets[i % len(sets)]["block_table"], mb,
+                                     sets[i % len(sets)]["start_pos"], nb, plans[i], stream=stream_inj(i))
+              for i in range(total)]
+        jc = [fs.prepare_inject_planned(ds.store, fs.FS_ALL_LAYERS, B, k, plans[i], cache_of(i),
+                                        stream=stream_inj(i)) for i in range(total)]
+        return rc, ic, pc, jc
+    ret_p, inj_p, _, _ = prep(lambda i: lanes[i % 2], lambda i: lanes[i % 2],
+                              lambda i: caches if i % 2 == 0 else caches2)         # two lanes
     cur = torch.cuda.current_stream()
-    ret_s, inj_s = prep(lambda i: cur, lambda i: cur)                          # one stream, in order
+    ret_s, inj_s, plan_s, injp_s = prep(lambda i: cur, lambda i: cur)           # one stream, in order
 
     def step_pipelined(i):
         lane = lanes[i % 2]
@@ -190,9 +200,10 @@ def main():
 
     # timed region 2: per-kernel average durations for the roofline, from
     # HIP events on the launch stream: the steps' retrievals back to back
-    # between two events, then their injects back to back between two more
-    # (each inject reads the ids its step's retrieval wrote); the average is
-    # the span over the number of launches
+    # between two events, then their fused injects, their plans and their
+    # injects from the plans, each kind back to back between two more (each
+    # reads what its step's retrieval or plan wrote); the average is the
+    # span over the number of launches
     e0.record()
     for i in range(args.warmup, total):
         ret_s[i]()
@@ -200,6 +211,12 @@ def main():
     for i in range(args.warmup, total):
         inj_s[i]()
     e2.record()
+    for i in range(args.warmup, total):
+        plan_s[i]()
+    e3.record()
+    for i in range(args.warmup, total):
+        injp_s[i]()
+    e4.record()
     torch.cuda.synchronize()
 
     # timed region 3 (reported beside, never value): each inject alone after
@@ -224,6 +241,8 @@ def main():
     scan_bytes = 4 * int(n_user.sum()) * s.embed_dim
     step_bytes = inject_bytes + scan_bytes
     inj_ms = np.full(args.steps, e1.elapsed_time(e2) / args.steps)
+    plan_ms = e2.elapsed_time(e3) / args.steps
+    planned_ms = e3.elapsed_time(e4) / args.steps
     ret_ms = np.full(args.steps, e0.elapsed_time(e1) / args.steps)
     achieved = float(inject_bytes.sum() / (inj_ms.sum() * 1e-3) / 1e9)
     value = float(step_bytes.sum() / wall / 1e9)
@@ -273,7 +292,9 @@ def main():
             "request_sets": args.sets,
         },
         "kernels_ms": {"retrieve_avg": round(float(ret_ms.mean()), 5),
-                       "inject_avg": round(float(inj_ms.mean()), 5)},
+                       "inject_avg": round(float(inj_ms.mean()), 5),
+                       "plan_avg": round(float(plan_ms), 5),
+                       "inject_from_plan_avg": round(float(planned_ms), 5)},
         "inject_cold": {
             "note": "each inject alone after a 1 GiB write that evicts the MALL and L2, own HIP events",
             "launches": n_cold,
@@ -525,7 +546,8 @@ def bench_overlap(args):
     (a prefill chunk through an MLP of the model's width: two bf16 GEMMs per
     layer), not part of the library.  Plans: one launch per layer; layer 0
     alone then the rest; chunks of 1, 2, 4, ... layers; all layers before the
-    forward starts.  Reported per plan: injection alone, both overlapped, and
+    forward starts; and the first and third with the batch planned once
+    (fs_plan_inject) and every chunk injecting from the plan.  Reported per plan: injection alone, both overlapped, and
     the exposed time (overlapped minus forward alone); value = the best plan's."""
     import numpy as np
     import torch
@@ -572,8 +594,13 @@ def bench_overlap(args):
     while b0 < nl:
         plans["doubling"].append((b0, min(nl, b0 + w)))
         b0, w = b0 + w, 2 * w
+    # the same chunkings with the batch planned once (fs_plan_inject) and
+    # every chunk injecting from the plan
+    for name in ("per_layer", "doubling"):
+        plans[name + "_planned"] = plans[name]
     calls = {name: [inj.prepare(B, user, ids[i], k, sets[i % len(sets)]["block_table"], mb,
-                                sets[i % len(sets)]["start_pos"], chunks=plan) for i in range(total)]
+                                sets[i % len(sets)]["start_pos"], chunks=plan,
+                                planned=name.endswith("_planned")) for i in range(total)]
              for name, plan in plans.items()}
 
     def forward(wait_layers: bool):

@@ -41,27 +41,43 @@ class LayerInjector:
         self.caches = caches
         self.num_layers = num_layers
         self.stream = stream or torch.cuda.Stream()
-        self._events: List[torch.cuda.Event] = [torch.cuda.Event() for _ in range(num_layers)]
+        # one event per launch: at most one per layer, and the plan
+        self._events: List[torch.cuda.Event] = [torch.cuda.Event() for _ in range(num_layers + 1)]
         self._event_of: List[Optional[torch.cuda.Event]] = [None] * num_layers
         self._waited = {}                 # stream -> the chunk event it last waited on
 
     def prepare(self, batch: int, user, ids, k: int, block_table, max_blocks: int, start_pos,
                 layers: Optional[Sequence[int]] = None,
-                chunks: Optional[Sequence["tuple[int, int]"]] = None) -> List["tuple[tuple, fs.Prepared]"]:
+                chunks: Optional[Sequence["tuple[int, int]"]] = None,
+                planned: bool = False) -> List["tuple[tuple, fs.Prepared]"]:
         """Marshal the calls once (validated like fs_inject), for batches that
         reuse the same buffers.  ``chunks``: consecutive (begin, end) layer
         ranges, each one fs_inject_layers launch; default one per layer (of
-        ``layers``, default all)."""
+        ``layers``, default all).  ``planned``: the batch is composed and
+        validated once into a plan of its own (fs_plan_inject, the first
+        launch), and every chunk injects from it (fs_inject_planned) instead
+        of planning again."""
         if chunks is None:
             ls = range(self.num_layers) if layers is None else layers
             chunks = [(l, l + 1) for l in ls]
         out = []
+        plan = None
+        if planned:
+            plan = fs.new_inject_plan(self.store, batch)
+            out.append(((0, 0), fs.prepare_plan_inject(self.store, batch, user, ids, k, block_table, max_blocks,
+                                                       start_pos, self.caches.num_blocks, plan,
+                                                       stream=self.stream)))
         for b, e in chunks:
             if not 0 <= b < e <= self.num_layers:
                 raise ValueError(f"layer chunk ({b}, {e}) outside [0, {self.num_layers})")
-            lay = b if e == b + 1 else (b, e)
-            out.append(((b, e), fs.prepare_inject(self.store, lay, batch, user, ids, k, block_table,
-                                                  max_blocks, start_pos, self.caches, stream=self.stream)))
+            if planned:
+                call = fs.prepare_inject_planned(self.store, (b, e), batch, k, plan, self.caches,
+                                                 stream=self.stream)
+            else:
+                lay = b if e == b + 1 else (b, e)
+                call = fs.prepare_inject(self.store, lay, batch, user, ids, k, block_table,
+                                         max_blocks, start_pos, self.caches, stream=self.stream)
+            out.append(((b, e), call))
         return out
 
     def launch(self, calls, after: Optional[torch.cuda.Stream] = None):

@@ -25,9 +25,10 @@ def _bits(t):
     return t.view(torch.int16)
 
 
+@pytest.mark.parametrize("planned", [False, True], ids=["fused", "planned"])
 @pytest.mark.parametrize("chunks", [None, [(0, 1), (1, 4)], [(0, 2), (2, 3), (3, 4)], [(0, 4)]],
                          ids=["per-layer", "first-then-rest", "uneven", "one-launch"])
-def test_layer_injector_under_forward_matches_all_layer_inject(chunks):
+def test_layer_injector_under_forward_matches_all_layer_inject(chunks, planned):
     wl = synth.make_workload("llama", seed=1003)
     s = wl.shape
     layers = [0, 1, 2, 3]
@@ -43,7 +44,8 @@ def test_layer_injector_under_forward_matches_all_layer_inject(chunks):
     kc, vc = synth.make_caches(wl, layers, "cuda")
     caches = fs.CacheTable(ds.store, kc, vc, kc[0].shape[0])
     inj = LayerInjector(ds.store, caches, len(layers))
-    calls = inj.prepare(B, req["user"], ids, k, req["block_table"], mb, req["start_pos"], chunks=chunks)
+    calls = inj.prepare(B, req["user"], ids, k, req["block_table"], mb, req["start_pos"], chunks=chunks,
+                        planned=planned)
     with pytest.raises(fs.FsError):                       # a range past the store's layers
         fs.fs_inject_layers(ds.store, 2, 5, B, req["user"], ids, k, req["block_table"], mb,
                             req["start_pos"], caches)
@@ -51,7 +53,7 @@ def test_layer_injector_under_forward_matches_all_layer_inject(chunks):
     g.manual_seed(5)
     x = torch.randn((256, 1024), generator=g, device="cuda")
     w = torch.randn((1024, 1024), generator=g, device="cuda") * 0.03
-    say(f"layer pipeline: inject on the side stream under a stand-in forward, chunks {chunks}")
+    say(f"layer pipeline: inject on the side stream under a stand-in forward, chunks {chunks}, planned {planned}")
     inj.launch(calls)
     for l in layers:
         inj.wait(l)
