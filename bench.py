@@ -750,13 +750,19 @@ def bench_pinned(args):
 
 
 def inject_source_digest() -> str:
-    """sha256 over the sources of the inject kernel (counters taken on another
-    build of it no longer describe it)."""
+    """sha256 over the code of the inject kernel's sources, comments and
+    whitespace removed (counters taken on other code no longer describe it;
+    a comment does not change the kernel)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ("inject.hip", "fs_internal.h", "fs_device.h"):
-        with open(os.path.join(ROOT, "kv_cache_injection_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "kv_cache_injection_amd", "csrc", f)) as fh:
+            text = fh.read()
+        # string literals are kept whole; // and /* */ comments go
+        text = re.sub(r'("(?:\\.|[^"\\])*")|//[^\n]*|/\*.*?\*/',
+                      lambda m: m.group(1) or " ", text, flags=re.S)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

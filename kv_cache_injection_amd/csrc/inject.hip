@@ -26,7 +26,10 @@
 // Pinned-host stores: a plan kernel (one block per request) validates each
 // request, including that every layer's staging slot holds its ids, and
 // writes a token map (arena row and cache slot of every segment token); the
-// inject kernel then reads the staged rows through that map.  The fetch
+// inject kernel then reads the staged rows through that map.  Device stores
+// can take the same two steps with the map in a caller-owned plan
+// (fs_plan_inject, fs_inject_planned): the injecting blocks then read their
+// rows and slots instead of planning.  The fetch
 // kernel fills the staging ring from host memory beforehand (fs_fetch_async),
 // one wave per group of tokens, copying one whole token row per instruction
 // pair so that the host link sees large contiguous reads.
