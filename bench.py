@@ -22,7 +22,13 @@ Prints ONE JSON line:
   roofline    the inject kernel: its algorithmic bytes per launch over its
               average launch time (HIP events on the launch stream around the
               steps' injects issued back to back), against 8 TB/s
-  cpu_baseline  the CPU oracle on a bounded sample of the same workload
+  kernels_ms  average launch times of the retrieval, the inject, and beside
+              them the plan kernel and the inject from a plan
+              (fs_plan_inject, fs_inject_planned), each issued back to back
+  inject_cold each inject alone after a 1 GiB write that evicts the MALL and
+              L2 (median, p10, p90)
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload, on
+              one thread and on all given cores
 
 Algorithmic bytes: inject = 8 * L * layers * heads * head_dim (K and V, bf16,
 read once and written once) per request of segment length L; retrieval =
