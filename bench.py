@@ -19,6 +19,7 @@ one after the other.
 
 Prints ONE JSON line:
   value       whole-step algorithmic HBM bytes / step time (GB/s)
+  injected_payload_GBps  the K and V bytes landed in the caches / step time
   roofline    the inject kernel: its algorithmic bytes per launch over its
               average launch time (HIP events on the launch stream around the
               steps' injects issued back to back), against 8 TB/s
@@ -288,6 +289,7 @@ def main():
         "dtype": "f64",
         "data": "synthetic",
         "requests_per_s": round(B * args.steps / wall, 1),
+        "injected_payload_GBps": round(float(inject_bytes.sum() / 2 / wall / 1e9), 2),
         "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "config": {
             "workload": f"{s.name}: {nl} layers x {s.num_kv_heads} KV heads x head_dim {s.head_dim}, "
