@@ -40,7 +40,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <type_traits>
 
 #include "fs_device.h"
 #include "fs_internal.h"
@@ -55,24 +54,13 @@ using fsd::wave_or;
 constexpr int kThreads = 64;        // one wave per fetch block
 constexpr int kInjectThreads = 256; // 4 waves per inject block
 constexpr int kInjectOcc = 6;       // waves per SIMD the register budget allows
-// a launch whose output may exceed this streams its cache writes past the
-// 256 MB last-level cache (non-temporal stores)
-constexpr double kStreamStoreBytes = 1024.0 * 1024.0 * 1024.0;
 constexpr int kPlanThreads = 1024;
 
 #define FS_GLOBAL __attribute__((address_space(1)))
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 ld_stream(const FS_GLOBAL u32x4* p) { return __builtin_nontemporal_load(p); }
-// Cache writes: non-temporal (streamed past the 256 MB last-level cache) for
-// launches whose output could not stay in it, plain (write-back, allocated
-// in the last-level cache) otherwise: the write-back of one launch's output
-// then overlaps the next launch's reads, and its consumer finds it there.
-template <bool kStream>
-__device__ __forceinline__ void st_cache(FS_GLOBAL u32x4* p, u32x4 v) {
-    if constexpr (kStream) __builtin_nontemporal_store(v, p);
-    else *p = v;
-}
+__device__ __forceinline__ void st_stream(FS_GLOBAL u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
 struct PlanArgs {
     const int32_t* user;
@@ -356,7 +344,7 @@ __global__ __launch_bounds__(kPlanThreads) void fs_plan_kernel(PlanArgs a) {
 //
 // kPlanned = true (pinned stores): the plan kernel has validated the request
 // (including every layer's staging slot) and written the token map.
-template <int D, bool kPlanned, bool kStream>
+template <int D, bool kPlanned>
 __global__ __launch_bounds__(kInjectThreads, kInjectOcc) void fs_inject_kernel(InjectArgs a, PlanArgs pa) {
     constexpr int kTeam = D / 16;            // lanes per token
     constexpr int kTok = 64 / kTeam;         // tokens per group
@@ -483,10 +471,10 @@ __global__ __launch_bounds__(kInjectThreads, kInjectOcc) void fs_inject_kernel(I
         const int o = h * (D / 8) + tl;
         u32x4 ya, yb;
         rot_v(ka, kb, c, sn, ya, yb);
-        st_cache<kStream>(kd + o, ya);
-        st_cache<kStream>(kd + o + kHalf, yb);
-        st_cache<kStream>(vd + o, va);
-        st_cache<kStream>(vd + o + kHalf, vb);
+        st_stream(kd + o, ya);
+        st_stream(kd + o + kHalf, yb);
+        st_stream(vd + o, va);
+        st_stream(vd + o + kHalf, vb);
     }
 }
 
@@ -654,18 +642,6 @@ hipError_t launch_inject(const InjectLaunch& r) {
     const int64_t groups = std::max<int64_t>(1, (int64_t(r.k) * st->max_fact_len + kTok - 1) / kTok);
     const dim3 grid(static_cast<unsigned>(groups), static_cast<unsigned>(r.batch),
                     static_cast<unsigned>(r.layer_end - r.layer_begin));
-    // the launch's largest possible output (K and V of the longest segments)
-    // against the last-level cache: plain stores while it fits with room to
-    // spare, non-temporal above
-    const double out_bound = 4.0 * double(groups) * kTok * double(r.batch) * double(r.layer_end - r.layer_begin) *
-                             double(d.num_kv_heads) * double(D);
-    const bool stream = out_bound > double(kStreamStoreBytes);
-    auto inject = [&](auto planned, size_t lds) {
-        if (stream)
-            fs_inject_kernel<D, decltype(planned)::value, true><<<grid, kInjectThreads, lds, r.stream>>>(a, pa);
-        else
-            fs_inject_kernel<D, decltype(planned)::value, false><<<grid, kInjectThreads, lds, r.stream>>>(a, pa);
-    };
     if (r.plan_in) {
         // inject from the caller's plan: the blocks read their tokens' rows
         // and slots instead of planning
@@ -674,14 +650,14 @@ hipError_t launch_inject(const InjectLaunch& r) {
         a.tok_src = v.tok_src;
         a.tok_dst = v.tok_dst;
         a.req_len = v.req_len;
-        inject(std::true_type{}, 0);
+        fs_inject_kernel<D, true><<<grid, kInjectThreads, 0, r.stream>>>(a, pa);
     } else if (d.kv_location == FS_KV_PINNED_HOST) {
         fs_plan_kernel<<<dim3(r.batch), kPlanThreads, plan_lds, r.stream>>>(pa);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        inject(std::true_type{}, 0);
+        fs_inject_kernel<D, true><<<grid, kInjectThreads, 0, r.stream>>>(a, pa);
     } else {
-        inject(std::false_type{}, plan_lds);
+        fs_inject_kernel<D, false><<<grid, kInjectThreads, plan_lds, r.stream>>>(a, pa);
     }
     return hipGetLastError();
 }
