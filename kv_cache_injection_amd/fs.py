@@ -329,10 +329,16 @@ def prepare_plan_inject(store, batch: int, user, ids, k: int, block_table, max_b
 
 def prepare_inject_planned(store, layers, batch: int, k: int, plan: torch.Tensor,
                            caches: "CacheTable", stream=None) -> Prepared:
-    """fs_inject_planned over ``layers`` (FS_ALL_LAYERS or a (begin, end) pair)."""
+    """fs_inject_planned over ``layers``: FS_ALL_LAYERS, one layer, or a
+    (begin, end) pair."""
     if not isinstance(caches, CacheTable):
         raise TypeError("prepare_inject_planned takes a CacheTable")
-    lb, le = (0, len(caches.present)) if layers == FS_ALL_LAYERS else (int(layers[0]), int(layers[1]))
+    if isinstance(layers, tuple):
+        lb, le = int(layers[0]), int(layers[1])
+    elif int(layers) == FS_ALL_LAYERS:
+        lb, le = 0, len(caches.present)
+    else:
+        lb, le = int(layers), int(layers) + 1
     if 0 <= lb < le <= len(caches.present) and not all(caches.present[lb:le]):
         raise ValueError(f"no cache given for some layer of [{lb}, {le})")
     args = (_handle(store), lb, le, int(batch), int(k), _ptr(plan, torch.uint8, name="plan"),
