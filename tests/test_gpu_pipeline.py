@@ -206,8 +206,8 @@ def test_planned_inject_equals_fused_inject():
         if i == 0:
             fs.fs_inject_planned(ds.store, fs.FS_ALL_LAYERS, B, k, plan, tb)
         else:
-            fs.fs_inject_planned(ds.store, (0, 1), B, k, plan, tb)
-            fs.fs_inject_planned(ds.store, (1, 4), B, k, plan, tb)
+            fs.fs_inject_planned(ds.store, 0, B, k, plan, tb)          # one layer
+            fs.fs_inject_planned(ds.store, (1, 4), B, k, plan, tb)     # a range
         torch.cuda.synchronize()
         for l in range(len(layers)):
             assert torch.equal(_bits(kc[l]), _bits(rk[l])), f"set {i} layer {l} K"
