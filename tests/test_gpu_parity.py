@@ -502,4 +502,10 @@ def test_pinned_host_store_fetch_then_inject():
                  wl.block_table.shape[1], req["start_pos"], kc, vc, nb)
     assert fs.fs_poll_errors(ds.store) == fs.FS_ERR_STAGING
     assert torch.equal(before_k.view(torch.int16), kc[0].view(torch.int16))
+    # caller-owned plans are for device stores
+    plan = fs.new_inject_plan(ds.store, B)
+    with pytest.raises(fs.FsError) as e:
+        fs.fs_plan_inject(ds.store, B, req["user"], ids, k, req["block_table"], wl.block_table.shape[1],
+                          req["start_pos"], nb, plan)
+    assert e.value.status == fs.FS_E_UNSUPPORTED
     ds.close()
