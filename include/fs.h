@@ -30,15 +30,21 @@
  *     that point.
  *   - Concurrency on one store (not detected): fs_retrieve_topk calls share
  *     the score scratch, so they must not overlap one another; on pinned
- *     stores fs_inject calls share the token-map scratch and the staging
- *     ring, so they must not overlap one another or an fs_fetch_async.  On
- *     device stores fs_inject uses no scratch, so one stream may inject
- *     while another retrieves for a later request (the caller orders each
- *     inject after the retrieval that produced its ids, e.g. with an event),
- *     and injects on different streams may overlap when they write disjoint
- *     cache blocks.  Several stores may be created over the same arenas and
- *     embeddings (each with its own scratch, e.g. one per stream) while none
- *     of them ingests or evicts: each keeps its own copy of the metadata.
+ *     stores fs_inject calls share the plan scratch and the staging ring, so
+ *     they must not overlap one another or an fs_fetch_async.  On device
+ *     stores each fs_inject call composes its plan into one of the store's
+ *     plan slots (FS_PLAN_SLOTS of them): a slot goes back to the stream that
+ *     used it last with no synchronisation (stream order protects it), and
+ *     to another stream only after that stream waits, on the device, for the
+ *     slot's last use.  So one stream may inject while another retrieves for
+ *     a later request (the caller orders each inject after the retrieval
+ *     that produced its ids, e.g. with an event), and injects on up to
+ *     FS_PLAN_SLOTS streams run side by side when they write disjoint cache
+ *     blocks.  The slot choice is guarded by a mutex, so host threads may
+ *     call fs_inject on one store.  Several stores may be created over the
+ *     same arenas and embeddings (each with its own scratch, e.g. one per
+ *     stream) while none of them ingests or evicts: each keeps its own copy
+ *     of the metadata.
  *   - Errors: a call returns a status.  Host-checkable errors return before
  *     anything is enqueued and nothing is written.  Conditions only the GPU
  *     can see set bits in the store's device error word (fs_poll_errors) and
@@ -98,10 +104,16 @@ typedef int32_t fs_status;
 #define FS_ERR_BLOCK_ID    0x10u  /* a used block id outside [0, num_blocks)       */
 #define FS_ERR_STAGING     0x20u  /* pinned store: inject ids differ from the ids
                                      the staging slot was fetched for              */
+#define FS_ERR_PLAN        0x40u  /* fs_inject_planned: the plan was not written by
+                                     fs_plan_inject of this store for this batch
+                                     and k, or was checked against more cache
+                                     blocks than the caches hold; nothing is
+                                     written from it                               */
 
 #define FS_ALL_LAYERS      (-1)
 #define FS_MAX_LAYERS      128
 #define FS_MAX_K           1024
+#define FS_PLAN_SLOTS      4      /* fs_inject plan slots per device store     */
 
 #define FS_KV_DEVICE       0      /* K/V arenas in device memory              */
 #define FS_KV_PINNED_HOST  1      /* K/V arenas in page-locked host memory    */
@@ -202,6 +214,10 @@ FS_API fs_status fs_retrieve_topk(const fs_store* store, int32_t batch,
  *   V cache (same address) = v[l][row(t)][h]            (bytes, unchanged)
  * Every other cache byte is left untouched.
  *
+ * Enqueues two kernels on `stream`: the plan (composition and validation of
+ * every request, one small block each) into a plan slot of the store, then
+ * the injection, which streams K and V rows through that plan.
+ *
  *   layer        0 .. num_layers-1, or FS_ALL_LAYERS
  *   batch        1 .. max_batch
  *   user         device int32 [batch]; ids must belong to the request's user
@@ -230,9 +246,10 @@ FS_API fs_status fs_inject(const fs_store* store, int32_t layer, int32_t batch,
 
 /*
  * fs_inject_layers — fs_inject over the layers [layer_begin, layer_end) in
- * one launch (same passages, same per-layer result, same checks and errors).
- * A layer-pipelined caller injects the first layers alone and the rest in
- * larger chunks: one launch per chunk instead of one per layer.
+ * one call (one plan, one inject launch; same passages, same per-layer
+ * result, same checks and errors).  A layer-pipelined caller injects the
+ * first layers alone and the rest in larger chunks: one call per chunk
+ * instead of one per layer.
  *   0 <= layer_begin < layer_end <= num_layers, else FS_E_RANGE.  On pinned
  *   stores every layer of the range reads its own staging slot, so the range
  *   spans at most staging_layers layers (FS_ERR_STAGING otherwise).
@@ -245,19 +262,18 @@ FS_API fs_status fs_inject_layers(const fs_store* store, int32_t layer_begin, in
                            int32_t num_blocks, void* stream);
 
 /*
- * fs_plan_inject, fs_inject_planned — fs_inject in two calls, with the
- * composition and validation (the segment of ids[b] laid from start_pos[b],
- * same passages as fs_inject) written once into a caller-owned plan instead
- * of being recomputed by the injecting blocks.  A serving loop plans request
- * i + 1 (a small launch, one block per request) while request i injects on
- * another stream, and each inject then starts moving bytes at once.  The
- * result of fs_plan_inject followed by fs_inject_planned equals fs_inject_layers
- * with the same arguments, bit for bit.  Device stores only
- * (FS_E_UNSUPPORTED otherwise).
+ * fs_plan_inject, fs_inject_planned — fs_inject's two kernels as two calls,
+ * with the plan (the segment of ids[b] laid from start_pos[b], validated;
+ * same passages as fs_inject) in a buffer the caller owns.  A serving loop
+ * plans request i + 1 while request i injects, and one plan serves any
+ * number of layer ranges (a layer-pipelined forward).  fs_plan_inject
+ * followed by fs_inject_planned writes exactly what fs_inject_layers writes
+ * with the same arguments.  Device stores only (FS_E_UNSUPPORTED otherwise).
  *
  * fs_inject_plan_size: bytes of a plan for `batch` requests (1 .. max_batch).
- * The plan holds per request its segment length (0 when rejected) and start
- * position, and every segment token's arena row and cache slot.
+ * The plan holds a header (this store, batch, k and the num_blocks it was
+ * checked against), per request its segment length (0 when rejected) and
+ * start position, and every segment token's arena row and cache slot.
  *
  * fs_plan_inject: arguments as fs_inject's; plan is device memory of at least
  *   fs_inject_plan_size(batch) bytes, 16-byte aligned (else FS_E_RANGE /
@@ -268,10 +284,16 @@ FS_API fs_status fs_inject_layers(const fs_store* store, int32_t layer_begin, in
  *
  * fs_inject_planned: the layers [layer_begin, layer_end) from a plan that
  *   fs_plan_inject wrote earlier in stream order (or after an event) with the
- *   same batch and k; k_cache and v_cache as fs_inject's, each holding at
- *   least the num_blocks the plan was checked against.  A plan may be used
- *   for any number of layer ranges; it must not be rewritten while an inject
- *   reads it.  Errors: FS_E_ARG, FS_E_RANGE, FS_E_UNSUPPORTED, FS_E_HIP.
+ *   same batch and k; k_cache and v_cache as fs_inject's, each holding
+ *   num_blocks blocks.  Device-checked: a plan whose header does not name
+ *   this store, batch and k, or that was checked against more than
+ *   num_blocks blocks (including a buffer fs_plan_inject never wrote), sets
+ *   FS_ERR_PLAN and writes nothing; every row the inject touches is also
+ *   bounds-checked against the arenas and caches (FS_ERR_PLAN).  A plan may
+ *   be used for any number of layer ranges; it must not be rewritten while
+ *   an inject reads it, and a plan of earlier requests stays valid for them
+ *   only (the caller's responsibility).  Errors: FS_E_ARG, FS_E_RANGE,
+ *   FS_E_BLOCKTABLE, FS_E_UNSUPPORTED, FS_E_HIP.
  */
 FS_API fs_status fs_inject_plan_size(const fs_store* store, int32_t batch, size_t* bytes);
 FS_API fs_status fs_plan_inject(const fs_store* store, int32_t batch, const int32_t* user,
@@ -280,7 +302,8 @@ FS_API fs_status fs_plan_inject(const fs_store* store, int32_t batch, const int3
                                 void* plan, size_t plan_bytes, void* stream);
 FS_API fs_status fs_inject_planned(const fs_store* store, int32_t layer_begin, int32_t layer_end,
                                    int32_t batch, int32_t k, const void* plan, size_t plan_bytes,
-                                   void* const* k_cache, void* const* v_cache, void* stream);
+                                   void* const* k_cache, void* const* v_cache, int32_t num_blocks,
+                                   void* stream);
 
 /*
  * fs_fetch_async — host-DRAM offload (gist.science summary, "Résultats":

@@ -92,12 +92,6 @@ constexpr int kBtCache = 1024;        // block-table entries a block caches in L
 constexpr unsigned kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters untouched
 constexpr int kMaxSplits = 16;
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
-    uint32_t u = __float_as_uint(x);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
-}
-
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
 __device__ __forceinline__ __bf16 as_bf16(uint16_t h) {
@@ -182,7 +176,6 @@ __global__ __launch_bounds__(kThreads, 2) void fs_attend_kernel(AttendArgs a) {
     const int grp = lane >> 4;        // 4-row group of the MFMA layouts
     const int c0 = a.ctx_begin[b];
     const int qp0 = a.q_pos[b];
-    const int64_t bs_mask = (int64_t(1) << a.log2_block) - 1;
     const int32_t* bt = a.bt + int64_t(b) * a.max_blocks;
     const int jb = qt * kBQ;          // the block's first query
     const int j_lo = jb + qs * kQT;   // the wave's first query

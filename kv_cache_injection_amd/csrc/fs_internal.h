@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "fs.h"
@@ -31,6 +32,7 @@ struct fs_store {
     int device = 0;
     int32_t num_cus = 0;          // compute units of the device (inject grid sizing)
     int32_t max_fact_len = 0;     // longest fact, tokens
+    double mean_fact_len = 0;     // mean fact length at creation (inject grid sizing)
     int32_t seg_tokens = 0;       // max_k * max_fact_len: longest possible segment
     int32_t max_user_facts = 0;   // largest user, facts
     int32_t log2_block = 0;
@@ -50,10 +52,25 @@ struct fs_store {
     int32_t* d_tk_counts = nullptr;    // [max_batch]
     const void** d_src_k = nullptr;    // [L] device-visible arena pointers
     const void** d_src_v = nullptr;
-    // inject plan scratch (written by the plan kernel, read by the inject kernel)
-    int64_t* d_tok_src = nullptr;      // [max_batch][seg_tokens] arena row of segment token t
-    int64_t* d_tok_dst = nullptr;      // [max_batch][seg_tokens] cache slot (block*bs + slot)
-    int32_t* d_req_len = nullptr;      // [max_batch] segment length, 0 if rejected
+    const void** d_src_kv = nullptr;   // [L][2]: the same, K then V of each layer
+    // identity written into every plan header this store makes (plans are
+    // refused by another store)
+    uint32_t tag = 0;
+    // fs_inject's plan slots: each call composes its plan into a slot and
+    // injects from it.  A slot is reused by the stream that used it last
+    // without any synchronisation (stream order); handing it to another
+    // stream first makes that stream wait for an event recorded on the last
+    // one.  Pinned stores use slot 0 only (their calls must not overlap).
+    struct PlanSlot {
+        void* buf = nullptr;                 // fsi_plan_bytes(max_batch) bytes
+        hipStream_t last = nullptr;          // stream of the last call that used it
+        bool used = false;
+        uint64_t stamp = 0;                  // last use (LRU choice)
+        hipEvent_t ev = nullptr;             // recorded on `last` when the slot changes streams
+    };
+    mutable std::vector<PlanSlot> slots;
+    mutable std::mutex slot_mu;
+    mutable uint64_t slot_clock = 0;
 
     // pinned stores: staging ring
     int32_t stage_tokens = 0;          // max_k * max_fact_len
@@ -107,32 +124,65 @@ struct InjectLaunch {
     void* const* v_cache;
     int32_t num_blocks;
     hipStream_t stream;
-    // caller-owned plans (device stores): plan_out set = compose and
-    // validate into it and launch nothing else; plan_in set = inject from it
-    // (user, ids, block_table, start_pos unused)
+    // plan_out set: compose and validate into it (and inject from it when
+    // inject is set); plan_in set: inject from it (user, ids, block_table,
+    // start_pos unused)
     void* plan_out = nullptr;
     const void* plan_in = nullptr;
+    bool inject = false;
 };
 hipError_t fsi_launch_inject(const InjectLaunch& a);
 
-// Layout of a caller-owned inject plan for `batch` requests: segment length
-// (0 if rejected) and start position per request, padded to 16 bytes, then
-// each segment token's arena row and cache slot, seg_tokens per request.
-struct PlanView {
-    int32_t* req_len;
-    int32_t* start;
-    int64_t* tok_src;
-    int64_t* tok_dst;
+// Layout of an inject plan for `batch` requests:
+//   PlanHeader (32 bytes); then per request {segment length (0 when
+//   rejected), start position} as two int32 (padded to 16 bytes); then per
+//   request seg_tokens entries {arena row, cache slot (block * block_size +
+//   slot)} as two int64.  Each request's pair and each token's pair is one
+//   scalar load for the injecting kernel.
+constexpr uint32_t kPlanMagic = 0x4E414C50u;   // "PLAN"
+struct PlanHeader {
+    uint64_t key;          // fsi_plan_key of the call that wrote it
+    uint32_t magic;
+    uint32_t tag;          // fs_store::tag of the store that wrote it
+    int32_t batch, k, seg_tokens;
+    int32_t num_blocks;    // the cache size the block ids were checked against
 };
-inline size_t fsi_plan_header_bytes(int32_t batch) { return (size_t(batch) * 8 + 15) / 16 * 16; }
+static_assert(sizeof(PlanHeader) == 32, "plan header is 32 bytes");
+struct PlanReq {
+    int32_t len, start;
+};
+struct PlanTok {
+    int64_t src, dst;
+};
+struct PlanView {
+    PlanHeader* hdr;
+    PlanReq* req;
+    PlanTok* tok;          // [batch][seg_tokens]
+};
+inline size_t fsi_plan_header_bytes(int32_t batch) {
+    return sizeof(PlanHeader) + (size_t(batch) * sizeof(PlanReq) + 15) / 16 * 16;
+}
 inline size_t fsi_plan_bytes(const fs_store* st, int32_t batch) {
-    return fsi_plan_header_bytes(batch) + 2 * sizeof(int64_t) * size_t(batch) * size_t(st->seg_tokens);
+    return fsi_plan_header_bytes(batch) + sizeof(PlanTok) * size_t(batch) * size_t(st->seg_tokens);
 }
 inline PlanView fsi_plan_view(const fs_store* st, int32_t batch, const void* plan) {
+    (void)st;
     char* p = static_cast<char*>(const_cast<void*>(plan));
-    int64_t* rows = reinterpret_cast<int64_t*>(p + fsi_plan_header_bytes(batch));
-    const size_t n = size_t(batch) * size_t(st->seg_tokens);
-    return PlanView{reinterpret_cast<int32_t*>(p), reinterpret_cast<int32_t*>(p) + batch, rows, rows + n};
+    return PlanView{reinterpret_cast<PlanHeader*>(p), reinterpret_cast<PlanReq*>(p + sizeof(PlanHeader)),
+                    reinterpret_cast<PlanTok*>(p + fsi_plan_header_bytes(batch))};
+}
+// A 64-bit identity of (store, batch, k, segment bound, cache size): the plan
+// kernel writes the key of its call, the inject kernel compares it with the
+// key of its own call (FNV-1a over the six words)
+inline uint64_t fsi_plan_key(uint32_t tag, int32_t batch, int32_t k, int32_t seg_tokens, int32_t num_blocks) {
+    const uint32_t w[6] = {kPlanMagic, tag, uint32_t(batch), uint32_t(k), uint32_t(seg_tokens), uint32_t(num_blocks)};
+    uint64_t h = 0xcbf29ce484222325ull;
+    for (uint32_t x : w)
+        for (int byte = 0; byte < 4; ++byte) {
+            h ^= (x >> (8 * byte)) & 0xFFu;
+            h *= 0x100000001b3ull;
+        }
+    return h;
 }
 
 constexpr size_t kZeroRowBytes = 512;

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -47,15 +48,47 @@ void free_store(fs_store* s) {
     void* bufs[] = {s->d_fact_begin, s->d_fact_len, s->d_user_begin, s->d_user_count,
                     s->d_ingest_items, s->d_inv_freq, s->d_zero_row, s->d_err,
                     s->d_scores, s->d_tk_ids, s->d_tk_scores, s->d_tk_counts,
-                    (void*)s->d_src_k, (void*)s->d_src_v, s->d_tok_src,
-                    s->d_tok_dst, s->d_req_len, s->d_stage_k,
+                    (void*)s->d_src_k, (void*)s->d_src_v, (void*)s->d_src_kv, s->d_stage_k,
                     s->d_stage_v, s->d_stage_ids, s->d_stage_meta};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
+    for (auto& sl : s->slots) {
+        if (sl.buf) (void)hipFree(sl.buf);
+        if (sl.ev) (void)hipEventDestroy(sl.ev);
+    }
     if (s->ingest_copied) (void)hipEventDestroy(s->ingest_copied);
     if (s->h_ingest_items) (void)hipHostFree(s->h_ingest_items);
     if (s->h_ingest_counts) (void)hipHostFree(s->h_ingest_counts);
     delete s;
+}
+
+// A plan slot for one fs_inject call on stream s (caller holds slot_mu):
+// the slot this stream used last, else an unused one, else the least
+// recently used one, after making s wait for that slot's last use.
+void* acquire_slot(const fs_store* st, hipStream_t s, hipError_t* err) {
+    auto& slots = st->slots;
+    int pick = -1;
+    for (size_t i = 0; i < slots.size() && pick < 0; ++i)
+        if (slots[i].used && slots[i].last == s) pick = static_cast<int>(i);
+    for (size_t i = 0; i < slots.size() && pick < 0; ++i)
+        if (!slots[i].used) pick = static_cast<int>(i);
+    if (pick < 0) {
+        pick = 0;
+        for (size_t i = 1; i < slots.size(); ++i)
+            if (slots[i].stamp < slots[pick].stamp) pick = static_cast<int>(i);
+        fs_store::PlanSlot& sl = slots[pick];
+        hipError_t e = hipEventRecord(sl.ev, sl.last);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s, sl.ev, 0);
+        if (e != hipSuccess) {
+            *err = e;
+            return nullptr;
+        }
+    }
+    fs_store::PlanSlot& sl = slots[pick];
+    sl.used = true;
+    sl.last = s;
+    sl.stamp = ++st->slot_clock;
+    return sl.buf;
 }
 
 fs_status check_desc(const fs_store_desc* d) {
@@ -149,6 +182,7 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
     if (!st) return fail(FS_E_NOMEM, "host allocation failed");
     st->desc = d;
     st->max_fact_len = max_len;
+    st->mean_fact_len = double(total) / double(d.num_facts);
     st->max_user_facts = static_cast<int32_t>(max_user);
     st->log2_block = ilog2(d.block_size);
     st->emb = emb;
@@ -220,9 +254,7 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
         {(void**)&st->d_tk_counts, sizeof(int32_t) * size_t(d.max_batch), "top-k chunk scratch"},
         {(void**)&st->d_src_k, sizeof(void*) * d.num_layers, "arena table"},
         {(void**)&st->d_src_v, sizeof(void*) * d.num_layers, "arena table"},
-        {(void**)&st->d_tok_src, sizeof(int64_t) * size_t(d.max_batch) * size_t(st->seg_tokens), "segment plan"},
-        {(void**)&st->d_tok_dst, sizeof(int64_t) * size_t(d.max_batch) * size_t(st->seg_tokens), "segment plan"},
-        {(void**)&st->d_req_len, sizeof(int32_t) * size_t(d.max_batch), "segment plan"},
+        {(void**)&st->d_src_kv, 2 * sizeof(void*) * d.num_layers, "arena table"},
     };
     for (auto& a : allocs) {
         e = hipMalloc(a.p, a.bytes);
@@ -231,6 +263,23 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
             free_store(st);
             return fail(FS_E_NOMEM, "hipMalloc(%s, %zu bytes): %s", a.what, a.bytes, hipGetErrorString(e));
         }
+    }
+    // plan slots of fs_inject (pinned stores: one, their calls never overlap)
+    st->slots.resize(pinned ? 1 : FS_PLAN_SLOTS);
+    for (auto& sl : st->slots) {
+        e = hipMalloc(&sl.buf, fsi_plan_bytes(st, d.max_batch));
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            free_store(st);
+            return fail(FS_E_NOMEM, "plan slot (%zu bytes): %s", fsi_plan_bytes(st, d.max_batch),
+                        hipGetErrorString(e));
+        }
+    }
+    {
+        // a process-unique identity for the plans this store writes
+        static std::atomic<uint32_t> next_tag{0x2545F491u};
+        st->tag = next_tag.fetch_add(0x9E3779B9u);
     }
     if (pinned) {
         st->stage_tokens = st->seg_tokens;
@@ -257,6 +306,11 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
     st->h_fact_begin.assign(fb.begin(), fb.end() - 1);
     st->h_fact_len.assign(fact_len, fact_len + d.num_facts);
     st->next_row = total;                     // rows past the facts are free for ingest
+    std::vector<const void*> src_kv(2 * size_t(d.num_layers));
+    for (int l = 0; l < d.num_layers; ++l) {
+        src_kv[2 * l] = st->src_k[l];
+        src_kv[2 * l + 1] = st->src_v[l];
+    }
     std::vector<int32_t> meta_init(4 * size_t(pinned ? d.staging_layers : 0), -1);
     uint32_t zero = 0;
     const std::vector<unsigned char> zero_row(kZeroRowBytes, 0);
@@ -270,6 +324,7 @@ fs_status fs_create_store(const fs_store_desc* desc, const int64_t* user_fact_be
         {st->d_zero_row, zero_row.data(), kZeroRowBytes},
         {(void*)st->d_src_k, st->src_k.data(), sizeof(void*) * d.num_layers},
         {(void*)st->d_src_v, st->src_v.data(), sizeof(void*) * d.num_layers},
+        {(void*)st->d_src_kv, src_kv.data(), 2 * sizeof(void*) * d.num_layers},
         {st->d_stage_meta, meta_init.data(), sizeof(int32_t) * meta_init.size()},
     };
     for (auto& c : cps) {
@@ -341,9 +396,17 @@ fs_status fs_inject_layers(const fs_store* store, int32_t layer_begin, int32_t l
             return fail(FS_E_ARG, "layer %d cache not 16-byte aligned", l);
     }
     if (k == 0) return FS_OK;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     InjectLaunch a{store, layer_begin, layer_end, batch, user, ids, k, block_table, max_blocks, start_pos,
-                   k_cache, v_cache, num_blocks, reinterpret_cast<hipStream_t>(stream)};
-    hipError_t e = fsi_launch_inject(a);
+                   k_cache, v_cache, num_blocks, s};
+    a.inject = true;
+    // the slot stays locked until both kernels are enqueued, so no other
+    // call can hand it to another stream in between
+    std::lock_guard<std::mutex> lock(store->slot_mu);
+    hipError_t e = hipSuccess;
+    a.plan_out = acquire_slot(store, s, &e);
+    if (e != hipSuccess) return hip_fail(e, "plan slot hand-over");
+    e = fsi_launch_inject(a);
     if (e != hipSuccess) return hip_fail(e, "inject launch");
     return FS_OK;
 }
@@ -398,7 +461,7 @@ fs_status fs_plan_inject(const fs_store* store, int32_t batch, const int32_t* us
 
 fs_status fs_inject_planned(const fs_store* store, int32_t layer_begin, int32_t layer_end, int32_t batch, int32_t k,
                             const void* plan, size_t plan_bytes, void* const* k_cache, void* const* v_cache,
-                            void* stream) {
+                            int32_t num_blocks, void* stream) {
     g_msg[0] = 0;
     if (!store) return fail(FS_E_ARG, "null store");
     const fs_status c = check_plan(store, batch, k, plan, plan_bytes);
@@ -408,6 +471,7 @@ fs_status fs_inject_planned(const fs_store* store, int32_t layer_begin, int32_t 
         return fail(FS_E_RANGE, "layer range [%d, %d) invalid for %d layers", layer_begin, layer_end,
                     d.num_layers);
     if (!k_cache || !v_cache) return fail(FS_E_ARG, "null pointer argument");
+    if (num_blocks < 1) return fail(FS_E_BLOCKTABLE, "num_blocks %d < 1", num_blocks);
     for (int l = layer_begin; l < layer_end; ++l) {
         if (!k_cache[l] || !v_cache[l]) return fail(FS_E_ARG, "layer %d cache pointer is null", l);
         if (!aligned(k_cache[l], 16) || !aligned(v_cache[l], 16))
@@ -415,7 +479,7 @@ fs_status fs_inject_planned(const fs_store* store, int32_t layer_begin, int32_t 
     }
     if (k == 0) return FS_OK;
     InjectLaunch a{store, layer_begin, layer_end, batch, nullptr, nullptr, k, nullptr, 0, nullptr,
-                   k_cache, v_cache, 0, reinterpret_cast<hipStream_t>(stream)};
+                   k_cache, v_cache, num_blocks, reinterpret_cast<hipStream_t>(stream)};
     a.plan_in = plan;
     hipError_t e = fsi_launch_inject(a);
     if (e != hipSuccess) return hip_fail(e, "inject launch");

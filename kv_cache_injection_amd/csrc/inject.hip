@@ -1,41 +1,32 @@
-// Fused gather -> Chunked RoPE -> paged scatter, and the host-memory fetch.
+// Compose -> Chunked RoPE -> paged scatter, and the host-memory fetch.
 //
 // InferScale's online phase (gist.science summary, "Phase En-ligne"): keys
 // are stored before RoPE; at serving time the retrieved facts are composed
 // into one contiguous segment, every stored key is rotated to its new
 // serving-time position, and the composed K/V is scatter-copied into the
 // paged KV cache.  Values are copied raw.  The re-rotation is exact under
-// RoPE (Theorem 6 as the pages describe it), so the kernel evaluates the
-// rotation in fp64 and rounds once to bf16.
+// RoPE (Theorem 6 as the pages describe it), so the rotation is evaluated in
+// fp64 and rounded once to bf16.
 //
-// Device stores: one fs_inject call is one launch of the inject kernel, one
-// 256-thread block per (token group, request, layer).  Wave 0 plans the
-// request in LDS (prefix sums of the selected facts' lengths, ids checked
-// against the user) while the other waves evaluate cos/sin of p*w_i in fp64
-// for every (token, frequency) of the group, one sincos per entry; the first
-// K/V loads go out before the request's check (start position, block-table
-// coverage and entries) completes, and a rejected request writes nothing.  A
-// team of head_dim/16 lanes owns one token: lane tl holds the 8 rotate-half
-// pairs i = 8*tl .. 8*tl+7 (one 16-byte vector from each half of the head
-// row).  Each wave streams whole heads of the group: 4 non-temporal 16-byte
-// loads per lane, rotation of K, 4 non-temporal stores.  Thousands of small
-// blocks let the dispatcher keep every CU fed to the end of the launch (a
-// persistent grid with equal shares per CU finished later: the CUs do not
-// drain at the same rate).
+// Two kernels per injection:
 //
-// Pinned-host stores: a plan kernel (one block per request) validates each
-// request, including that every layer's staging slot holds its ids, and
-// writes a token map (arena row and cache slot of every segment token); the
-// inject kernel then reads the staged rows through that map.  Device stores
-// can take the same two steps with the map in a caller-owned plan
-// (fs_plan_inject, fs_inject_planned): the injecting blocks then read their
-// rows and slots instead of planning.  The fetch
-// kernel fills the staging ring from host memory beforehand (fs_fetch_async),
-// one wave per group of tokens, copying one whole token row per instruction
-// pair so that the host link sees large contiguous reads.
+// Plan (fs_plan_kernel, one block per request): composes the segment (prefix
+// sums of the selected facts' lengths, ids checked against the user),
+// validates the request (start position, block-table coverage and entries,
+// for pinned stores the staging slot) and writes a plan: a header naming the
+// store, batch, k and cache size it was checked for, the segment length (0
+// for a rejected request) and start position, and every segment token's
+// arena row and cache slot.
 //
-// HBM-bound copy with a small amount of arithmetic; no dense contraction, so
-// no MFMA.
+// Inject (fs_row_kernel, and fs_short_kernel for rows under 1 KB): a pure
+// stream over the plan.  Each 256-thread workgroup moves whole token rows of
+// K or of V (never both) for one request and layer, one 16-byte vector per
+// lane, read once and written once, so a workgroup carries 4 KB and the
+// launch holds tens of thousands of them.  K rows are rotated on the way
+// through with cos/sin evaluated in fp64 while the row is in flight.
+//
+// HBM-bound gather/copy with a small amount of arithmetic; no dense
+// contraction, so no MFMA.
 
 #include <hip/hip_runtime.h>
 
@@ -52,15 +43,25 @@ using fsd::f64_to_bf16_bits;
 using fsd::wave_or;
 
 constexpr int kThreads = 64;        // one wave per fetch block
-constexpr int kInjectThreads = 256; // 4 waves per inject block
-constexpr int kInjectOcc = 6;       // waves per SIMD the register budget allows
+constexpr int kFlatThreads = 256;   // 4 waves per inject workgroup
 constexpr int kPlanThreads = 1024;
 
 #define FS_GLOBAL __attribute__((address_space(1)))
+#define FS_CONST __attribute__((address_space(4)))
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 ld_stream(const FS_GLOBAL u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_stream(FS_GLOBAL u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+// a load the caller knows is wave-uniform and not written during the kernel:
+// through the scalar cache (its own counter, so it never waits on the
+// vector loads in flight)
+template <class T>
+__device__ __forceinline__ T sload(const T* p) { return *(const FS_CONST T*)p; }
+__device__ __forceinline__ PlanReq sload(const PlanReq* p) {
+    const uint64_t v = sload(reinterpret_cast<const uint64_t*>(p));
+    return PlanReq{static_cast<int32_t>(v & 0xFFFFFFFFu), static_cast<int32_t>(v >> 32)};
+}
+__device__ __forceinline__ PlanTok sload(const PlanTok* p) { return PlanTok{sload(&p->src), sload(&p->dst)}; }
 
 struct PlanArgs {
     const int32_t* user;
@@ -78,34 +79,15 @@ struct PlanArgs {
     const int32_t* user_count;      // live facts per user (from user_begin[u])
     int32_t num_users;
     int64_t num_facts;
-    int32_t layer_begin, layer_end, heads;
+    int32_t layer_begin, layer_end;
     const int32_t* stage_ids;       // non-null for pinned stores
     const int32_t* stage_meta;
     int32_t staging_layers, max_batch, max_k;
     int32_t seg_tokens;
-    int64_t* tok_src;
-    int64_t* tok_dst;
-    int32_t* req_len;
-    int32_t* start_out;             // a caller-owned plan's copy of start_pos, or null
+    uint32_t tag;
+    uint64_t key;
+    PlanView out;
     uint32_t* err;
-};
-
-struct InjectArgs {
-    const int32_t* start_pos;
-    const int64_t* tok_src;
-    const int64_t* tok_dst;
-    const int32_t* req_len;
-    int32_t seg_tokens;
-    const double* inv_freq;         // [D/2] w_i
-    int32_t heads;
-    int32_t layer_begin;
-    const void* const* src_k;       // device table [num_layers] (device store)
-    const void* const* src_v;
-    const uint16_t* stage_k;        // non-null: read the staging ring instead
-    const uint16_t* stage_v;
-    int32_t staging_layers, stage_tokens, max_batch;
-    void* kc[FS_MAX_LAYERS];
-    void* vc[FS_MAX_LAYERS];
 };
 
 __device__ __forceinline__ int wave_min(int v) {
@@ -127,7 +109,7 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
     return v;
 }
 
-// Segment plan of request b, shared by the block through LDS.
+// Segment plan of request b, by one wave, into LDS.
 //   off[j]  = first segment token of the j-th selected fact (j < nf)
 //   row0[j] = its first arena row
 // Returns the error bits (0 when the request can be served); *L and *nf get
@@ -148,8 +130,7 @@ __device__ uint32_t plan_request(const int32_t* user, const int32_t* ids, int k,
     const int64_t ub0 = bad_user ? 0 : user_begin[u];
     const int64_t ub1 = bad_user ? 0 : ub0 + user_count[u];     // the user's live facts
     // Lengths are counted only up to the first -1 pad, so every token t < L
-    // maps into a valid fact of the user even when the request is rejected
-    // (the kernels may read before the verdict is in, never out of bounds).
+    // maps into a valid fact of the user even when the request is rejected.
     int carry = 0, first_pad = k, last_real = -1;
     for (int c0 = 0; c0 < k; c0 += 64) {
         const int j = c0 + lane;
@@ -199,58 +180,8 @@ __device__ __forceinline__ int find_fact(const int32_t* off, int nf, int t) {
     return lo;
 }
 
-__device__ __forceinline__ uint32_t rot_word(uint32_t wa, uint32_t wb, int e, const double* c,
-                                             const double* s, uint32_t* out_b) {
-    // two adjacent pairs: elements (2e, 2e+1) of this lane's first-half vector
-    // and the same elements of its second-half vector
-    const double a0 = bf16_lo(wa), a1 = bf16_hi(wa);
-    const double b0 = bf16_lo(wb), b1 = bf16_hi(wb);
-    const double y0 = fma(a0, c[2 * e], -(b0 * s[2 * e]));
-    const double z0 = fma(b0, c[2 * e], a0 * s[2 * e]);
-    const double y1 = fma(a1, c[2 * e + 1], -(b1 * s[2 * e + 1]));
-    const double z1 = fma(b1, c[2 * e + 1], a1 * s[2 * e + 1]);
-    *out_b = f64_to_bf16_bits(z0) | (f64_to_bf16_bits(z1) << 16);
-    return f64_to_bf16_bits(y0) | (f64_to_bf16_bits(y1) << 16);
-}
-
-struct FetchArgs {
-    const int32_t* user;
-    const int32_t* ids;
-    int32_t k;
-    const int64_t* fact_begin;
-    const int32_t* fact_len;
-    const int64_t* user_begin;
-    const int32_t* user_count;      // live facts per user (from user_begin[u])
-    int32_t num_users;
-    int64_t num_facts;
-    int32_t heads;
-    int32_t layer_begin, layer_end, layers_per_block;
-    const void* const* src_k;       // device table of device-visible host addresses
-    const void* const* src_v;
-    uint16_t* stage_k;
-    uint16_t* stage_v;
-    int32_t* stage_ids;
-    int32_t* stage_meta;
-    int32_t staging_layers, stage_tokens, max_batch, max_k, batch;
-    uint32_t* err;
-};
-
-__device__ __forceinline__ void rot_v(const u32x4& xa, const u32x4& xb, const double* c,
-                                      const double* s, u32x4& ya, u32x4& yb) {
-    uint32_t b0, b1, b2, b3;
-    ya.x = rot_word(xa.x, xb.x, 0, c, s, &b0);
-    ya.y = rot_word(xa.y, xb.y, 1, c, s, &b1);
-    ya.z = rot_word(xa.z, xb.z, 2, c, s, &b2);
-    ya.w = rot_word(xa.w, xb.w, 3, c, s, &b3);
-    yb.x = b0;
-    yb.y = b1;
-    yb.z = b2;
-    yb.w = b3;
-}
-
-// Validation of one planned request, shared by the plan kernel and the
-// single-request inject path: start position, block-table coverage and
-// entries, and for pinned stores that every staging slot holds these ids.
+// Validation of one composed request: start position, block-table coverage
+// and entries, and for pinned stores that every staging slot holds these ids.
 __device__ uint32_t check_request(const PlanArgs& a, int b, int L) {
     const int lane = threadIdx.x & 63;
     uint32_t bits = 0;
@@ -292,8 +223,9 @@ __device__ uint32_t check_request(const PlanArgs& a, int b, int L) {
     return bits;
 }
 
-// Batches: one block per request.  Wave 0 plans into LDS, then the whole
-// block writes the token map; a rejected request gets length 0.
+// One block per request.  Wave 0 composes and validates into LDS, then the
+// whole block writes the token map; a rejected request gets length 0.
+// Block 0 also writes the plan header.
 __global__ __launch_bounds__(kPlanThreads) void fs_plan_kernel(PlanArgs a) {
     extern __shared__ int64_t plan_lds[];
     __shared__ int s_len, s_nf;
@@ -310,8 +242,18 @@ __global__ __launch_bounds__(kPlanThreads) void fs_plan_kernel(PlanArgs a) {
             if (bits) atomicOr(a.err, bits);
             s_len = bits ? 0 : L;
             s_nf = nf;
-            a.req_len[b] = bits ? 0 : L;
-            if (a.start_out) a.start_out[b] = a.start_pos[b];
+            a.out.req[b] = PlanReq{bits ? 0 : L, a.start_pos[b]};
+            if (b == 0) {
+                PlanHeader h{};
+                h.key = a.key;
+                h.magic = kPlanMagic;
+                h.tag = a.tag;
+                h.batch = a.batch;
+                h.k = a.k;
+                h.seg_tokens = a.seg_tokens;
+                h.num_blocks = a.num_blocks;
+                *a.out.hdr = h;
+            }
         }
     }
     __syncthreads();
@@ -319,164 +261,319 @@ __global__ __launch_bounds__(kPlanThreads) void fs_plan_kernel(PlanArgs a) {
     const int s = a.start_pos[b];
     const int32_t* bt = a.block_table + int64_t(b) * a.max_blocks;
     const int bs_mask = (1 << a.log2_block) - 1;
-    int64_t* src = a.tok_src + int64_t(b) * a.seg_tokens;
-    int64_t* dst = a.tok_dst + int64_t(b) * a.seg_tokens;
+    PlanTok* tok = a.out.tok + int64_t(b) * a.seg_tokens;
     for (int t = threadIdx.x; t < L; t += blockDim.x) {
         const int j = find_fact(off, nf, t);
-        src[t] = row0[j] + (t - off[j]);
         const int p = s + t;
-        dst[t] = (int64_t(bt[p >> a.log2_block]) << a.log2_block) | (p & bs_mask);
+        tok[t] = PlanTok{row0[j] + (t - off[j]), (int64_t(bt[p >> a.log2_block]) << a.log2_block) | (p & bs_mask)};
     }
 }
 
-// One block per (token group g, request b, layer l).  The group's tokens are
-// t = g*kTok + team.
-//
-// kPlanned = false (device stores): the block plans its request itself.  Wave 0
-// reads the ids and prefix-sums the fact lengths into LDS while the other
-// waves fill the cos/sin table.  After the first barrier every lane locates
-// its token's arena row and cache slot and issues its first loads, while wave
-// 0 validates the whole request (so a rejected request writes nothing in any
-// block); the second barrier publishes the verdict before any store.  Reads
-// before the verdict stay in bounds: the plan counts only valid facts of the
-// user, and block-table reads are range-checked.  No launch is spent on
-// planning.
-//
-// kPlanned = true (pinned stores): the plan kernel has validated the request
-// (including every layer's staging slot) and written the token map.
-template <int D, bool kPlanned>
-__global__ __launch_bounds__(kInjectThreads, kInjectOcc) void fs_inject_kernel(InjectArgs a, PlanArgs pa) {
-    constexpr int kTeam = D / 16;            // lanes per token
-    constexpr int kTok = 64 / kTeam;         // tokens per group
-    constexpr int kHalf = D / 16;            // 16-byte vectors per half head row
-    constexpr int kCS = kTok * (D / 2);      // (cos, sin) entries of the group
-    constexpr int kWaves = kInjectThreads / 64;
-    __shared__ double2 s_cs[kCS];
-    __shared__ int s_L, s_nf, s_bits;
-    extern __shared__ int64_t plan_lds[];
-    int64_t* row0 = plan_lds;
-    int32_t* off = reinterpret_cast<int32_t*>(plan_lds + pa.k);
-    const int b = blockIdx.y;
-    const int g = blockIdx.x;
-    const int l = a.layer_begin + blockIdx.z;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int team = lane / kTeam;
-    const int tl = lane % kTeam;
-    const int t = g * kTok + team;
-    const int64_t p0 = int64_t(a.start_pos[b]) + int64_t(g) * kTok;
-    const bool reporter = !kPlanned && g == 0 && blockIdx.z == 0;
+struct FlatArgs {
+    // read by every wave first (kept together)
+    const PlanHeader* hdr;
+    const PlanReq* req;
+    const PlanTok* tok;
+    uint64_t key;                   // what the plan header must hold
+    const void* const* src_kv;      // device table [num_layers][2] (device stores)
+    const double* inv_freq;         // [D/2] w_i
+    int64_t row_elems;              // heads * D
+    int64_t num_rows;               // arena rows: every source row lies below
+    int64_t cache_rows;             // num_blocks * block_size
+    int32_t units;                  // workgroups per (kind, request, layer)
+    int32_t layer_begin;
+    int32_t seg_tokens;
+    int32_t lg_vpr;                 // log2 of the row's vectors, rounded up to a power of two
+    int32_t vpr;                    // the row's 16-byte vectors (heads * D / 8)
+    // rarely read
+    const uint16_t* stage_k;        // staging ring (pinned stores)
+    const uint16_t* stage_v;
+    int32_t staging_layers, stage_tokens, max_batch;
+    uint32_t* err;
+    void* cache[2 * FS_MAX_LAYERS]; // [layer][K, V]
+};
 
-    int L;
-    int64_t src_row = 0, dst_row = 0;
-    if (kPlanned) {
-        L = a.req_len[b];
-        if (g * kTok >= L) return;           // uniform over the block
-        if (t < L) {
-            src_row = a.tok_src[int64_t(b) * a.seg_tokens + t];
-            dst_row = a.tok_dst[int64_t(b) * a.seg_tokens + t];
-        }
-    } else if (wave == 0) {
-        int Lr = 0, nf = 0;
-        const uint32_t bits = plan_request(pa.user, pa.ids, pa.k, pa.user_begin, pa.user_count, pa.num_users, pa.num_facts,
-                                           pa.fact_len, pa.fact_begin, b, off, row0, &Lr, &nf);
-        const uint32_t any = wave_or(bits);
-        if (lane == 0) {
-            s_L = Lr;
-            s_nf = nf;
-            s_bits = any;
-        }
+// The lane's rotate-half partner: the same vector position in the other half
+// of its head, D/16 lanes away (xor; heads start at multiples of D/8 lanes).
+template <int D>
+__device__ __forceinline__ uint32_t partner(uint32_t v) {
+    if constexpr (D == 128) {
+        // rotate each row of 16 lanes by 8: lane i receives lane i ^ 8
+        return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xF, 0xF, false));
+    } else if constexpr (D == 64) {
+        // swizzle within 32 lanes: and 0x1f, or 0, xor 4
+        return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x101F));
+    } else {
+        // xor 16
+        return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x401F));
     }
-    constexpr int kCsBegin = kPlanned ? 0 : 64;             // threads filling the table
-    constexpr int kCsStride = kInjectThreads - kCsBegin;
-    // when the stride is a multiple of D/2 a thread meets one frequency only:
-    // it is loaded once, not before every sincos
-    constexpr bool kOneFreq = kCsStride % (D / 2) == 0;
-    if (kPlanned || wave > 0) {
-        const double w_own = kOneFreq ? a.inv_freq[(threadIdx.x - kCsBegin) % (D / 2)] : 0.0;
-        for (int e = threadIdx.x - kCsBegin; e < kCS; e += kCsStride) {
-            const int tt = e / (D / 2);
-            const int i = e - tt * (D / 2);
+}
+
+// Rotate-half of one 16-byte vector (8 bf16) of a K row: the first half's
+// lanes compute y_i = x_i c - x_{i+D/2} s, the second half's
+// y_{i+D/2} = x_{i+D/2} c + x_i s, each from its own vector and its
+// partner's; the vector holds pairs i = 8*tl .. 8*tl+7 and cp points at the
+// row's cos/sin entry 8*tl.
+template <int D>
+__device__ __forceinline__ u32x4 rotate_vec(u32x4 x, int vec, const double2* row_cs) {
+    constexpr int kHalfV = D / 16;
+    u32x4 p;
+    p.x = partner<D>(x.x);
+    p.y = partner<D>(x.y);
+    p.z = partner<D>(x.z);
+    p.w = partner<D>(x.w);
+    const int vh = vec & (D / 8 - 1);
+    const bool second = vh >= kHalfV;
+    const int tl = second ? vh - kHalfV : vh;
+    const double sg = second ? 1.0 : -1.0;
+    const double2* cp = row_cs + 8 * tl;
+    u32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const double2 c0 = cp[2 * e], c1 = cp[2 * e + 1];
+        const double y0 =
+            fma(static_cast<double>(bf16_lo(x[e])), c0.x, sg * (static_cast<double>(bf16_lo(p[e])) * c0.y));
+        const double y1 =
+            fma(static_cast<double>(bf16_hi(x[e])), c1.x, sg * (static_cast<double>(bf16_hi(p[e])) * c1.y));
+        y[e] = f64_to_bf16_bits(y0) | (f64_to_bf16_bits(y1) << 16);
+    }
+    return y;
+}
+
+// cos/sin(p * w_i) of kTok rows of the workgroup (row j at position
+// start + min(t0 + j, L - 1)) into LDS, entry j * D/2 + i.  The position is
+// formed before the range test: with it inside, the compiler evaluates the
+// large-argument reduction of sincos on every lane instead of branching
+// around it, which made the launch 3% slower.
+template <int D, int kTok>
+__device__ __forceinline__ void fill_cs(double2* s_cs, const double* w_e, int start, int t0, int L) {
+    constexpr int kE = kTok * (D / 2);
+    constexpr int kEPT = (kE + kFlatThreads - 1) / kFlatThreads;
+#pragma unroll
+    for (int q = 0; q < kEPT; ++q) {
+        const int e = static_cast<int>(threadIdx.x) + q * kFlatThreads;
+        const int tt = min(t0 + e / (D / 2), L - 1);
+        const double x = static_cast<double>(start + tt) * w_e[q];
+        if (e < kE) {
             double sv, cv;
-            sincos(static_cast<double>(p0 + tt) * (kOneFreq ? w_own : a.inv_freq[i]), &sv, &cv);
+            sincos(x, &sv, &cv);
             s_cs[e] = make_double2(cv, sv);
         }
     }
-    if (!kPlanned) {
-        __syncthreads();                     // plan in LDS
-        L = s_L;
-        if (g * kTok >= L && !reporter) return;   // uniform over the block
-        if (t < L) {
-            const int j = find_fact(off, s_nf, t);
-            src_row = row0[j] + (t - off[j]);
-        }
-    }
-    const bool act = t < L;
-    const int H = a.heads;
-    const int64_t row_elems = int64_t(H) * D;
-    const FS_GLOBAL u32x4* kbase;
-    const FS_GLOBAL u32x4* vbase;
-    if (a.stage_k) {
-        const int64_t srow = (int64_t(l % a.staging_layers) * a.max_batch + b) * a.stage_tokens + t;
-        kbase = (const FS_GLOBAL u32x4*)(a.stage_k + srow * row_elems);
-        vbase = (const FS_GLOBAL u32x4*)(a.stage_v + srow * row_elems);
-    } else {
-        kbase = (const FS_GLOBAL u32x4*)(static_cast<const uint16_t*>(a.src_k[l]) + src_row * row_elems);
-        vbase = (const FS_GLOBAL u32x4*)(static_cast<const uint16_t*>(a.src_v[l]) + src_row * row_elems);
-    }
-    u32x4 ka, kb, va, vb;
-    auto load_head = [&](int h) {
-        if (act && h < H) {
-            const int o = h * (D / 8) + tl;
-            ka = ld_stream(kbase + o);
-            kb = ld_stream(kbase + o + kHalf);
-            va = ld_stream(vbase + o);
-            vb = ld_stream(vbase + o + kHalf);
-        }
-    };
-    load_head(wave);                         // in flight across the barrier
-    // the token's cache slot: its block-table entry is read after the K/V
-    // loads are out, by every thread (index clamped in range, so no branch
-    // forces a wait on it here; a bad entry or a short table rejects the
-    // request below, before any store)
-    int blk_raw = 0;
-    const int64_t p_tok = p0 + team;
-    const int64_t bi_tok = p_tok >> pa.log2_block;
-    if (!kPlanned)
-        blk_raw = pa.block_table[int64_t(b) * pa.max_blocks +
-                                 (p_tok >= 0 && bi_tok < pa.max_blocks ? bi_tok : 0)];
-    if (!kPlanned && wave == 0) {
-        const uint32_t bits = wave_or(check_request(pa, b, L)) | s_bits;
-        if (lane == 0) {
-            s_bits = bits;
-            if (bits && reporter) atomicOr(pa.err, bits);
-        }
-    }
-    __syncthreads();                         // reached by every thread still here
-    if (!kPlanned && s_bits) return;
-    if (!act) return;
-    if (!kPlanned) dst_row = (int64_t(blk_raw) << pa.log2_block) | (p_tok & ((1 << pa.log2_block) - 1));
-    FS_GLOBAL u32x4* kd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.kc[l]) + dst_row * row_elems);
-    FS_GLOBAL u32x4* vd = (FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.vc[l]) + dst_row * row_elems);
-    double c[8], sn[8];
-    const double2* cs = s_cs + team * (D / 2) + 8 * tl;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const double2 v = cs[e];
-        c[e] = v.x;
-        sn[e] = v.y;
-    }
-    for (int h = wave; h < H; h += kWaves) {
-        if (h != wave) load_head(h);
-        const int o = h * (D / 8) + tl;
-        u32x4 ya, yb;
-        rot_v(ka, kb, c, sn, ya, yb);
-        st_stream(kd + o, ya);
-        st_stream(kd + o + kHalf, yb);
-        st_stream(vd + o, va);
-        st_stream(vd + o + kHalf, vb);
-    }
 }
+
+// The (request, layer) segment's K rows or V rows are cut into workgroups
+// of 256 16-byte vectors, one per lane: a row of 2^kLg vectors (the row's
+// heads * D / 8, rounded up to a power of two; the lanes of the padding stay
+// idle) gives each workgroup 256 >> kLg whole rows, or 2^(kLg-8)
+// workgroups one row.  The grid covers a segment of k of the store's longest
+// facts, so a workgroup past its request's real length exits; it reads only
+// that length first (a workgroup that also loaded its plan entries before
+// finding itself empty made the launch 5% slower), and a live one then
+// reads the rest.  The workgroups of one launch number in the tens of
+// thousands and a compute unit's scalar unit issues for all of them, so the
+// prologue is short: compile-time shifts and masks, one 64-bit key rather
+// than field-by-field plan checks, and one scalar load per request, row and
+// layer.
+//
+// Rows of 64 vectors or more (fs_row_kernel): every wave lies inside one row,
+// so the wave's plan entry comes through the scalar cache.  K workgroups
+// first issue the loads of the inverse frequencies of the cos/sin entries
+// they own, then the K row, then evaluate cos/sin(p * w_i) in fp64 into LDS
+// while the row is in flight; a lane's rotate-half partner (D/16 lanes away,
+// in the same head) arrives by a cross-lane move.  Per launch on the Llama
+// shape: 73 us, against 80 us for a block of 8 tokens x all heads x K and V
+// with a per-block plan and cos/sin table, 75 us for two vectors per lane,
+// and 66 us for the same bytes as a contiguous copy.
+template <int D, int kLg, bool kStaged>
+__global__ __launch_bounds__(kFlatThreads) void fs_row_kernel(FlatArgs a) {
+    constexpr int kSplit = kLg > 8 ? kLg - 8 : 0;              // log2 workgroups per row
+    constexpr int kTok = kLg <= 8 ? kFlatThreads >> kLg : 1;   // rows per workgroup
+    constexpr int kE = kTok * (D / 2);
+    constexpr int kEPT = (kE + kFlatThreads - 1) / kFlatThreads;
+    static_assert(kLg >= 6, "a wave lies inside one row");
+    __shared__ double2 s_cs[kE];
+
+    const int kind = blockIdx.x >= static_cast<unsigned>(a.units);
+    const int unit = static_cast<int>(blockIdx.x) - kind * a.units;
+    const int b = blockIdx.y;
+    const int l = a.layer_begin + static_cast<int>(blockIdx.z);
+    // the request's length and start first: a workgroup past the segment
+    // leaves after this one load
+    const PlanReq rq = sload(a.req + b);
+    const int L = rq.len;
+    const int t0 = kLg <= 8 ? unit * kTok : unit >> kSplit;    // first row of the workgroup
+    if (t0 >= L) return;
+    const int r = kLg <= 8 ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> kLg) : 0;
+    const int vec = kLg <= 8 ? static_cast<int>(threadIdx.x) & ((1 << kLg) - 1)
+                             : ((unit & ((1 << kSplit) - 1)) << 8) + static_cast<int>(threadIdx.x);
+    const int tw = t0 + r;                                      // the wave's row
+    // in range of the plan's token map whatever the header holds
+    const PlanTok* te = a.tok + int64_t(b) * a.seg_tokens + min(tw, a.seg_tokens - 1);
+    const int64_t stage_row = kStaged ? (int64_t(l % a.staging_layers) * a.max_batch + b) * a.stage_tokens + tw : 0;
+
+    if (kind == 1) {
+        // V: a raw row copy
+        if (tw >= L) return;
+        const uint64_t key = sload(&a.hdr->key);
+        const int64_t sr = kStaged ? stage_row : sload(&te->src);
+        const int64_t dr = sload(&te->dst);
+        const uint16_t* sb = kStaged ? a.stage_v : static_cast<const uint16_t*>(sload(a.src_kv + 2 * l + 1));
+        if (key != a.key || L > a.seg_tokens) {
+            // not a plan of this store, batch, k and cache size: nothing is written
+            if (blockIdx.x == static_cast<unsigned>(a.units) && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0)
+                atomicOr(a.err, FS_ERR_PLAN);
+            return;
+        }
+        // a row outside the arena or the caches is never touched (a plan
+        // this store wrote has none)
+        if (!(kStaged || static_cast<uint64_t>(sr) < static_cast<uint64_t>(a.num_rows)) ||
+            static_cast<uint64_t>(dr) >= static_cast<uint64_t>(a.cache_rows)) {
+            if ((threadIdx.x & 63) == 0) atomicOr(a.err, FS_ERR_PLAN);
+            return;
+        }
+        if (vec >= a.vpr) return;
+        const u32x4 x = ld_stream((const FS_GLOBAL u32x4*)(sb + sr * a.row_elems) + vec);
+        st_stream((FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.cache[2 * l + 1]) + dr * a.row_elems) + vec, x);
+        return;
+    }
+
+    // K: the frequencies of the table entries this thread evaluates, then
+    // the key, the wave's row entry and the layer's arena, all at once
+    double w_e[kEPT];
+#pragma unroll
+    for (int q = 0; q < kEPT; ++q)
+        w_e[q] = a.inv_freq[(static_cast<int>(threadIdx.x) + q * kFlatThreads) & (D / 2 - 1)];
+    const uint64_t key = sload(&a.hdr->key);
+    const int64_t sr = kStaged ? stage_row : sload(&te->src);
+    const int64_t dr = sload(&te->dst);
+    const uint16_t* sb = kStaged ? a.stage_k : static_cast<const uint16_t*>(sload(a.src_kv + 2 * l));
+    // naming every loaded value here keeps the compiler from sinking the
+    // loads into the branches below one round trip at a time
+    asm volatile("" ::"s"(key), "s"(sr), "s"(dr), "s"(sb));
+    if (key != a.key || L > a.seg_tokens) {
+        if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) atomicOr(a.err, FS_ERR_PLAN);
+        return;
+    }
+    const bool ok = (kStaged || static_cast<uint64_t>(sr) < static_cast<uint64_t>(a.num_rows)) &&
+                    static_cast<uint64_t>(dr) < static_cast<uint64_t>(a.cache_rows);
+    const bool act = tw < L && ok;
+    // the row load is issued by every lane (a wave without a row reads the
+    // arena's first row): a conditional load would leave the compiler unsure
+    // how many loads are in flight, and it would then wait for the row
+    // before the cos/sin evaluation instead of after it
+    asm volatile("" ::: "memory");
+    const u32x4 x = ld_stream((const FS_GLOBAL u32x4*)(sb + (act ? sr * a.row_elems : 0)) + min(vec, a.vpr - 1));
+    asm volatile("" ::: "memory");
+    fill_cs<D, kTok>(s_cs, w_e, rq.start, t0, L);
+    __syncthreads();
+    if (!act) {
+        // reported after the loads: a memory operation between the plan
+        // loads and the row load would make the compiler wait for every
+        // load in flight
+        if (tw < L && (threadIdx.x & 63) == 0) atomicOr(a.err, FS_ERR_PLAN);
+        return;
+    }
+    const u32x4 y = rotate_vec<D>(x, vec, s_cs + r * (D / 2));
+    if (vec < a.vpr) st_stream((FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.cache[2 * l]) + dr * a.row_elems) + vec, y);
+}
+
+// Rows of fewer than 64 vectors (fs_short_kernel): a wave holds 64 >> kLg
+// rows and each lane takes the entry of its own row among the wave's.
+template <int D, int kLg, bool kStaged>
+__global__ __launch_bounds__(kFlatThreads) void fs_short_kernel(FlatArgs a) {
+    constexpr int kVPR = 1 << kLg;
+    constexpr int kRPW = 64 >> kLg;                    // rows per wave
+    constexpr int kTok = kFlatThreads >> kLg;          // rows per workgroup
+    constexpr int kE = kTok * (D / 2);
+    constexpr int kEPT = (kE + kFlatThreads - 1) / kFlatThreads;
+    static_assert(kLg < 6, "rows shorter than a wave");
+    __shared__ double2 s_cs[kE];
+
+    const int kind = blockIdx.x >= static_cast<unsigned>(a.units);
+    const int unit = static_cast<int>(blockIdx.x) - kind * a.units;
+    const int b = blockIdx.y;
+    const int l = a.layer_begin + static_cast<int>(blockIdx.z);
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int tf = unit * kTok;                        // first row of the workgroup
+    const int tw0 = tf + wave * kRPW;                  // the wave's first row
+    const PlanReq rq = sload(a.req + b);
+    const int L = rq.len;
+    if (tf >= L) return;
+
+    double w_e[kEPT];
+    if (kind == 0) {
+#pragma unroll
+        for (int q = 0; q < kEPT; ++q)
+            w_e[q] = a.inv_freq[(static_cast<int>(threadIdx.x) + q * kFlatThreads) & (D / 2 - 1)];
+    }
+    const uint64_t key = sload(&a.hdr->key);
+    PlanTok tk[kRPW];
+    const PlanTok* tb = a.tok + int64_t(b) * a.seg_tokens;
+#pragma unroll
+    for (int j = 0; j < kRPW; ++j) tk[j] = sload(tb + min(tw0 + j, a.seg_tokens - 1));
+    const uint16_t* src_base =
+        kStaged ? (kind == 0 ? a.stage_k : a.stage_v) : static_cast<const uint16_t*>(sload(a.src_kv + 2 * l + kind));
+    asm volatile("" ::"s"(key), "s"(src_base));
+#pragma unroll
+    for (int j = 0; j < kRPW; ++j) asm volatile("" ::"s"(tk[j].src), "s"(tk[j].dst));
+    if (key != a.key || L > a.seg_tokens) {
+        if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) atomicOr(a.err, FS_ERR_PLAN);
+        return;
+    }
+    uint16_t* dst_base = static_cast<uint16_t*>(a.cache[2 * l + kind]);
+
+    // the lane's own row among the wave's
+    const int tj = tf + (static_cast<int>(threadIdx.x) >> kLg);
+    const int vj = static_cast<int>(threadIdx.x) & (kVPR - 1);
+    int64_t sr = tk[0].src, dr = tk[0].dst;
+#pragma unroll
+    for (int j = 1; j < kRPW; ++j)
+        if (tj - tw0 == j) {
+            sr = tk[j].src;
+            dr = tk[j].dst;
+        }
+    if (kStaged) sr = (int64_t(l % a.staging_layers) * a.max_batch + b) * a.stage_tokens + tj;
+    const bool ok = (kStaged || static_cast<uint64_t>(sr) < static_cast<uint64_t>(a.num_rows)) &&
+                    static_cast<uint64_t>(dr) < static_cast<uint64_t>(a.cache_rows);
+    const bool in = tj < L && vj < a.vpr;
+    const bool bad = in && !ok;
+    const bool act = in && ok;
+    const u32x4 x = ld_stream((const FS_GLOBAL u32x4*)(src_base + (act ? sr * a.row_elems + int64_t(vj) * 8 : 0)));
+    asm volatile("" ::: "memory");
+    if (kind == 1) {
+        if (act) st_stream((FS_GLOBAL u32x4*)(dst_base + dr * a.row_elems) + vj, x);
+        if (bad) atomicOr(a.err, FS_ERR_PLAN);
+        return;
+    }
+    fill_cs<D, kTok>(s_cs, w_e, rq.start, tf, L);
+    __syncthreads();
+    const u32x4 y = rotate_vec<D>(x, vj, s_cs + min(tj - tf, kTok - 1) * (D / 2));
+    if (act) st_stream((FS_GLOBAL u32x4*)(dst_base + dr * a.row_elems) + vj, y);
+    if (bad) atomicOr(a.err, FS_ERR_PLAN);
+}
+
+struct FetchArgs {
+    const int32_t* user;
+    const int32_t* ids;
+    int32_t k;
+    const int64_t* fact_begin;
+    const int32_t* fact_len;
+    const int64_t* user_begin;
+    const int32_t* user_count;      // live facts per user (from user_begin[u])
+    int32_t num_users;
+    int64_t num_facts;
+    int32_t heads;
+    int32_t layer_begin, layer_end, layers_per_block;
+    const void* const* src_k;       // device table of device-visible host addresses
+    const void* const* src_v;
+    uint16_t* stage_k;
+    uint16_t* stage_v;
+    int32_t* stage_ids;
+    int32_t* stage_meta;
+    int32_t staging_layers, stage_tokens, max_batch, max_k, batch;
+    uint32_t* err;
+};
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void fs_fetch_kernel(FetchArgs a) {
@@ -559,17 +656,16 @@ __global__ __launch_bounds__(kThreads) void fs_fetch_kernel(FetchArgs a) {
 
 int layers_per_block(int nl, int64_t blocks_per_layer) {
     // enough blocks to fill 256 CUs several times over, while reusing each
-    // team's cos/sin over as many layers as possible
+    // block's plan over as many layers as possible
     int lpb = nl;
     while (lpb > 1 && blocks_per_layer * ((nl + lpb - 1) / lpb) < 4096) lpb = (lpb + 1) / 2;
     return lpb;
 }
 
 template <int D>
-hipError_t launch_inject(const InjectLaunch& r) {
+hipError_t launch_plan(const InjectLaunch& r, void* plan) {
     const fs_store* st = r.st;
     const fs_store_desc& d = st->desc;
-
     PlanArgs pa{};
     pa.user = r.user;
     pa.ids = r.ids;
@@ -588,7 +684,6 @@ hipError_t launch_inject(const InjectLaunch& r) {
     pa.num_facts = d.num_facts;
     pa.layer_begin = r.layer_begin;
     pa.layer_end = r.layer_end;
-    pa.heads = d.num_kv_heads;
     if (d.kv_location == FS_KV_PINNED_HOST) {
         pa.stage_ids = st->d_stage_ids;
         pa.stage_meta = st->d_stage_meta;
@@ -597,33 +692,55 @@ hipError_t launch_inject(const InjectLaunch& r) {
     pa.max_batch = d.max_batch;
     pa.max_k = d.max_k;
     pa.seg_tokens = st->seg_tokens;
-    pa.tok_src = st->d_tok_src;
-    pa.tok_dst = st->d_tok_dst;
-    pa.req_len = st->d_req_len;
+    pa.tag = st->tag;
+    pa.key = fsi_plan_key(st->tag, r.batch, r.k, st->seg_tokens, r.num_blocks);
+    pa.out = fsi_plan_view(st, r.batch, plan);
     pa.err = st->d_err;
     const size_t plan_lds = sizeof(int64_t) * (size_t(r.k) + (size_t(r.k) + 2) / 2);
-    if (r.plan_out) {
-        // compose and validate into the caller's plan, nothing else
-        const PlanView v = fsi_plan_view(st, r.batch, r.plan_out);
-        pa.tok_src = v.tok_src;
-        pa.tok_dst = v.tok_dst;
-        pa.req_len = v.req_len;
-        pa.start_out = v.start;
-        fs_plan_kernel<<<dim3(r.batch), kPlanThreads, plan_lds, r.stream>>>(pa);
-        return hipGetLastError();
-    }
+    fs_plan_kernel<<<dim3(r.batch), kPlanThreads, plan_lds, r.stream>>>(pa);
+    return hipGetLastError();
+}
 
-    InjectArgs a{};
-    a.start_pos = r.start_pos;
-    a.tok_src = st->d_tok_src;
-    a.tok_dst = st->d_tok_dst;
-    a.req_len = st->d_req_len;
-    a.seg_tokens = st->seg_tokens;
+// longest padded row the inject kernels are built for: 2^10 vectors (16 KB,
+// e.g. 32 heads of 256 or 64 heads of 128)
+constexpr int kFlatMaxLg = 10;
+
+template <int D, int kLg>
+void dispatch_flat(int lg, const FlatArgs& a, dim3 grid, hipStream_t s) {
+    if constexpr (kLg <= kFlatMaxLg) {
+        if (lg != kLg) {
+            dispatch_flat<D, kLg + 1>(lg, a, grid, s);
+        } else if constexpr (kLg >= 6) {
+            if (a.stage_k) fs_row_kernel<D, kLg, true><<<grid, kFlatThreads, 0, s>>>(a);
+            else fs_row_kernel<D, kLg, false><<<grid, kFlatThreads, 0, s>>>(a);
+        } else {
+            if (a.stage_k) fs_short_kernel<D, kLg, true><<<grid, kFlatThreads, 0, s>>>(a);
+            else fs_short_kernel<D, kLg, false><<<grid, kFlatThreads, 0, s>>>(a);
+        }
+    }
+}
+
+template <int D>
+hipError_t launch_flat(const InjectLaunch& r, const void* plan) {
+    const fs_store* st = r.st;
+    const fs_store_desc& d = st->desc;
+    const PlanView v = fsi_plan_view(st, r.batch, plan);
+    FlatArgs a{};
+    a.hdr = v.hdr;
+    a.req = v.req;
+    a.tok = v.tok;
+    a.key = fsi_plan_key(st->tag, r.batch, r.k, st->seg_tokens, r.num_blocks);
+    a.src_kv = st->d_src_kv;
     a.inv_freq = st->d_inv_freq;
-    a.heads = d.num_kv_heads;
+    a.row_elems = int64_t(d.num_kv_heads) * D;
+    a.num_rows = d.num_tokens;
+    a.cache_rows = int64_t(r.num_blocks) << st->log2_block;
     a.layer_begin = r.layer_begin;
-    a.src_k = st->d_src_k;
-    a.src_v = st->d_src_v;
+    a.seg_tokens = st->seg_tokens;
+    a.vpr = d.num_kv_heads * (D / 8);
+    int lg = 0;
+    while ((1 << lg) < a.vpr) ++lg;
+    if (lg > kFlatMaxLg) return hipErrorInvalidValue;
     if (d.kv_location == FS_KV_PINNED_HOST) {
         a.stage_k = static_cast<const uint16_t*>(st->d_stage_k);
         a.stage_v = static_cast<const uint16_t*>(st->d_stage_v);
@@ -631,35 +748,34 @@ hipError_t launch_inject(const InjectLaunch& r) {
         a.stage_tokens = st->stage_tokens;
     }
     a.max_batch = d.max_batch;
+    a.err = st->d_err;
     for (int l = 0; l < d.num_layers; ++l) {
-        a.kc[l] = r.k_cache[l];
-        a.vc[l] = r.v_cache[l];
+        a.cache[2 * l] = r.k_cache[l];
+        a.cache[2 * l + 1] = r.v_cache[l];
     }
-    // token groups of the longest possible segment (at least one, which
-    // reports the request's errors); the blocks past a request's real length
-    // exit once its length is known
-    constexpr int kTok = 64 / (D / 16);
-    const int64_t groups = std::max<int64_t>(1, (int64_t(r.k) * st->max_fact_len + kTok - 1) / kTok);
-    const dim3 grid(static_cast<unsigned>(groups), static_cast<unsigned>(r.batch),
+    // units cover the longest possible segment of k facts (padded rows laid
+    // end to end); a workgroup past its request's real length exits after
+    // reading that length
+    const int64_t seg = int64_t(r.k) * st->max_fact_len;
+    const int64_t units = ((seg << lg) + kFlatThreads - 1) / kFlatThreads;
+    if (units > INT32_MAX / 2) return hipErrorInvalidValue;
+    a.units = static_cast<int32_t>(std::max<int64_t>(units, 1));
+    const dim3 grid(static_cast<unsigned>(2 * a.units), static_cast<unsigned>(r.batch),
                     static_cast<unsigned>(r.layer_end - r.layer_begin));
-    if (r.plan_in) {
-        // inject from the caller's plan: the blocks read their tokens' rows
-        // and slots instead of planning
-        const PlanView v = fsi_plan_view(st, r.batch, r.plan_in);
-        a.start_pos = v.start;
-        a.tok_src = v.tok_src;
-        a.tok_dst = v.tok_dst;
-        a.req_len = v.req_len;
-        fs_inject_kernel<D, true><<<grid, kInjectThreads, 0, r.stream>>>(a, pa);
-    } else if (d.kv_location == FS_KV_PINNED_HOST) {
-        fs_plan_kernel<<<dim3(r.batch), kPlanThreads, plan_lds, r.stream>>>(pa);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        fs_inject_kernel<D, true><<<grid, kInjectThreads, 0, r.stream>>>(a, pa);
-    } else {
-        fs_inject_kernel<D, false><<<grid, kInjectThreads, plan_lds, r.stream>>>(a, pa);
-    }
+    // a head is D/8 vectors, so rows start at 2^log2(D/8) vectors
+    constexpr int kLg0 = D == 64 ? 3 : (D == 128 ? 4 : 5);
+    dispatch_flat<D, kLg0>(lg, a, grid, r.stream);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_inject(const InjectLaunch& r) {
+    if (r.plan_out) {
+        hipError_t e = launch_plan<D>(r, r.plan_out);
+        if (e != hipSuccess || !r.inject) return e;
+        return launch_flat<D>(r, r.plan_out);
+    }
+    return launch_flat<D>(r, r.plan_in);
 }
 
 template <int D>

@@ -34,10 +34,12 @@ FS_ERR_START_POS = 0x04
 FS_ERR_BLOCK_SHORT = 0x08
 FS_ERR_BLOCK_ID = 0x10
 FS_ERR_STAGING = 0x20
+FS_ERR_PLAN = 0x40
 
 FS_ALL_LAYERS = -1
 FS_MAX_LAYERS = 128
 FS_MAX_K = 1024
+FS_PLAN_SLOTS = 4
 FS_KV_DEVICE = 0
 FS_KV_PINNED_HOST = 1
 
@@ -102,7 +104,7 @@ def _load() -> ctypes.CDLL:
         "fs_inject_layers": (i32, [P, i32, i32, i32, P, P, i32, P, i32, P, P, P, i32, P]),
         "fs_inject_plan_size": (i32, [P, i32, ctypes.POINTER(ctypes.c_size_t)]),
         "fs_plan_inject": (i32, [P, i32, P, P, i32, P, i32, P, i32, P, ctypes.c_size_t, P]),
-        "fs_inject_planned": (i32, [P, i32, i32, i32, i32, P, ctypes.c_size_t, P, P, P]),
+        "fs_inject_planned": (i32, [P, i32, i32, i32, i32, P, ctypes.c_size_t, P, P, i32, P]),
         "fs_fetch_async": (i32, [P, i32, P, P, i32, i32, i32, P]),
         "fs_attend_prefill": (i32, [P, i32, i32, i32, P, P, P, i32, P, i32, P, P, ctypes.c_float,
                                     P, P, ctypes.c_size_t, P]),
@@ -342,7 +344,7 @@ def prepare_inject_planned(store, layers, batch: int, k: int, plan: torch.Tensor
     if 0 <= lb < le <= len(caches.present) and not all(caches.present[lb:le]):
         raise ValueError(f"no cache given for some layer of [{lb}, {le})")
     args = (_handle(store), lb, le, int(batch), int(k), _ptr(plan, torch.uint8, name="plan"),
-            ctypes.c_size_t(plan.numel()), caches.k, caches.v, _stream(stream))
+            ctypes.c_size_t(plan.numel()), caches.k, caches.v, caches.num_blocks, _stream(stream))
     return Prepared(_lib.fs_inject_planned, args, "fs_inject_planned", (store, plan, caches))
 
 

@@ -338,7 +338,10 @@ def test_device_checked_fault_writes_nothing(fault, path):
 
 # ------------------------------------------------------ other shapes and layouts
 
-@pytest.mark.parametrize("D, H, bs", [(64, 4, 16), (256, 2, 8), (128, 3, 1), (128, 8, 32)])
+# rows of 32, 64, 48 (padded to 64), 128, 384 (padded to 512, two workgroups
+# a row) and 1024 (four workgroups a row) 16-byte vectors
+@pytest.mark.parametrize("D, H, bs", [(64, 4, 16), (256, 2, 8), (128, 3, 1), (128, 8, 32), (256, 12, 4),
+                                      (128, 64, 16)])
 def test_head_dims_and_block_sizes(D, H, bs):
     import dataclasses
     base = synth.CONFIGS["tiny"]
