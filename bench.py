@@ -14,22 +14,29 @@ retrieval and then its injection on stream i % 2, so step i+1's retrieval
 (latency-bound, a few MB) and the start of its injection overlap step i's
 injection (bandwidth-bound).  Retrievals share the store's scratch, so each
 waits on an event after the previous one; the lanes inject into separate
-cache pools.  ms_per_step_in_order repeats the steps on one stream, strictly
-one after the other.
+cache pools.  request_latency_us.in_order repeats the steps on one stream,
+strictly one after the other: one request's retrieval, plan and row
+injection (the time-to-inject of a single request).
 
 Prints ONE JSON line:
   value       whole-step algorithmic HBM bytes / step time (GB/s)
   injected_payload_GBps  the K and V bytes landed in the caches / step time
-  roofline    the inject kernel: its algorithmic bytes per launch over its
+  roofline    the row-streaming inject kernel (fs_inject_planned launches one
+              and nothing else): its algorithmic bytes per launch over its
               average launch time (HIP events on the launch stream around the
-              steps' injects issued back to back), against 8 TB/s
-  kernels_ms  average launch times of the retrieval, the inject, and beside
-              them the plan kernel and the inject from a plan
-              (fs_plan_inject, fs_inject_planned), each issued back to back
-  inject_cold each inject alone after a 1 GiB write that evicts the MALL and
-              L2 (median, p10, p90)
+              steps' launches issued back to back), against 8 TB/s; "cold"
+              repeats it with each launch alone after a 1 GiB write that
+              evicts the MALL and L2 (median, p10, p90)
+  kernels_ms  average launch times of the retrieval, the fused inject (plan
+              kernel + row kernel), the plan kernel alone and the row kernel
+              alone (fs_plan_inject, fs_inject_planned), each issued back to
+              back
+  request_latency_us  one request at a time, in order: the whole step, and
+              its parts from kernels_ms
+  inject_cold each fused inject alone after the same 1 GiB write
   cpu_baseline  the CPU oracle on a bounded sample of the same workload, on
-              one thread and on all given cores
+              every core of the process's CPU share, and beside it on one
+              thread
 
 Algorithmic bytes: inject = 8 * L * layers * heads * head_dim (K and V, bf16,
 read once and written once) per request of segment length L; retrieval =
@@ -205,6 +212,14 @@ def main():
     torch.cuda.synchronize()
     u1 = time.perf_counter()
 
+    # every kernel region 2 times has run before it: the in-order steps ran
+    # the retrievals and fused injects; the plans and the injects from plans
+    # run here (a first launch pays one-time costs)
+    for i in range(min(total, max(args.warmup, 5))):
+        plan_s[i]()
+        injp_s[i]()
+    torch.cuda.synchronize()
+
     # timed region 2: per-kernel average durations for the roofline, from
     # HIP events on the launch stream: the steps' retrievals back to back
     # between two events, then their fused injects, their plans and their
@@ -226,20 +241,25 @@ def main():
     e4.record()
     torch.cuda.synchronize()
 
-    # timed region 3 (reported beside, never value): each inject alone after
-    # a 1 GiB write that evicts the MALL and L2, between its own HIP events
+    # timed region 3 (reported beside, never value): each row-kernel launch
+    # (from the plan region 2 wrote) and each fused inject alone after a
+    # 1 GiB write that evicts the MALL and L2, between its own HIP events
     # (an event pair adds ~2 us to one launch), for median and p10/p90
     n_cold = min(args.steps, 50)
     flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
-    cold = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_cold)]
-    for j, (ca, cb) in enumerate(cold):
-        flush.fill_(j)
-        ca.record()
-        inj_s[args.warmup + j]()
-        cb.record()
-    torch.cuda.synchronize()
+
+    def timed_cold(calls):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_cold)]
+        for j, (ca, cb) in enumerate(ev):
+            flush.fill_(j)
+            ca.record()
+            calls[args.warmup + j]()
+            cb.record()
+        torch.cuda.synchronize()
+        return np.array([ca.elapsed_time(cb) for ca, cb in ev])
+    row_cold_ms = timed_cold(injp_s)
+    cold_ms = timed_cold(inj_s)
     del flush
-    cold_ms = np.array([ca.elapsed_time(cb) for ca, cb in cold])
 
     wall = t1 - t0
     row_bytes = 2 * s.num_kv_heads * s.head_dim                      # one token, one layer, K or V
@@ -251,7 +271,12 @@ def main():
     plan_ms = e2.elapsed_time(e3) / args.steps
     planned_ms = e3.elapsed_time(e4) / args.steps
     ret_ms = np.full(args.steps, e0.elapsed_time(e1) / args.steps)
-    achieved = float(inject_bytes.sum() / (inj_ms.sum() * 1e-3) / 1e9)
+    achieved = float(inject_bytes.sum() / (planned_ms * args.steps * 1e-3) / 1e9)
+    row_cold_gbs = inject_bytes[:n_cold] / (row_cold_ms * 1e-3) / 1e9
+    vpr = s.num_kv_heads * s.head_dim // 8
+    lg = (vpr - 1).bit_length()
+    kname = f"fs_{'row' if lg >= 6 else 'short'}_kernel<{s.head_dim}, {lg}>"
+    in_order_us = (u1 - u0) / args.steps * 1e6
     value = float(step_bytes.sum() / wall / 1e9)
     ms_per_step = wall / args.steps * 1e3
     traffic = recorded_traffic(args.config, nl)
@@ -303,6 +328,13 @@ def main():
                        "inject_avg": round(float(inj_ms.mean()), 5),
                        "plan_avg": round(float(plan_ms), 5),
                        "inject_from_plan_avg": round(float(planned_ms), 5)},
+        "request_latency_us": {
+            "in_order": round(in_order_us, 2),
+            "retrieve": round(float(ret_ms.mean()) * 1e3, 2),
+            "inject": round(float(inj_ms.mean()) * 1e3, 2),
+            "in_order_over_inject": round(in_order_us / (float(inj_ms.mean()) * 1e3), 3),
+            "note": "one request at a time on one stream: retrieval (score + top-k), then fs_inject "
+                    "(plan kernel + row kernel); retrieve and inject are the back-to-back averages"},
         "inject_cold": {
             "note": "each inject alone after a 1 GiB write that evicts the MALL and L2, own HIP events",
             "launches": n_cold,
@@ -310,10 +342,16 @@ def main():
             "ms_p10": round(float(np.percentile(cold_ms, 10)), 5),
             "ms_p90": round(float(np.percentile(cold_ms, 90)), 5),
             "GBps_median": round(float(np.median(inject_bytes[:n_cold] / (cold_ms * 1e-3) / 1e9)), 1)},
-        "roofline": {"bound": "hbm", "kernel": "fs_inject_kernel<128>",
+        "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": float(inject_bytes.mean()), "traffic": traffic},
+                     "bytes_per_launch": float(inject_bytes.mean()), "traffic": traffic,
+                     "cold": {"launches": n_cold,
+                              "ms_median": round(float(np.median(row_cold_ms)), 5),
+                              "ms_p10": round(float(np.percentile(row_cold_ms, 10)), 5),
+                              "ms_p90": round(float(np.percentile(row_cold_ms, 90)), 5),
+                              "achieved_median": round(float(np.median(row_cold_gbs)), 1),
+                              "frac_median": round(float(np.median(row_cold_gbs)) / HBM_PEAK_GBS, 4)}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -804,15 +842,31 @@ def host_cpu_model() -> str:
     return "unknown"
 
 
+def cpu_share() -> tuple[int, dict]:
+    """Threads for the all-cores leg: the CPUs this process may run on,
+    capped by OMP_NUM_THREADS when that is set (the CPU share a job is given
+    on a shared host), with the counts it came from."""
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    share = affinity
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        share = min(share, int(omp))
+    return share, {"host_cpus": os.cpu_count(), "affinity_cpus": affinity,
+                   "OMP_NUM_THREADS": omp or None}
+
+
 def cpu_baseline(wl, ds, layers, n_req, max_host_bytes=16 << 30):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     retrieve + compose + rotate + scatter for ``n_req`` requests, over the
     resident layers whose arenas fit ``max_host_bytes`` of host memory (all of
-    them for the Llama-shaped store).  Timed twice: on one thread (BLAS
-    limited to one thread too), and on all the host cores given to the
-    process (at most 16), each request's layers split over a thread pool
-    (numpy releases the interpreter lock inside its array operations).  Same
-    algorithmic-bytes accounting."""
+    them for the Llama-shaped store).  Timed on every core of the process's
+    CPU share (cpu_share): each request's retrieval with BLAS on that many
+    threads, then its layers split over a thread pool of that size (numpy
+    releases the interpreter lock inside its array operations); and beside
+    it on one thread.  Same algorithmic-bytes accounting."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
@@ -849,31 +903,27 @@ def cpu_baseline(wl, ds, layers, n_req, max_host_bytes=16 << 30):
             L = [f.result() for f in futs][0]
         return 8 * L * nl * s.num_kv_heads * s.head_dim + 4 * n_user * s.embed_dim
 
+    share, counts = cpu_share()
+    nt = max(1, share)
+    chunks = [c for c in (use[j::nt] for j in range(nt)) if c]
+    with threadpool_limits(limits=nt), ThreadPoolExecutor(len(chunks)) as pool:
+        t1 = time.perf_counter()
+        total_all = sum(one_request(i, pool, chunks) for i in range(n_req))
+        dt_all = time.perf_counter() - t1
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        total_bytes = sum(one_request(i) for i in range(n_req))
+        total_one = sum(one_request(i) for i in range(n_req))
         dt = time.perf_counter() - t0
-        try:
-            ncore = len(os.sched_getaffinity(0))
-        except AttributeError:
-            ncore = os.cpu_count() or 1
-        nt = max(1, min(16, ncore, nl))
-        chunks = [use[j::nt] for j in range(nt)]
-        with ThreadPoolExecutor(nt) as pool:
-            t1 = time.perf_counter()
-            total_all = sum(one_request(i, pool, chunks) for i in range(n_req))
-            dt_all = time.perf_counter() - t1
-    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s",
-            "requests_per_s": round(n_req / dt, 4), "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 2),
+    return {"value": round(total_all / dt_all / 1e9, 4), "unit": "GB/s",
+            "requests_per_s": round(n_req / dt_all, 4), "cores": nt, "kind": "oracle",
+            "seconds": round(dt_all, 2),
             "sample": f"{n_req} request(s) of the {s.name} workload (the first request of each "
-                      f"set), {nl} layer(s), k={wl.k}: numpy fp64 oracle, one thread",
-            "cpu_model": host_cpu_model(),
-            "all_cores": {"value": round(total_all / dt_all / 1e9, 4), "unit": "GB/s",
-                          "requests_per_s": round(n_req / dt_all, 4), "cores": nt,
-                          "seconds": round(dt_all, 2),
-                          "sample": "the same requests, each request's layers split over a pool of "
-                                    f"{nt} threads"}}
+                      f"set), {nl} layer(s), k={wl.k}: numpy fp64 oracle, retrieval with BLAS on {nt} "
+                      f"threads, each request's layers split over a pool of {min(nt, nl)} threads",
+            "cpu_model": host_cpu_model(), **counts,
+            "one_thread": {"value": round(total_one / dt / 1e9, 4), "unit": "GB/s",
+                           "requests_per_s": round(n_req / dt, 4), "cores": 1,
+                           "seconds": round(dt, 2), "sample": "the same requests on one thread"}}
 
 
 if __name__ == "__main__":

@@ -40,6 +40,7 @@ namespace {
 using fsd::bf16_hi;
 using fsd::bf16_lo;
 using fsd::f64_to_bf16_bits;
+using fsd::sincos_angle;
 using fsd::wave_or;
 
 constexpr int kThreads = 64;        // one wave per fetch block
@@ -309,6 +310,13 @@ __device__ __forceinline__ uint32_t partner(uint32_t v) {
     }
 }
 
+// The first workgroup of the launch checks the plan's key even when its
+// request is empty (a live one checks it on its way), so a plan that is not
+// this call's is reported whatever its lengths hold.
+__device__ __forceinline__ void plan_check_once(const FlatArgs& a) {
+    if (threadIdx.x == 0 && sload(&a.hdr->key) != a.key) atomicOr(a.err, FS_ERR_PLAN);
+}
+
 // Rotate-half of one 16-byte vector (8 bf16) of a K row: the first half's
 // lanes compute y_i = x_i c - x_{i+D/2} s, the second half's
 // y_{i+D/2} = x_{i+D/2} c + x_i s, each from its own vector and its
@@ -341,10 +349,10 @@ __device__ __forceinline__ u32x4 rotate_vec(u32x4 x, int vec, const double2* row
 }
 
 // cos/sin(p * w_i) of kTok rows of the workgroup (row j at position
-// start + min(t0 + j, L - 1)) into LDS, entry j * D/2 + i.  The position is
-// formed before the range test: with it inside, the compiler evaluates the
-// large-argument reduction of sincos on every lane instead of branching
-// around it, which made the launch 3% slower.
+// start + min(t0 + j, L - 1)) into LDS, entry j * D/2 + i.  The angle lies
+// below 2^31, so a reduction by pi/2 in three parts covers it with no
+// large-argument path (the library's sincos carries one, and computing it on
+// every lane beside the short path cost the launch 3%).
 template <int D, int kTok>
 __device__ __forceinline__ void fill_cs(double2* s_cs, const double* w_e, int start, int t0, int L) {
     constexpr int kE = kTok * (D / 2);
@@ -352,11 +360,10 @@ __device__ __forceinline__ void fill_cs(double2* s_cs, const double* w_e, int st
 #pragma unroll
     for (int q = 0; q < kEPT; ++q) {
         const int e = static_cast<int>(threadIdx.x) + q * kFlatThreads;
-        const int tt = min(t0 + e / (D / 2), L - 1);
-        const double x = static_cast<double>(start + tt) * w_e[q];
         if (e < kE) {
+            const int tt = min(t0 + e / (D / 2), L - 1);
             double sv, cv;
-            sincos(x, &sv, &cv);
+            sincos_angle(static_cast<double>(start + tt) * w_e[q], &sv, &cv);
             s_cs[e] = make_double2(cv, sv);
         }
     }
@@ -403,7 +410,10 @@ __global__ __launch_bounds__(kFlatThreads) void fs_row_kernel(FlatArgs a) {
     const PlanReq rq = sload(a.req + b);
     const int L = rq.len;
     const int t0 = kLg <= 8 ? unit * kTok : unit >> kSplit;    // first row of the workgroup
-    if (t0 >= L) return;
+    if (t0 >= L) {
+        if ((blockIdx.x | blockIdx.y | blockIdx.z) == 0) plan_check_once(a);
+        return;
+    }
     const int r = kLg <= 8 ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> kLg) : 0;
     const int vec = kLg <= 8 ? static_cast<int>(threadIdx.x) & ((1 << kLg) - 1)
                              : ((unit & ((1 << kSplit) - 1)) << 8) + static_cast<int>(threadIdx.x);
@@ -499,7 +509,10 @@ __global__ __launch_bounds__(kFlatThreads) void fs_short_kernel(FlatArgs a) {
     const int tw0 = tf + wave * kRPW;                  // the wave's first row
     const PlanReq rq = sload(a.req + b);
     const int L = rq.len;
-    if (tf >= L) return;
+    if (tf >= L) {
+        if ((blockIdx.x | blockIdx.y | blockIdx.z) == 0) plan_check_once(a);
+        return;
+    }
 
     double w_e[kEPT];
     if (kind == 0) {

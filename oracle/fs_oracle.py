@@ -33,7 +33,7 @@ What the pages fix, and the readings taken where they are silent:
   * RoPE variant (the pages name the models, not the variant): rotate-half
     pairing (element i with i + D/2), frequency w_i = theta^(-2i/D), no
     frequency scaling.
-  * Values are "raw" [online]: copied byte for byte.
+  * Values are stored and injected unchanged [online]: copied byte for byte.
   * Keys are produced in bf16: the exact fp64 rotation rounded once to the
     nearest bf16, ties to even.
 
@@ -125,9 +125,9 @@ def decisive_gap(scores: Sequence[float], k: int) -> float:
 
 def retrieve(emb: np.ndarray, user_fact_begin: np.ndarray, user: int,
              query: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Top-k facts of one user's store for one query [abstract: "retrieves
-    relevant facts at serving time"].  Returns (global fact ids, scores),
-    both of length k with -1 / -inf padding past min(k, N_user)."""
+    """Top-k facts of one user's store for one query: the retrieval step that
+    runs when a request is served [abstract].  Returns (global fact ids,
+    scores), both of length k with -1 / -inf padding past min(k, N_user)."""
     a, b = int(user_fact_begin[user]), int(user_fact_begin[user + 1])
     s = score(emb[a:b], query)
     local = select_topk(s, k)

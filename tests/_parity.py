@@ -128,27 +128,12 @@ def written_mask(wl: synth.Workload, ids_by_req: Dict[int, np.ndarray], num_bloc
     return m
 
 
-def table_mask(wl: synth.Workload, requests: Sequence[int], num_blocks: int):
-    """Boolean [num_blocks, block_size]: every slot of every block that the
-    listed requests' block tables reference."""
-    s = wl.shape
-    m = np.zeros((num_blocks, s.block_size), bool)
-    for b in requests:
-        t = wl.block_table[b]
-        m[t[(t >= 0) & (t < num_blocks)]] = True
-    return m
-
-
-def check_sentinel(kc: list, vc: list, mask: np.ndarray, layer_idx: Sequence[int],
-                   skip: Optional[np.ndarray] = None) -> None:
+def check_sentinel(kc: list, vc: list, mask: np.ndarray, layer_idx: Sequence[int]) -> None:
     """Every slot outside ``mask`` still holds the sentinel, in every byte, and
-    every slot inside it was written.  Slots in ``skip`` are not examined
-    (blocks of requests whose segments were not computed by the oracle)."""
+    every slot inside it was written."""
     sent = np.int16(np.uint16(synth.SENTINEL_BITS).view(np.int16)).item()
-    if skip is None:
-        skip = np.zeros_like(mask)
-    keep = torch.from_numpy(~mask & ~skip).cuda()
-    wrote = torch.from_numpy(mask & ~skip).cuda()
+    keep = torch.from_numpy(~mask).cuda()
+    wrote = torch.from_numpy(mask).cuda()
     for li in layer_idx:
         for name, c in (("K", kc[li]), ("V", vc[li])):
             untouched = c.view(torch.int16)[keep]

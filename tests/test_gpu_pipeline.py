@@ -248,3 +248,65 @@ def test_planned_inject_equals_fused_inject():
     o = check_retrieval(wl0, rid.cpu().numpy(), scores.cpu().numpy(), ntok.cpu().numpy(), [0], k)
     check_injection(wl0, ds, pools[0][0], pools[0][1], o, [0, 3])
     ds.close()
+
+
+def test_planned_inject_refuses_a_foreign_plan():
+    """fs_inject_planned with a plan that is not this call's: never written
+    (zeros), random bytes, or written for another batch, k, cache size or
+    store.  Each sets FS_ERR_PLAN and leaves every cache byte as it was; the
+    call's own plan then writes what fs_inject writes."""
+    wl = synth.make_workload("concurrent", num_users=4, facts_per_user=120, batch=4)
+    s = wl.shape
+    layers = [0, 1]
+    B, k = s.batch, wl.k
+    mb = wl.block_table.shape[1]
+    say("foreign plans: building two stores over the same shapes")
+    ds = build_store(wl, layers)
+    ds2 = build_store(wl, layers)
+    req = request_tensors(wl)
+    ids = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    fs.fs_retrieve_topk(ds.store, B, req["user"], req["query"], k, ids, None, None)
+    kc, vc = synth.make_caches(wl, layers, "cuda")
+    nb = kc[0].shape[0]
+    tb = fs.CacheTable(ds.store, kc, vc, nb)
+    size = fs.fs_inject_plan_size(ds.store, B)
+    sent = np.int16(np.uint16(synth.SENTINEL_BITS).view(np.int16)).item()
+
+    def plan_with(store, batch=B, kk=k, num_blocks=nb):
+        p = torch.zeros(size, dtype=torch.uint8, device="cuda")
+        fs.fs_plan_inject(store, batch, req["user"][:batch], ids[:batch, :kk].contiguous(), kk,
+                          req["block_table"][:batch], mb, req["start_pos"][:batch], num_blocks, p)
+        return p
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    cases = {
+        "never written": torch.zeros(size, dtype=torch.uint8, device="cuda"),
+        "random bytes": torch.randint(0, 256, (size,), generator=g, device="cuda", dtype=torch.uint8),
+        "batch 2": plan_with(ds.store, batch=2),
+        "k - 1": plan_with(ds.store, kk=k - 1),
+        "num_blocks + 8": plan_with(ds.store, num_blocks=nb + 8),
+        "other store": plan_with(ds2.store),
+    }
+    torch.cuda.synchronize()
+    assert fs.fs_poll_errors(ds.store) == 0 and fs.fs_poll_errors(ds2.store) == 0
+    for name, p in cases.items():
+        say(f"foreign plans: {name}")
+        fs.fs_inject_planned(ds.store, fs.FS_ALL_LAYERS, B, k, p, tb)
+        torch.cuda.synchronize()
+        assert fs.fs_poll_errors(ds.store) == fs.FS_ERR_PLAN, name
+        for l in range(len(layers)):
+            assert bool((kc[l].view(torch.int16) == sent).all()), f"{name}: layer {l} K written"
+            assert bool((vc[l].view(torch.int16) == sent).all()), f"{name}: layer {l} V written"
+    say("foreign plans: the call's own plan")
+    fs.fs_inject_planned(ds.store, fs.FS_ALL_LAYERS, B, k, plan_with(ds.store), tb)
+    rk, rv = synth.make_caches(wl, layers, "cuda")
+    fs.fs_inject(ds.store, fs.FS_ALL_LAYERS, B, req["user"], ids, k, req["block_table"], mb,
+                 req["start_pos"], rk, rv, nb)
+    torch.cuda.synchronize()
+    assert fs.fs_poll_errors(ds.store) == 0
+    for l in range(len(layers)):
+        assert torch.equal(_bits(kc[l]), _bits(rk[l])), f"layer {l} K"
+        assert torch.equal(_bits(vc[l]), _bits(rv[l])), f"layer {l} V"
+    ds.close()
+    ds2.close()
