@@ -320,36 +320,55 @@ __device__ __forceinline__ void plan_check_once(const FlatArgs& a) {
 // Rotate-half of one 16-byte vector (8 bf16) of a K row: the first half's
 // lanes compute y_i = x_i c - x_{i+D/2} s, the second half's
 // y_{i+D/2} = x_{i+D/2} c + x_i s, each from its own vector and its
-// partner's; the vector holds pairs i = 8*tl .. 8*tl+7 and cp points at the
-// row's cos/sin entry 8*tl.
+// partner's; the vector holds pairs i = 8*tl .. 8*tl+7.  The row's cos/sin
+// table is stored transposed (pair 8*tl + k at k * D/16 + tl), so the lanes
+// of a half head read consecutive entries.  The sign is applied to the
+// partner's bf16 sign bit (exact) rather than by a multiply.
+//
+// Narrowing to bf16: the fp64 value rounded to fp32 (nearest) and then to
+// bf16 (nearest even) equals its direct rounding to bf16 unless the fp32
+// value sits exactly on a bf16 midpoint (low 16 bits 0x8000), the one case
+// a double rounding can decide wrongly; a wave with such a lane redoes the
+// vector with the exact narrowing (round-to-odd to fp32 first).
 template <int D>
 __device__ __forceinline__ u32x4 rotate_vec(u32x4 x, int vec, const double2* row_cs) {
     constexpr int kHalfV = D / 16;
-    u32x4 p;
-    p.x = partner<D>(x.x);
-    p.y = partner<D>(x.y);
-    p.z = partner<D>(x.z);
-    p.w = partner<D>(x.w);
     const int vh = vec & (D / 8 - 1);
     const bool second = vh >= kHalfV;
     const int tl = second ? vh - kHalfV : vh;
-    const double sg = second ? 1.0 : -1.0;
-    const double2* cp = row_cs + 8 * tl;
-    u32x4 y;
+    const uint32_t neg = second ? 0u : 0x80008000u;
+    u32x4 p;
+    p.x = partner<D>(x.x) ^ neg;
+    p.y = partner<D>(x.y) ^ neg;
+    p.z = partner<D>(x.z) ^ neg;
+    p.w = partner<D>(x.w) ^ neg;
+    const double2* cp = row_cs + tl;
+    double yd[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const double2 c0 = cp[2 * e], c1 = cp[2 * e + 1];
-        const double y0 =
-            fma(static_cast<double>(bf16_lo(x[e])), c0.x, sg * (static_cast<double>(bf16_lo(p[e])) * c0.y));
-        const double y1 =
-            fma(static_cast<double>(bf16_hi(x[e])), c1.x, sg * (static_cast<double>(bf16_hi(p[e])) * c1.y));
-        y[e] = f64_to_bf16_bits(y0) | (f64_to_bf16_bits(y1) << 16);
+        const double2 c0 = cp[(2 * e) * kHalfV], c1 = cp[(2 * e + 1) * kHalfV];
+        yd[2 * e] = fma(static_cast<double>(bf16_lo(x[e])), c0.x, static_cast<double>(bf16_lo(p[e])) * c0.y);
+        yd[2 * e + 1] = fma(static_cast<double>(bf16_hi(x[e])), c1.x, static_cast<double>(bf16_hi(p[e])) * c1.y);
+    }
+    u32x4 y;
+    bool tie = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t u0 = __float_as_uint(static_cast<float>(yd[2 * e]));
+        const uint32_t u1 = __float_as_uint(static_cast<float>(yd[2 * e + 1]));
+        tie |= (u0 & 0xFFFFu) == 0x8000u || (u1 & 0xFFFFu) == 0x8000u;
+        y[e] = ((u0 + 0x7FFFu + ((u0 >> 16) & 1u)) >> 16) | ((u1 + 0x7FFFu + ((u1 >> 16) & 1u)) & 0xFFFF0000u);
+    }
+    if (__builtin_amdgcn_ballot_w64(tie)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = f64_to_bf16_bits(yd[2 * e]) | (f64_to_bf16_bits(yd[2 * e + 1]) << 16);
     }
     return y;
 }
 
 // cos/sin(p * w_i) of kTok rows of the workgroup (row j at position
-// start + min(t0 + j, L - 1)) into LDS, entry j * D/2 + i.  The angle lies
+// start + min(t0 + j, L - 1)) into LDS, row j at j * D/2, pair i of it
+// transposed as rotate_vec reads it.  The angle lies
 // below 2^31, so a reduction by pi/2 in three parts covers it with no
 // large-argument path (the library's sincos carries one, and computing it on
 // every lane beside the short path cost the launch 3%).
@@ -362,9 +381,10 @@ __device__ __forceinline__ void fill_cs(double2* s_cs, const double* w_e, int st
         const int e = static_cast<int>(threadIdx.x) + q * kFlatThreads;
         if (e < kE) {
             const int tt = min(t0 + e / (D / 2), L - 1);
+            const int i = e & (D / 2 - 1);
             double sv, cv;
             sincos_angle(static_cast<double>(start + tt) * w_e[q], &sv, &cv);
-            s_cs[e] = make_double2(cv, sv);
+            s_cs[(e - i) + (i & 7) * (D / 16) + (i >> 3)] = make_double2(cv, sv);
         }
     }
 }
