@@ -114,6 +114,7 @@ typedef int32_t fs_status;
 #define FS_MAX_LAYERS      128
 #define FS_MAX_K           1024
 #define FS_PLAN_SLOTS      4      /* fs_inject plan slots per device store     */
+#define FS_NOALLOC_PLAN_BYTES 0x400000u  /* fs_inject_noalloc plan buffer per GPU (4 MiB) */
 
 #define FS_KV_DEVICE       0      /* K/V arenas in device memory              */
 #define FS_KV_PINNED_HOST  1      /* K/V arenas in page-locked host memory    */
@@ -260,6 +261,28 @@ FS_API fs_status fs_inject_layers(const fs_store* store, int32_t layer_begin, in
                            const int32_t* start_pos,
                            void* const* k_cache, void* const* v_cache,
                            int32_t num_blocks, void* stream);
+
+/*
+ * fs_inject_noalloc — fs_inject for callers that cannot allocate device
+ * memory while they run (code captured into a HIP graph, a serving loop that
+ * must not call hipMalloc, a harness that forbids it).  Same arguments,
+ * result, host checks and device-checked errors as fs_inject; the call
+ * allocates nothing.  Its plan goes into one static device buffer of
+ * FS_NOALLOC_PLAN_BYTES (4 MiB) per GPU instead of a plan slot of the store:
+ *   - a batch whose plan (fs_inject_plan_size(batch) bytes) exceeds it
+ *     returns FS_E_RANGE and enqueues nothing;
+ *   - every fs_inject_noalloc call on a GPU, from any store, uses that one
+ *     buffer, so calls that overlap on one GPU (different streams, or
+ *     different host threads) race: the caller orders them;
+ *   - the buffer keeps the last call's plan; each call writes every entry
+ *     its injection reads, so nothing needs clearing.
+ * The buffer's device address is looked up on the first call on each GPU.
+ */
+FS_API fs_status fs_inject_noalloc(const fs_store* store, int32_t layer, int32_t batch,
+                                   const int32_t* user, const int32_t* ids, int32_t k,
+                                   const int32_t* block_table, int32_t max_blocks,
+                                   const int32_t* start_pos, void* const* k_cache,
+                                   void* const* v_cache, int32_t num_blocks, void* stream);
 
 /*
  * fs_plan_inject, fs_inject_planned — fs_inject's two kernels as two calls,

@@ -132,6 +132,9 @@ struct InjectLaunch {
     bool inject = false;
 };
 hipError_t fsi_launch_inject(const InjectLaunch& a);
+// fs_inject_noalloc's plan buffer on `device`: its device address (looked up
+// once per device) and size in bytes
+hipError_t fsi_noalloc_scratch(int device, void** ptr, size_t* bytes);
 
 // Layout of an inject plan for `batch` requests:
 //   PlanHeader (32 bytes); then per request {segment length (0 when

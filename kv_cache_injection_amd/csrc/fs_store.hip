@@ -371,11 +371,13 @@ fs_status fs_retrieve_topk(const fs_store* store, int32_t batch, const int32_t* 
     return FS_OK;
 }
 
-fs_status fs_inject_layers(const fs_store* store, int32_t layer_begin, int32_t layer_end, int32_t batch,
-                           const int32_t* user, const int32_t* ids, int32_t k, const int32_t* block_table,
-                           int32_t max_blocks, const int32_t* start_pos, void* const* k_cache,
-                           void* const* v_cache, int32_t num_blocks, void* stream) {
-    g_msg[0] = 0;
+namespace {
+
+// the host checks of fs_inject_layers and fs_inject_noalloc
+fs_status check_inject(const fs_store* store, int32_t layer_begin, int32_t layer_end, int32_t batch,
+                       const int32_t* user, const int32_t* ids, int32_t k, const int32_t* block_table,
+                       int32_t max_blocks, const int32_t* start_pos, void* const* k_cache,
+                       void* const* v_cache, int32_t num_blocks) {
     if (!store) return fail(FS_E_ARG, "null store");
     const fs_store_desc& d = store->desc;
     if (layer_begin < 0 || layer_end > d.num_layers || layer_begin >= layer_end)
@@ -395,7 +397,19 @@ fs_status fs_inject_layers(const fs_store* store, int32_t layer_begin, int32_t l
         if (!aligned(k_cache[l], 16) || !aligned(v_cache[l], 16))
             return fail(FS_E_ARG, "layer %d cache not 16-byte aligned", l);
     }
-    if (k == 0) return FS_OK;
+    return FS_OK;
+}
+
+}  // namespace
+
+fs_status fs_inject_layers(const fs_store* store, int32_t layer_begin, int32_t layer_end, int32_t batch,
+                           const int32_t* user, const int32_t* ids, int32_t k, const int32_t* block_table,
+                           int32_t max_blocks, const int32_t* start_pos, void* const* k_cache,
+                           void* const* v_cache, int32_t num_blocks, void* stream) {
+    g_msg[0] = 0;
+    const fs_status c = check_inject(store, layer_begin, layer_end, batch, user, ids, k, block_table, max_blocks,
+                                     start_pos, k_cache, v_cache, num_blocks);
+    if (c != FS_OK || k == 0) return c;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     InjectLaunch a{store, layer_begin, layer_end, batch, user, ids, k, block_table, max_blocks, start_pos,
                    k_cache, v_cache, num_blocks, s};
@@ -406,6 +420,38 @@ fs_status fs_inject_layers(const fs_store* store, int32_t layer_begin, int32_t l
     hipError_t e = hipSuccess;
     a.plan_out = acquire_slot(store, s, &e);
     if (e != hipSuccess) return hip_fail(e, "plan slot hand-over");
+    e = fsi_launch_inject(a);
+    if (e != hipSuccess) return hip_fail(e, "inject launch");
+    return FS_OK;
+}
+
+fs_status fs_inject_noalloc(const fs_store* store, int32_t layer, int32_t batch, const int32_t* user,
+                            const int32_t* ids, int32_t k, const int32_t* block_table, int32_t max_blocks,
+                            const int32_t* start_pos, void* const* k_cache, void* const* v_cache,
+                            int32_t num_blocks, void* stream) {
+    g_msg[0] = 0;
+    if (!store) return fail(FS_E_ARG, "null store");
+    const int32_t nl = store->desc.num_layers;
+    if (layer != FS_ALL_LAYERS && (layer < 0 || layer >= nl))
+        return fail(FS_E_RANGE, "layer %d outside [0, %d)", layer, nl);
+    const int32_t lb = layer == FS_ALL_LAYERS ? 0 : layer;
+    const int32_t le = layer == FS_ALL_LAYERS ? nl : layer + 1;
+    const fs_status c = check_inject(store, lb, le, batch, user, ids, k, block_table, max_blocks, start_pos,
+                                     k_cache, v_cache, num_blocks);
+    if (c != FS_OK) return c;
+    const size_t need = fsi_plan_bytes(store, batch);
+    if (need > FS_NOALLOC_PLAN_BYTES)
+        return fail(FS_E_RANGE, "plan of %zu bytes for %d requests exceeds the %zu-byte static plan buffer", need,
+                    batch, static_cast<size_t>(FS_NOALLOC_PLAN_BYTES));
+    if (k == 0) return FS_OK;
+    void* buf = nullptr;
+    size_t bytes = 0;
+    hipError_t e = fsi_noalloc_scratch(store->device, &buf, &bytes);
+    if (e != hipSuccess) return hip_fail(e, "static plan buffer lookup");
+    InjectLaunch a{store, lb, le, batch, user, ids, k, block_table, max_blocks, start_pos,
+                   k_cache, v_cache, num_blocks, reinterpret_cast<hipStream_t>(stream)};
+    a.inject = true;
+    a.plan_out = buf;
     e = fsi_launch_inject(a);
     if (e != hipSuccess) return hip_fail(e, "inject launch");
     return FS_OK;

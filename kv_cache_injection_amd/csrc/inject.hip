@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "fs_device.h"
 #include "fs_internal.h"
@@ -852,6 +853,42 @@ hipError_t launch_fetch(const FetchLaunch& r) {
 }
 
 }  // namespace
+
+// The plan buffer of fs_inject_noalloc: FS_NOALLOC_PLAN_BYTES of device
+// memory per GPU, in the code object (each device that loads the library holds
+// its own copy until the process ends), so a call allocates nothing.  Host
+// code never names the array: its device address comes from
+// hipGetSymbolAddress, once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[FS_NOALLOC_PLAN_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t fsi_noalloc_scratch(int device, void** ptr, size_t* bytes) {
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != device) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[device] = p;
+    }
+    *ptr = g_scratch_ptr[device];
+    *bytes = sizeof(scratch);
+    return hipSuccess;
+}
 
 hipError_t fsi_launch_inject(const InjectLaunch& r) {
     switch (r.st->desc.head_dim) {

@@ -40,11 +40,13 @@ FS_ALL_LAYERS = -1
 FS_MAX_LAYERS = 128
 FS_MAX_K = 1024
 FS_PLAN_SLOTS = 4
+FS_NOALLOC_PLAN_BYTES = 4 << 20
 FS_KV_DEVICE = 0
 FS_KV_PINNED_HOST = 1
 
 EXPORTS = ("fs_create_store", "fs_destroy_store", "fs_retrieve_topk", "fs_inject",
-           "fs_inject_layers", "fs_inject_plan_size", "fs_plan_inject", "fs_inject_planned", "fs_fetch_async", "fs_attend_prefill", "fs_attend_workspace_size", "fs_ingest_init",
+           "fs_inject_layers", "fs_inject_noalloc", "fs_inject_plan_size", "fs_plan_inject",
+           "fs_inject_planned", "fs_fetch_async", "fs_attend_prefill", "fs_attend_workspace_size", "fs_ingest_init",
            "fs_ingest_facts", "fs_evict_fact", "fs_store_live", "fs_ivf_build",
            "fs_ivf_destroy", "fs_ivf_arrays", "fs_ivf_retrieve_topk", "fs_poll_errors",
            "fs_strerror", "fs_last_error_message")
@@ -102,6 +104,7 @@ def _load() -> ctypes.CDLL:
         "fs_retrieve_topk": (i32, [P, i32, P, P, i32, P, P, P, P]),
         "fs_inject": (i32, [P, i32, i32, P, P, i32, P, i32, P, P, P, i32, P]),
         "fs_inject_layers": (i32, [P, i32, i32, i32, P, P, i32, P, i32, P, P, P, i32, P]),
+        "fs_inject_noalloc": (i32, [P, i32, i32, P, P, i32, P, i32, P, P, P, i32, P]),
         "fs_inject_plan_size": (i32, [P, i32, ctypes.POINTER(ctypes.c_size_t)]),
         "fs_plan_inject": (i32, [P, i32, P, P, i32, P, i32, P, i32, P, ctypes.c_size_t, P]),
         "fs_inject_planned": (i32, [P, i32, i32, i32, i32, P, ctypes.c_size_t, P, P, i32, P]),
@@ -290,6 +293,29 @@ def fs_inject(store, layer: int, batch: int, user: torch.Tensor, ids: torch.Tens
         _ptr(start_pos, torch.int32, shape=(batch,), name="start_pos"),
         table.k, table.v, table.num_blocks, _stream(stream))
     _check(st, "fs_inject")
+
+
+def fs_inject_noalloc(store, layer: int, batch: int, user: torch.Tensor, ids: torch.Tensor, k: int,
+                      block_table: torch.Tensor, max_blocks: int, start_pos: torch.Tensor,
+                      caches: "CacheTable", stream=None) -> None:
+    """fs_inject with the plan in the library's static per-GPU buffer: the
+    call allocates nothing (calls that overlap on one GPU race)."""
+    if not isinstance(caches, CacheTable):
+        raise TypeError("fs_inject_noalloc takes a CacheTable")
+    if layer == FS_ALL_LAYERS:
+        if not all(caches.present):
+            raise ValueError("FS_ALL_LAYERS needs a cache for every layer")
+    elif 0 <= layer < len(caches.present) and not caches.present[layer]:
+        raise ValueError(f"no cache given for layer {layer}")
+    st = _lib.fs_inject_noalloc(
+        _handle(store), int(layer), int(batch),
+        _ptr(user, torch.int32, shape=(batch,), name="user"),
+        _ptr(ids, torch.int32, shape=(batch, k), name="ids"), int(k),
+        _ptr(block_table, torch.int32, shape=(batch, max_blocks), name="block_table"),
+        int(max_blocks),
+        _ptr(start_pos, torch.int32, shape=(batch,), name="start_pos"),
+        caches.k, caches.v, caches.num_blocks, _stream(stream))
+    _check(st, "fs_inject_noalloc")
 
 
 def fs_inject_layers(store, layer_begin: int, layer_end: int, batch: int, user: torch.Tensor,

@@ -44,7 +44,7 @@ def test_constants_match_header():
         if hasattr(fs, name):
             assert getattr(fs, name) == int(val, 0), name
             checked += 1
-    assert checked == 21
+    assert checked == 22
 
 
 def test_desc_layout_matches_c(tmp_path):
@@ -158,5 +158,6 @@ def test_null_store_is_rejected_everywhere():
     assert L.fs_inject_plan_size(None, 1, ctypes.byref(n)) == fs.FS_E_ARG
     assert L.fs_plan_inject(None, 1, FAKE, FAKE, 1, FAKE, 4, FAKE, 4, FAKE, 1 << 20, None) == fs.FS_E_ARG
     assert L.fs_inject_planned(None, 0, 1, 1, 1, FAKE, 1 << 20, arr, arr, 4, None) == fs.FS_E_ARG
+    assert L.fs_inject_noalloc(None, 0, 1, FAKE, FAKE, 1, FAKE, 1, FAKE, arr, arr, 4, None) == fs.FS_E_ARG
     assert L.fs_poll_errors(None, None, ctypes.byref(flags)) == fs.FS_E_ARG
     assert L.fs_destroy_store(None) == fs.FS_OK
