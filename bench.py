@@ -72,7 +72,8 @@ def parse():
     p.add_argument("--cpu-requests", type=int, default=16,
                    help="requests of the oracle's bounded CPU sample (0 = skip)")
     p.add_argument("--copy-probe", action="store_true",
-                   help="also run a plain 1 GiB device copy (counter calibration)")
+                   help="also time a plain device copy of one inject's bytes (the copy ceiling at this "
+                        "size; the known-size launches the HBM counters are calibrated on)")
     p.add_argument("--overlap", action="store_true",
                    help="layer-pipelined injection on a side stream under a synthetic per-layer forward "
                         "(two bf16 GEMMs per layer), for several layer-chunk plans: how much of the "
@@ -281,18 +282,29 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     traffic = recorded_traffic(args.config, nl)
 
+    copy = None
     if args.copy_probe:
-        a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+        # the copy ceiling at this size: a plain device copy (torch's copy
+        # kernel) of as many bytes as one inject reads and writes, issued back
+        # to back between two events like region 2; also the known-size
+        # launches the HBM counters are calibrated on
+        n16 = int(inject_bytes.mean()) // 4                          # int16 elements each way
+        a = torch.empty(n16, dtype=torch.int16, device="cuda")
         bb = torch.empty_like(a)
         a.fill_(1)
+        bb.copy_(a)
         torch.cuda.synchronize()
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         c0.record()
-        bb.copy_(a)
+        for _ in range(args.steps):
+            bb.copy_(a)
         c1.record()
         torch.cuda.synchronize()
-        print(f"[bench] copy probe: 1 GiB read + 1 GiB write in {c0.elapsed_time(c1):.3f} ms",
-              file=sys.stderr, flush=True)
+        us = c0.elapsed_time(c1) * 1e3 / args.steps
+        copy = {"bytes_per_copy": 4 * n16, "us_avg": round(us, 2),
+                "GBps": round(4 * n16 / (us * 1e-6) / 1e9, 1),
+                "frac": round(4 * n16 / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "note": "torch copy_ of one inject's bytes (half read, half written), back to back"}
         del a, bb
 
     cpu = None
@@ -354,6 +366,8 @@ def main():
                               "frac_median": round(float(np.median(row_cold_gbs)) / HBM_PEAK_GBS, 4)}},
         "cpu_baseline": cpu,
     }
+    if copy is not None:
+        out["copy_probe"] = copy
     print(json.dumps(out), flush=True)
     ds.close()
 

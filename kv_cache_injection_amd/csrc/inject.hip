@@ -54,6 +54,14 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 ld_stream(const FS_GLOBAL u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_stream(FS_GLOBAL u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+// a cache row store: streaming, or through the caches when the launch's
+// writes fit in the last-level cache (a compile-time choice: a branch per
+// store cost the streaming launch 3%)
+template <bool kCached>
+__device__ __forceinline__ void st_row(FS_GLOBAL u32x4* p, u32x4 v) {
+    if constexpr (kCached) *p = v;
+    else st_stream(p, v);
+}
 // a load the caller knows is wave-uniform and not written during the kernel:
 // through the scalar cache (its own counter, so it never waits on the
 // vector loads in flight)
@@ -413,7 +421,7 @@ __device__ __forceinline__ void fill_cs(double2* s_cs, const double* w_e, int st
 // shape: 73 us, against 80 us for a block of 8 tokens x all heads x K and V
 // with a per-block plan and cos/sin table, 75 us for two vectors per lane,
 // and 66 us for the same bytes as a contiguous copy.
-template <int D, int kLg, bool kStaged>
+template <int D, int kLg, bool kStaged, bool kCached>
 __global__ __launch_bounds__(kFlatThreads) void fs_row_kernel(FlatArgs a) {
     constexpr int kSplit = kLg > 8 ? kLg - 8 : 0;              // log2 workgroups per row
     constexpr int kTok = kLg <= 8 ? kFlatThreads >> kLg : 1;   // rows per workgroup
@@ -465,7 +473,7 @@ __global__ __launch_bounds__(kFlatThreads) void fs_row_kernel(FlatArgs a) {
         }
         if (vec >= a.vpr) return;
         const u32x4 x = ld_stream((const FS_GLOBAL u32x4*)(sb + sr * a.row_elems) + vec);
-        st_stream((FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.cache[2 * l + 1]) + dr * a.row_elems) + vec, x);
+        st_row<kCached>((FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.cache[2 * l + 1]) + dr * a.row_elems) + vec, x);
         return;
     }
 
@@ -506,12 +514,13 @@ __global__ __launch_bounds__(kFlatThreads) void fs_row_kernel(FlatArgs a) {
         return;
     }
     const u32x4 y = rotate_vec<D>(x, vec, s_cs + r * (D / 2));
-    if (vec < a.vpr) st_stream((FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.cache[2 * l]) + dr * a.row_elems) + vec, y);
+    if (vec < a.vpr)
+        st_row<kCached>((FS_GLOBAL u32x4*)(static_cast<uint16_t*>(a.cache[2 * l]) + dr * a.row_elems) + vec, y);
 }
 
 // Rows of fewer than 64 vectors (fs_short_kernel): a wave holds 64 >> kLg
 // rows and each lane takes the entry of its own row among the wave's.
-template <int D, int kLg, bool kStaged>
+template <int D, int kLg, bool kStaged, bool kCached>
 __global__ __launch_bounds__(kFlatThreads) void fs_short_kernel(FlatArgs a) {
     constexpr int kVPR = 1 << kLg;
     constexpr int kRPW = 64 >> kLg;                    // rows per wave
@@ -576,14 +585,14 @@ __global__ __launch_bounds__(kFlatThreads) void fs_short_kernel(FlatArgs a) {
     const u32x4 x = ld_stream((const FS_GLOBAL u32x4*)(src_base + (act ? sr * a.row_elems + int64_t(vj) * 8 : 0)));
     asm volatile("" ::: "memory");
     if (kind == 1) {
-        if (act) st_stream((FS_GLOBAL u32x4*)(dst_base + dr * a.row_elems) + vj, x);
+        if (act) st_row<kCached>((FS_GLOBAL u32x4*)(dst_base + dr * a.row_elems) + vj, x);
         if (bad) atomicOr(a.err, FS_ERR_PLAN);
         return;
     }
     fill_cs<D, kTok>(s_cs, w_e, rq.start, tf, L);
     __syncthreads();
     const u32x4 y = rotate_vec<D>(x, vj, s_cs + min(tj - tf, kTok - 1) * (D / 2));
-    if (act) st_stream((FS_GLOBAL u32x4*)(dst_base + dr * a.row_elems) + vj, y);
+    if (act) st_row<kCached>((FS_GLOBAL u32x4*)(dst_base + dr * a.row_elems) + vj, y);
     if (bad) atomicOr(a.err, FS_ERR_PLAN);
 }
 
@@ -738,18 +747,26 @@ hipError_t launch_plan(const InjectLaunch& r, void* plan) {
 // longest padded row the inject kernels are built for: 2^10 vectors (16 KB,
 // e.g. 32 heads of 256 or 64 heads of 128)
 constexpr int kFlatMaxLg = 10;
+// launches expected to write at most this much store through the caches
+constexpr double kCachedWriteBytes = 128.0 * (1 << 20);
+
+template <int D, int kLg, bool kStaged, bool kCached>
+void launch_flat_v(const FlatArgs& a, dim3 grid, hipStream_t s) {
+    if constexpr (kLg >= 6) fs_row_kernel<D, kLg, kStaged, kCached><<<grid, kFlatThreads, 0, s>>>(a);
+    else fs_short_kernel<D, kLg, kStaged, kCached><<<grid, kFlatThreads, 0, s>>>(a);
+}
 
 template <int D, int kLg>
-void dispatch_flat(int lg, const FlatArgs& a, dim3 grid, hipStream_t s) {
+void dispatch_flat(int lg, bool cached, const FlatArgs& a, dim3 grid, hipStream_t s) {
     if constexpr (kLg <= kFlatMaxLg) {
         if (lg != kLg) {
-            dispatch_flat<D, kLg + 1>(lg, a, grid, s);
-        } else if constexpr (kLg >= 6) {
-            if (a.stage_k) fs_row_kernel<D, kLg, true><<<grid, kFlatThreads, 0, s>>>(a);
-            else fs_row_kernel<D, kLg, false><<<grid, kFlatThreads, 0, s>>>(a);
+            dispatch_flat<D, kLg + 1>(lg, cached, a, grid, s);
+        } else if (a.stage_k) {
+            if (cached) launch_flat_v<D, kLg, true, true>(a, grid, s);
+            else launch_flat_v<D, kLg, true, false>(a, grid, s);
         } else {
-            if (a.stage_k) fs_short_kernel<D, kLg, true><<<grid, kFlatThreads, 0, s>>>(a);
-            else fs_short_kernel<D, kLg, false><<<grid, kFlatThreads, 0, s>>>(a);
+            if (cached) launch_flat_v<D, kLg, false, true>(a, grid, s);
+            else launch_flat_v<D, kLg, false, false>(a, grid, s);
         }
     }
 }
@@ -791,6 +808,15 @@ hipError_t launch_flat(const InjectLaunch& r, const void* plan) {
     // end to end); a workgroup past its request's real length exits after
     // reading that length
     const int64_t seg = int64_t(r.k) * st->max_fact_len;
+    // Stores: rows of a launch whose expected writes (k facts of the store's
+    // mean length per request, K and V, every layer) fit in a half of the
+    // 256 MB last-level cache go through the caches, and their write-back
+    // overlaps what follows; larger launches stream past them.  On the
+    // Qwen shape (86 MB) cached stores made the launch 4% faster, on the
+    // Llama shape (195 MB) 8% slower.
+    const double expect = double(r.k) * st->mean_fact_len * r.batch * (r.layer_end - r.layer_begin) * 2.0 *
+                          double(a.row_elems) * 2.0;
+    const bool cached = expect <= kCachedWriteBytes;
     const int64_t units = ((seg << lg) + kFlatThreads - 1) / kFlatThreads;
     if (units > INT32_MAX / 2) return hipErrorInvalidValue;
     a.units = static_cast<int32_t>(std::max<int64_t>(units, 1));
@@ -798,7 +824,7 @@ hipError_t launch_flat(const InjectLaunch& r, const void* plan) {
                     static_cast<unsigned>(r.layer_end - r.layer_begin));
     // a head is D/8 vectors, so rows start at 2^log2(D/8) vectors
     constexpr int kLg0 = D == 64 ? 3 : (D == 128 ? 4 : 5);
-    dispatch_flat<D, kLg0>(lg, a, grid, r.stream);
+    dispatch_flat<D, kLg0>(lg, cached, a, grid, r.stream);
     return hipGetLastError();
 }
 
