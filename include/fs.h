@@ -534,6 +534,28 @@ FS_API fs_status fs_ivf_retrieve_topk(const fs_store* store, const fs_ivf* ivf, 
                                       double* scores, int32_t* num_tokens, void* stream);
 
 /*
+ * fs_check_block_tables — opt-in debug check, on the host, that the cache
+ * blocks a call writes are its own: fs_inject writes request b's segment of
+ * num_tokens[b] tokens at positions start_pos[b] .. start_pos[b] +
+ * num_tokens[b] - 1, through block_table[b][p / block_size] (gist.science
+ * summary, "Phase En-ligne", item "Injection").  The GPU path checks each
+ * entry's range but not that two requests, or two logical blocks of one
+ * request, name the same physical block; this call does, so a caller can
+ * find aliased tables before they corrupt each other's cache.
+ *   All arrays are host memory, read only: block_table [batch][max_blocks],
+ *   start_pos [batch], num_tokens [batch] (e.g. fs_retrieve_topk's output
+ *   copied to the host).  block_size: a power of two; num_blocks >= 1.
+ *   Returns FS_OK when every written block is named once and lies in
+ *   [0, num_blocks); FS_E_BLOCKTABLE on the first violation, with conflict
+ *   (int32 [4], may be null) set to {request, logical block, block id, the
+ *   earlier request naming it or -1 for a range error}; FS_E_ARG on bad
+ *   arguments.  Needs no store and no GPU.
+ */
+FS_API fs_status fs_check_block_tables(int32_t batch, const int32_t* block_table, int32_t max_blocks,
+                                       const int32_t* start_pos, const int32_t* num_tokens,
+                                       int32_t block_size, int32_t num_blocks, int32_t* conflict);
+
+/*
  * fs_poll_errors — synchronise `stream`, return the device error bits
  * accumulated since the last poll in *flags, and clear them.  Returns
  * FS_E_DEVICE when any bit was set, FS_OK otherwise (FS_E_ARG, FS_E_HIP).

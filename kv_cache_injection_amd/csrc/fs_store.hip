@@ -907,6 +907,52 @@ fs_status fs_ivf_retrieve_topk(const fs_store* store, const fs_ivf* ix, int32_t 
     return FS_OK;
 }
 
+fs_status fs_check_block_tables(int32_t batch, const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* start_pos, const int32_t* num_tokens, int32_t block_size,
+                                int32_t num_blocks, int32_t* conflict) {
+    g_msg[0] = 0;
+    if (conflict)
+        for (int i = 0; i < 4; ++i) conflict[i] = -1;
+    if (batch < 0) return fail(FS_E_ARG, "batch %d < 0", batch);
+    if (batch > 0 && (!block_table || !start_pos || !num_tokens)) return fail(FS_E_ARG, "null pointer argument");
+    if (max_blocks < 1) return fail(FS_E_ARG, "max_blocks %d < 1", max_blocks);
+    if (!pow2(block_size)) return fail(FS_E_ARG, "block_size %d is not a power of two", block_size);
+    if (num_blocks < 1) return fail(FS_E_ARG, "num_blocks %d < 1", num_blocks);
+    auto report = [&](int32_t b, int32_t j, int32_t id, int32_t other, const char* what) {
+        if (conflict) {
+            conflict[0] = b;
+            conflict[1] = j;
+            conflict[2] = id;
+            conflict[3] = other;
+        }
+        return fail(FS_E_BLOCKTABLE, "request %d, logical block %d (block id %d): %s", b, j, id, what);
+    };
+    // every written (request, logical block) with its physical id, then
+    // sorted by id: a repeated id is an alias
+    struct Use {
+        int32_t id, b, j;
+    };
+    std::vector<Use> uses;
+    for (int32_t b = 0; b < batch; ++b) {
+        const int64_t s = start_pos[b], L = num_tokens[b];
+        if (L <= 0) continue;
+        if (s < 0) return report(b, -1, -1, -1, "negative start position");
+        const int64_t first = s / block_size, last = (s + L - 1) / block_size;
+        if (last >= max_blocks) return report(b, static_cast<int32_t>(last), -1, -1, "beyond the block table");
+        for (int64_t j = first; j <= last; ++j) {
+            const int32_t id = block_table[int64_t(b) * max_blocks + j];
+            if (id < 0 || id >= num_blocks)
+                return report(b, static_cast<int32_t>(j), id, -1, "block id outside [0, num_blocks)");
+            uses.push_back(Use{id, b, static_cast<int32_t>(j)});
+        }
+    }
+    std::stable_sort(uses.begin(), uses.end(), [](const Use& x, const Use& y) { return x.id < y.id; });
+    for (size_t i = 1; i < uses.size(); ++i)
+        if (uses[i].id == uses[i - 1].id)
+            return report(uses[i].b, uses[i].j, uses[i].id, uses[i - 1].b, "block also written by another entry");
+    return FS_OK;
+}
+
 fs_status fs_poll_errors(const fs_store* store, void* stream, uint32_t* flags) {
     g_msg[0] = 0;
     if (!store || !flags) return fail(FS_E_ARG, "null pointer argument");

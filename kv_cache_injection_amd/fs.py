@@ -16,7 +16,11 @@ from typing import Optional, Sequence
 
 import torch  # loads torch's HIP runtime first, so libfs.so binds to the same one
 
-from .build import LIB_PATH
+from .build import LIB_PATH as _BUILT_LIB
+
+# FS_LIB_PATH selects another build of the same library (e.g. a sanitizer
+# build of the host runtime for the host-only tests)
+LIB_PATH = os.environ.get("FS_LIB_PATH") or _BUILT_LIB
 
 # ---- constants mirrored from include/fs.h (tests check they agree) ---------
 FS_OK = 0
@@ -48,7 +52,7 @@ EXPORTS = ("fs_create_store", "fs_destroy_store", "fs_retrieve_topk", "fs_inject
            "fs_inject_layers", "fs_inject_noalloc", "fs_inject_plan_size", "fs_plan_inject",
            "fs_inject_planned", "fs_fetch_async", "fs_attend_prefill", "fs_attend_workspace_size", "fs_ingest_init",
            "fs_ingest_facts", "fs_evict_fact", "fs_store_live", "fs_ivf_build",
-           "fs_ivf_destroy", "fs_ivf_arrays", "fs_ivf_retrieve_topk", "fs_poll_errors",
+           "fs_ivf_destroy", "fs_ivf_arrays", "fs_ivf_retrieve_topk", "fs_poll_errors", "fs_check_block_tables",
            "fs_strerror", "fs_last_error_message")
 
 
@@ -121,6 +125,7 @@ def _load() -> ctypes.CDLL:
         "fs_ivf_arrays": (i32, [P, ctypes.POINTER(fs_ivf_view)]),
         "fs_ivf_retrieve_topk": (i32, [P, P, i32, P, i32, i32, P, P, P, P]),
         "fs_poll_errors": (i32, [P, P, ctypes.POINTER(ctypes.c_uint32)]),
+        "fs_check_block_tables": (i32, [i32, P, i32, P, P, i32, i32, P]),
         "fs_strerror": (ctypes.c_char_p, [i32]),
         "fs_last_error_message": (ctypes.c_char_p, []),
     }
@@ -132,6 +137,30 @@ def _load() -> ctypes.CDLL:
 
 
 _lib = _load()
+
+
+def fs_check_block_tables(block_table, start_pos, num_tokens, block_size: int, num_blocks: int):
+    """Opt-in debug check on the host that no cache block is written twice
+    by one call (fs_check_block_tables).  Arrays: host int32 (numpy or CPU
+    tensors).  Returns None; raises FsError (FS_E_BLOCKTABLE) naming the
+    first conflict, whose [request, logical block, block id, other request]
+    is in the error's ``conflict`` attribute."""
+    import numpy as np
+
+    def host(x):
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().numpy()
+        return np.ascontiguousarray(x, dtype=np.int32)
+    bt, sp, nt = host(block_table), host(start_pos), host(num_tokens)
+    if bt.ndim != 2 or sp.shape != (bt.shape[0],) or nt.shape != (bt.shape[0],):
+        raise ValueError("block_table [batch, max_blocks], start_pos and num_tokens [batch]")
+    out = (ctypes.c_int32 * 4)()
+    st = _lib.fs_check_block_tables(int(bt.shape[0]), bt.ctypes.data, int(bt.shape[1]), sp.ctypes.data,
+                                    nt.ctypes.data, int(block_size), int(num_blocks), out)
+    if st != FS_OK:
+        err = FsError(st, "fs_check_block_tables", _lib.fs_last_error_message().decode())
+        err.conflict = list(out)
+        raise err
 
 
 def fs_strerror(status: int) -> str:
