@@ -346,11 +346,17 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
         // scores i = tid + j*blockDim.x: the first kKeep stay in registers
         // for the later passes, the rest (large users) are re-read
         double xv[kKeep];
+        // and, for plain requests, their facts' lengths, fetched with them:
+        // a candidate's length loaded only once it is found costs a round
+        // trip per candidate a thread holds
+        int32_t lv[kKeep];
+        const bool pre_len = !mapped && a.fact_len;
         const int tail0 = tid + kKeep * kTopkThreads;
 #pragma unroll
         for (int j = 0; j < kKeep; ++j) {
             const int i = tid + j * kTopkThreads;
             xv[j] = i < n ? sc[i] : 0.0;
+            lv[j] = pre_len && i < n ? a.fact_len[base + i] : 0;
         }
         double lo = __builtin_huge_val(), hi = -__builtin_huge_val();
         int bad = 0;
@@ -438,20 +444,60 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
             __syncthreads();
             const int t = s_t, C = s_C;
             if (C <= kCandMax) {
-                auto gather = [&](double x, int i) {
+                // len < 0: the length is loaded here
+                auto gather = [&](double x, int i, int32_t len) {
                     if (value_bin(x, lo, scale) >= t) {
                         const int slot = atomicAdd(&s_nc, 1);
                         const int32_t id = cand_id(i);
                         s_ck[slot] = order_key(x);
                         s_ci[slot] = id;
-                        s_cl[slot] = a.fact_len ? a.fact_len[base + id] : 0;
+                        s_cl[slot] = len >= 0 ? len : (a.fact_len ? a.fact_len[base + id] : 0);
                     }
                 };
 #pragma unroll
                 for (int j = 0; j < kKeep; ++j)
-                    if (tid + j * kTopkThreads < n) gather(xv[j], tid + j * kTopkThreads);
-                for (int i = tail0; i < n; i += kTopkThreads) gather(sc[i], i);
+                    if (tid + j * kTopkThreads < n) gather(xv[j], tid + j * kTopkThreads, pre_len ? lv[j] : -1);
+                for (int i = tail0; i < n; i += kTopkThreads) gather(sc[i], i, -1);
                 __syncthreads();
+                if (C <= 64) {
+                    // one wave sorts the candidates in registers (bitonic,
+                    // best first): a lane per candidate, the padding lanes
+                    // worse than any candidate
+                    if (wave == 0) {
+                        uint64_t key = lane < C ? s_ck[lane] : 0;
+                        int32_t idx = lane < C ? s_ci[lane] : INT32_MAX;
+                        int32_t len = lane < C ? s_cl[lane] : 0;
+                        for (int kw = 2; kw <= 64; kw <<= 1) {
+                            for (int jw = kw >> 1; jw > 0; jw >>= 1) {
+                                const uint64_t ok = __shfl_xor(key, jw, 64);
+                                const int32_t oi = __shfl_xor(idx, jw, 64);
+                                const int32_t ol = __shfl_xor(len, jw, 64);
+                                // the lower lane of a pair keeps the better one in a
+                                // best-first run, the worse one in a worst-first run
+                                const bool lower = (lane & jw) == 0;
+                                const bool best_first = (lane & kw) == 0;
+                                const bool other_better = better(ok, oi, key, idx);
+                                if (other_better == (lower == best_first)) {
+                                    key = ok;
+                                    idx = oi;
+                                    len = ol;
+                                }
+                            }
+                        }
+                        const int tok = lane < kk ? len : 0;
+                        int sum = tok;
+#pragma unroll
+                        for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+                        if (lane < kk) {
+                            cand_key[lane] = key;
+                            cand_idx[lane] = idx;
+                        }
+                        if (lane == 0) s_tokens = sum;
+                    }
+                    __syncthreads();
+                    tokens_known = true;
+                    goto outputs;
+                }
                 int my_tokens = 0;
                 for (int j = tid; j < C; j += blockDim.x) {
                     const uint64_t kj = s_ck[j];

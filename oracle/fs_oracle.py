@@ -51,7 +51,7 @@ __all__ = [
     "bf16_to_f64", "f64_to_bf16", "score", "select_topk", "decisive_gap",
     "retrieve", "compose", "segment_rows", "placement", "request_problem",
     "rope_inv_freq", "rope_rotate", "inject_request", "expected_rows",
-    "gather_rows", "causal_attention", "attend_prefill", "ivf_probe", "cwe_window",
+    "gather_rows", "causal_attention", "attend_prefill", "ivf_probe", "ivf_init", "ivf_update", "cwe_window",
     "capture_rows",
 ]
 
@@ -359,6 +359,36 @@ def ivf_probe(emb: np.ndarray, centroids: np.ndarray, list_begin: np.ndarray,
     ids[: order.size] = cand[order]
     sc[: order.size] = s[order]
     return ids, sc
+
+
+def ivf_init(emb: np.ndarray, nlist: int) -> np.ndarray:
+    """The index's starting centroids (its own definition, as for
+    ``ivf_probe``): centroid c is row floor(c * N / nlist) of ``emb``,
+    scaled to unit length in fp64.  Returns fp64 [nlist, E]."""
+    n = emb.shape[0]
+    rows = np.asarray(emb, np.float64)[[c * n // nlist for c in range(nlist)]]
+    norm = np.sqrt((rows * rows).sum(axis=1, keepdims=True))
+    return np.where(norm > 0, rows / np.where(norm > 0, norm, 1.0), 0.0)
+
+
+def ivf_update(emb: np.ndarray, list_begin: np.ndarray, members: np.ndarray,
+               prev: np.ndarray) -> np.ndarray:
+    """One spherical k-means update (the index's own definition): each
+    centroid becomes the unit vector along the sum of its list's embeddings,
+    the direction that maximises the sum of the members' inner products with
+    a unit vector; an empty list, or a zero sum, keeps the previous centroid.
+    ``members`` holds rows of ``emb``.  Returns fp64 [nlist, E]."""
+    out = np.array(prev, np.float64, copy=True)
+    e64 = np.asarray(emb, np.float64)
+    for c in range(len(list_begin) - 1):
+        rows = np.asarray(members[list_begin[c]:list_begin[c + 1]], np.int64)
+        if rows.size == 0:
+            continue
+        v = e64[rows].sum(axis=0)
+        norm = math.sqrt(float(v @ v))
+        if norm > 0:
+            out[c] = v / norm
+    return out
 
 
 # --------------------------------------------------------------------------

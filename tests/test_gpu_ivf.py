@@ -77,6 +77,25 @@ def test_build_invariants(clustered):
     assert np.all(s[np.arange(n), lst] >= s.max(axis=1) - 1e-5)
 
 
+def test_build_centroids_follow_init_and_update(clustered):
+    """Builds with 0, 1 and 2 k-means iterations on one store: the first's
+    centroids are oracle.ivf_init's; each next build's centroids are
+    oracle.ivf_update of the previous build's final lists (the assignment
+    its next iteration uses), to one fp32 rounding."""
+    emb, _, st, _, _ = clustered
+    builds = [fs.fs_ivf_build(st, 0, 48, it, 48) for it in (0, 1, 2)]
+    arrs = [_host_index(ix) for ix in builds]
+    want = oracle.ivf_init(emb, 48)
+    assert np.allclose(arrs[0][0], want, rtol=2.0 ** -23, atol=1e-12), "init"
+    for i in (0, 1):
+        cent, lb, mem, _ = arrs[i]
+        want = oracle.ivf_update(emb, lb, mem, cent.astype(np.float64))
+        assert np.allclose(arrs[i + 1][0], want, rtol=2.0 ** -23, atol=1e-12), f"update {i + 1}"
+        assert not np.array_equal(arrs[i + 1][0], cent), "the update moved no centroid"
+    for ix in builds:
+        ix.close()
+
+
 @pytest.mark.parametrize("nprobe", [1, 6, 48])
 @pytest.mark.parametrize("k", [1, 50, 256])
 def test_probe_matches_oracle(clustered, nprobe, k):
