@@ -464,6 +464,39 @@ def test_large_store_batch32():
     ds.close()
 
 
+@pytest.mark.parametrize("D, H, bs", [(64, 2, 16), (256, 12, 8), (128, 3, 4)])
+def test_pinned_store_short_split_and_padded_rows(D, H, bs):
+    """Pinned-host arenas with rows of 16 vectors (several rows per wave),
+    384 vectors (padded to 512: two workgroups a row) and 48 vectors (padded
+    to 64): fetch every layer into the staging ring, inject, and compare every
+    request's rows with the oracle and every other byte with the sentinel."""
+    import dataclasses
+    base = synth.CONFIGS["concurrent"]
+    shape = dataclasses.replace(base, name=f"pin{D}x{H}", num_layers=2, num_kv_heads=H, head_dim=D,
+                                block_size=bs, num_users=3, facts_per_user=60, len_lo=2, len_hi=30,
+                                batch=3, k=12, start_lo=0, start_hi=200, table="shared_pool",
+                                pool_blocks=3 * ((200 + 12 * 30) // bs + 1) + 8, embed_dim=64, rope_theta=1e6)
+    wl = synth.make_workload(shape, seed=D + 7 * H)
+    s = wl.shape
+    layers = [0, 1]
+    say(f"pinned {D}x{H}: building pinned store")
+    ds = build_store(wl, layers, pinned=True, staging_layers=2)
+    req = request_tensors(wl)
+    B, k = s.batch, wl.k
+    ids, scores, ntok = gpu_retrieve(ds, req, k, B)
+    kc, vc = synth.make_caches(wl, layers, "cuda")
+    nb = kc[0].shape[0]
+    fs.fs_fetch_async(ds.store, B, req["user"], ids, k, 0, 2)
+    for l in layers:
+        fs.fs_inject(ds.store, l, B, req["user"], ids, k, req["block_table"], wl.block_table.shape[1],
+                     req["start_pos"], kc, vc, nb)
+    assert fs.fs_poll_errors(ds.store) == 0
+    o = check_retrieval(wl, _host(ids), _host(scores), _host(ntok), range(B), k)
+    check_injection(wl, ds, kc, vc, o, layers)
+    check_sentinel(kc, vc, written_mask(wl, o, nb), layers)
+    ds.close()
+
+
 def test_pinned_host_store_fetch_then_inject():
     # Mistral shape with the K/V arenas in page-locked host memory (4 of 32
     # layers resident: 9.8 GB pinned), fetched over the host link on a side
