@@ -121,7 +121,7 @@ typedef int32_t fs_status;
 
 typedef struct fs_store_desc {
     int32_t num_layers;      /* 1 .. FS_MAX_LAYERS                               */
-    int32_t num_kv_heads;    /* >= 1                                             */
+    int32_t num_kv_heads;    /* >= 1; num_kv_heads * head_dim <= 8192          */
     int32_t head_dim;        /* 64, 128 or 256 (rotate-half pairs i, i+head_dim/2) */
     int32_t embed_dim;       /* multiple of 4, 4 .. 4096                         */
     double  rope_theta;      /* RoPE base, > 1 (w_i = theta^(-2i/head_dim))      */

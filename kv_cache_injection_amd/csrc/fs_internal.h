@@ -30,7 +30,7 @@ constexpr int kTopkChunk = 16384;
 struct fs_store {
     fs_store_desc desc;
     int device = 0;
-    int32_t num_cus = 0;          // compute units of the device (inject grid sizing)
+    int32_t num_cus = 0;          // compute units of the device (attention split sizing)
     int32_t max_fact_len = 0;     // longest fact, tokens
     double mean_fact_len = 0;     // mean fact length at creation (inject grid sizing)
     int32_t seg_tokens = 0;       // max_k * max_fact_len: longest possible segment

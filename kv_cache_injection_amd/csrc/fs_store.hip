@@ -99,6 +99,9 @@ fs_status check_desc(const fs_store_desc* d) {
         return fail(FS_E_ARG, "head_dim %d must be a positive multiple of 16", d->head_dim);
     if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256)
         return fail(FS_E_UNSUPPORTED, "head_dim %d: built for 64, 128, 256", d->head_dim);
+    if (int64_t(d->num_kv_heads) * d->head_dim > 8192)
+        return fail(FS_E_UNSUPPORTED, "num_kv_heads * head_dim = %lld: token rows above 16 KB are not built",
+                    static_cast<long long>(int64_t(d->num_kv_heads) * d->head_dim));
     if (d->embed_dim < 4 || d->embed_dim % 4 != 0)
         return fail(FS_E_ARG, "embed_dim %d must be a positive multiple of 4", d->embed_dim);
     if (d->embed_dim > 4096) return fail(FS_E_UNSUPPORTED, "embed_dim %d > 4096", d->embed_dim);

@@ -293,7 +293,6 @@ struct FlatArgs {
     int32_t units;                  // workgroups per (kind, request, layer)
     int32_t layer_begin;
     int32_t seg_tokens;
-    int32_t lg_vpr;                 // log2 of the row's vectors, rounded up to a power of two
     int32_t vpr;                    // the row's 16-byte vectors (heads * D / 8)
     // rarely read
     const uint16_t* stage_k;        // staging ring (pinned stores)

@@ -96,6 +96,7 @@ def _create(desc, ufb=(0, 2, 4), fl=(10, 10, 10, 10), emb=FAKE, arenas=None):
     ("num_layers", 0, fs.FS_E_ARG),
     ("num_layers", 129, fs.FS_E_ARG),
     ("num_kv_heads", 0, fs.FS_E_ARG),
+    ("num_kv_heads", 65, fs.FS_E_UNSUPPORTED),     # 65 x 128: rows above 16 KB
     ("head_dim", 100, fs.FS_E_ARG),
     ("head_dim", 96, fs.FS_E_UNSUPPORTED),
     ("embed_dim", 6, fs.FS_E_ARG),

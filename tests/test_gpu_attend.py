@@ -143,20 +143,17 @@ def test_attend_device_errors_write_nothing(split):
     st.close()
 
 
-def test_attend_rejects_cache_positions_of_16_mib():
-    """A cache position of 65,536 KV heads x 128 x bf16 is 16 MiB: the
-    kernel's 24-bit offset arithmetic does not cover it, so the call is
-    rejected before any launch."""
+def test_store_refuses_rows_beyond_what_the_kernels_cover():
+    """A cache position of 65,536 KV heads x 128 x bf16 (16 MiB) is beyond the
+    16 KB token rows the inject kernels are built for and beyond the
+    attention's 24-bit offset arithmetic: fs_create_store refuses it, so no
+    call ever sees such a row."""
     hkv = 65536
     one = [torch.zeros((1, hkv, D), dtype=torch.bfloat16, device="cuda")]
-    st = _store(hkv, 1, 1e4, facts=np.array([1], np.int32), k_pre=one, v=[one[0].clone()])
-    q = torch.zeros((1, 1, hkv, D), dtype=torch.bfloat16, device="cuda")
-    kc = torch.zeros((1, 1, hkv, D), dtype=torch.bfloat16, device="cuda")
-    out = torch.zeros((1, 1, hkv, D), device="cuda")
-    zero = torch.zeros((1,), dtype=torch.int32, device="cuda")
-    with pytest.raises(fs.FsError, match="16 MiB"):
-        fs.fs_attend_prefill(st, 1, q, kc, kc.clone(), zero.reshape(1, 1), 1, zero, zero, 0.1, out)
-    st.close()
+    with pytest.raises(fs.FsError) as e:
+        _store(hkv, 1, 1e4, facts=np.array([1], np.int32), k_pre=one, v=[one[0].clone()])
+    assert e.value.status == fs.FS_E_UNSUPPORTED
+    assert "16 KB" in str(e.value)
 
 
 def test_theorem3_inject_then_attend_equals_prompt_attention():
