@@ -407,6 +407,25 @@ def test_random_layouts(case):
     ds.close()
 
 
+@pytest.mark.parametrize("k", [65, 300, 1024])
+def test_large_k(k):
+    """k above the 64 candidates one wave sorts (the rank-by-count path of
+    the top-k) and up to FS_MAX_K: 2 users x 1,500 short facts, 2 requests,
+    segments of up to ~2,500 tokens (the plan's prefix over 16 chunks of 64
+    ids); retrieval, every row of both layers and the sentinel."""
+    import dataclasses
+    shape = dataclasses.replace(synth.CONFIGS["concurrent"], name=f"k{k}", num_layers=2, num_kv_heads=2, head_dim=64,
+                                num_users=2, facts_per_user=1500, len_lo=1, len_hi=3, batch=2, k=k,
+                                start_lo=0, start_hi=100, block_size=16, embed_dim=64, rope_theta=1e4,
+                                table="shared_pool", pool_blocks=2 * ((99 + k * 3) // 16 + 1) + 4)
+    wl = synth.make_workload(shape, seed=5000 + k)
+    ds, req, ids, scores, ntok, kc, vc = _run(wl, [0, 1])
+    o = check_retrieval(wl, _host(ids), _host(scores), _host(ntok), range(2), k)
+    check_injection(wl, ds, kc, vc, o, [0, 1])
+    check_sentinel(kc, vc, written_mask(wl, o, kc[0].shape[0]), [0, 1])
+    ds.close()
+
+
 def test_multi_user_batch_small():
     wl = synth.make_workload("concurrent", num_users=12, facts_per_user=150, batch=12)
     ds, req, ids, scores, ntok, kc, vc = _run(wl, [0, 5])
