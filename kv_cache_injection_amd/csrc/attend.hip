@@ -232,6 +232,15 @@ __global__ __launch_bounds__(kThreads, 2) void fs_attend_kernel(AttendArgs a) {
         ko[i] = uint32_t(hk) * (kD * 2) + 16 * k_slot(rr[i], slot);
         vo[i] = uint32_t(hk) * (kD * 2) + 16 * v_slot(rr[i], slot);
     }
+    // when a wave's 16 rows lie in one cache block (blocks of 16 positions or
+    // more, context start on a 16-position boundary) each lane's offset from
+    // that block's first row is the same for every tile
+    uint32_t lk[4], lv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lk[i] = uint32_t(4 * i + (lane >> 4)) * row_b + ko[i];
+        lv[i] = uint32_t(4 * i + (lane >> 4)) * row_b + vo[i];
+    }
     const unsigned char* kc_b = reinterpret_cast<const unsigned char*>(a.kc);
     const unsigned char* vc_b = reinterpret_cast<const unsigned char*>(a.vc);
     const int64_t dkv = vc_b - kc_b;
@@ -379,9 +388,23 @@ __global__ __launch_bounds__(kThreads, 2) void fs_attend_kernel(AttendArgs a) {
     // entry indices are clamped to the block's range and read without a
     // branch; rows past the block's last position then take -1
     const int e_first32 = static_cast<int>(e_first), e_span = static_cast<int>(e_last - e_first);
+    const bool wave_blocks = bt_cached && a.log2_block >= 4 && (c0 & 15) == 0;
     auto load_tile = [&](unsigned char* buf, int t) {
         int blk[4];
         const uint32_t tb = uint32_t(c0) + uint32_t(t) * kKT;
+        if (wave_blocks && tb + kKT - 1 <= uint32_t(p_end)) {
+            // every row of the tile is real and the wave's 16 rows share one
+            // cache block: one table entry and one base address per wave
+            const uint32_t p0 = tb + 16 * wave;
+            const int v = __builtin_amdgcn_readfirstlane(s_bt[min(static_cast<int>(p0 >> a.log2_block) - e_first32, e_span)]);
+            const unsigned char* kb = kc_b + uint64_t(uint32_t(v)) * blk_b + __umul24(p0 & pmask, row_b);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                __builtin_amdgcn_global_load_lds(kb + lk[i], (__attribute__((address_space(3))) void*)(buf + (16 * wave + 4 * i) * kRowB), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(kb + dkv + lv[i], (__attribute__((address_space(3))) void*)(buf + kHalfB + (16 * wave + 4 * i) * kRowB), 16, 0, 0);
+            }
+            return;
+        }
         if (bt_cached) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
