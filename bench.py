@@ -14,9 +14,11 @@ retrieval and then its injection on stream i % 2, so step i+1's retrieval
 (latency-bound, a few MB) and the start of its injection overlap step i's
 injection (bandwidth-bound).  Retrievals share the store's scratch, so each
 waits on an event after the previous one; the lanes inject into separate
-cache pools.  request_latency_us.in_order repeats the steps on one stream,
-strictly one after the other: one request's retrieval, plan and row
-injection (the time-to-inject of a single request).
+cache pools.  request_latency_us.in_order runs the requests on one stream,
+strictly one after the other, as a single request is served:
+fs_retrieve_plan (scores, then top-k whose block also writes the inject
+plan) and fs_inject_planned (the row kernel); in_order_two_calls does the
+same with fs_retrieve_topk then fs_inject (plan kernel + row kernel).
 
 Prints ONE JSON line:
   value       whole-step algorithmic HBM bytes / step time (GB/s)
@@ -28,9 +30,9 @@ Prints ONE JSON line:
               repeats it with each launch alone after a 1 GiB write that
               evicts the MALL and L2 (median, p10, p90)
   kernels_ms  average launch times of the retrieval, the fused inject (plan
-              kernel + row kernel), the plan kernel alone and the row kernel
-              alone (fs_plan_inject, fs_inject_planned), each issued back to
-              back
+              kernel + row kernel), the plan kernel alone, the row kernel
+              alone (fs_plan_inject, fs_inject_planned) and the planning
+              retrieval (fs_retrieve_plan), each issued back to back
   request_latency_us  one request at a time, in order: the whole step, and
               its parts from kernels_ms
   inject_cold each fused inject alone after the same 1 GiB write
@@ -141,7 +143,7 @@ def main():
     ids = torch.empty((total, B, k), dtype=torch.int32, device="cuda")   # one slot per step
     ntok = torch.zeros((total, B), dtype=torch.int32, device="cuda")
     plans = [fs.new_inject_plan(ds.store, B) for _ in range(total)]     # one plan per step
-    e0, e1, e2, e3, e4 = (torch.cuda.Event(enable_timing=True) for _ in range(5))
+    e0, e1, e2, e3, e4, e5 = (torch.cuda.Event(enable_timing=True) for _ in range(6))
 
     # Pipelined steps on two lanes (streams at the default priority): step i
     # retrieves and injects on lane i % 2, so each inject follows its own
@@ -176,6 +178,10 @@ def main():
                               lambda i: caches if i % 2 == 0 else caches2)         # two lanes
     cur = torch.cuda.current_stream()
     ret_s, inj_s, plan_s, injp_s = prep(lambda i: cur, lambda i: cur)           # one stream, in order
+    # retrieval that also writes the step's plan (one stream)
+    rp_s = [fs.prepare_retrieve_plan(ds.store, B, user, sets[i % len(sets)]["query"], k, ids[i],
+                                     sets[i % len(sets)]["block_table"], mb, sets[i % len(sets)]["start_pos"],
+                                     nb, plans[i], num_tokens=ntok[i], stream=cur) for i in range(total)]
 
     def step_pipelined(i):
         lane = lanes[i % 2]
@@ -205,21 +211,31 @@ def main():
         raise RuntimeError(f"device error bits 0x{flags:x}")
     L = ntok.cpu().numpy().astype(np.int64)[args.warmup:]          # [steps, B]
 
-    # timed region 1b: the same steps on one stream, strictly in order
-    torch.cuda.synchronize()
-    u0 = time.perf_counter()
-    for i in range(args.warmup, total):
-        step_serial(i)
-    torch.cuda.synchronize()
-    u1 = time.perf_counter()
-
-    # every kernel region 2 times has run before it: the in-order steps ran
-    # the retrievals and fused injects; the plans and the injects from plans
-    # run here (a first launch pays one-time costs)
+    # every kernel regions 1b and 2 time has run before them: the pipelined
+    # steps ran the retrievals and fused injects; the plans, the injects from
+    # plans and the planning retrievals run here (a first launch pays
+    # one-time costs)
     for i in range(min(total, max(args.warmup, 5))):
         plan_s[i]()
         injp_s[i]()
+        rp_s[i]()
+        injp_s[i]()
     torch.cuda.synchronize()
+
+    # timed region 1b: the same steps on one stream, strictly in order, as a
+    # single request is served: retrieval with planning, then the row kernel
+    # from that plan; then retrieval, then the fused inject
+    torch.cuda.synchronize()
+    u0 = time.perf_counter()
+    for i in range(args.warmup, total):
+        rp_s[i]()
+        injp_s[i]()
+    torch.cuda.synchronize()
+    u1 = time.perf_counter()
+    for i in range(args.warmup, total):
+        step_serial(i)
+    torch.cuda.synchronize()
+    u2 = time.perf_counter()
 
     # timed region 2: per-kernel average durations for the roofline, from
     # HIP events on the launch stream: the steps' retrievals back to back
@@ -240,6 +256,9 @@ def main():
     for i in range(args.warmup, total):
         injp_s[i]()
     e4.record()
+    for i in range(args.warmup, total):
+        rp_s[i]()
+    e5.record()
     torch.cuda.synchronize()
 
     # timed region 3 (reported beside, never value): each row-kernel launch
@@ -272,12 +291,14 @@ def main():
     plan_ms = e2.elapsed_time(e3) / args.steps
     planned_ms = e3.elapsed_time(e4) / args.steps
     ret_ms = np.full(args.steps, e0.elapsed_time(e1) / args.steps)
+    ret_plan_ms = e4.elapsed_time(e5) / args.steps
     achieved = float(inject_bytes.sum() / (planned_ms * args.steps * 1e-3) / 1e9)
     row_cold_gbs = inject_bytes[:n_cold] / (row_cold_ms * 1e-3) / 1e9
     vpr = s.num_kv_heads * s.head_dim // 8
     lg = (vpr - 1).bit_length()
     kname = f"fs_{'row' if lg >= 6 else 'short'}_kernel<{s.head_dim}, {lg}>"
     in_order_us = (u1 - u0) / args.steps * 1e6
+    in_order_two_us = (u2 - u1) / args.steps * 1e6
     value = float(step_bytes.sum() / wall / 1e9)
     ms_per_step = wall / args.steps * 1e3
     traffic = recorded_traffic(args.config, nl)
@@ -319,7 +340,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
-        "ms_per_step_in_order": round((u1 - u0) / args.steps * 1e3, 5),
+        "ms_per_step_in_order": round(in_order_us * 1e-3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -339,14 +360,22 @@ def main():
         "kernels_ms": {"retrieve_avg": round(float(ret_ms.mean()), 5),
                        "inject_avg": round(float(inj_ms.mean()), 5),
                        "plan_avg": round(float(plan_ms), 5),
-                       "inject_from_plan_avg": round(float(planned_ms), 5)},
+                       "inject_from_plan_avg": round(float(planned_ms), 5),
+                       "retrieve_plan_avg": round(float(ret_plan_ms), 5)},
         "request_latency_us": {
             "in_order": round(in_order_us, 2),
+            "in_order_two_calls": round(in_order_two_us, 2),
             "retrieve": round(float(ret_ms.mean()) * 1e3, 2),
+            "retrieve_plan": round(float(ret_plan_ms) * 1e3, 2),
             "inject": round(float(inj_ms.mean()) * 1e3, 2),
+            "inject_from_plan": round(float(planned_ms) * 1e3, 2),
             "in_order_over_inject": round(in_order_us / (float(inj_ms.mean()) * 1e3), 3),
-            "note": "one request at a time on one stream: retrieval (score + top-k), then fs_inject "
-                    "(plan kernel + row kernel); retrieve and inject are the back-to-back averages"},
+            "in_order_over_inject_from_plan": round(in_order_us / (float(planned_ms) * 1e3), 3),
+            "in_order_two_calls_over_inject": round(in_order_two_us / (float(inj_ms.mean()) * 1e3), 3),
+            "note": "one request at a time on one stream.  in_order: fs_retrieve_plan (scores, then a "
+                    "top-k that also writes the inject plan), then fs_inject_planned (row kernel).  "
+                    "in_order_two_calls: fs_retrieve_topk (scores + top-k), then fs_inject (plan kernel + "
+                    "row kernel).  The other figures are back-to-back averages of one call kind"},
         "inject_cold": {
             "note": "each inject alone after a 1 GiB write that evicts the MALL and L2, own HIP events",
             "launches": n_cold,

@@ -329,6 +329,31 @@ FS_API fs_status fs_inject_planned(const fs_store* store, int32_t layer_begin, i
                                    void* stream);
 
 /*
+ * fs_retrieve_plan — retrieval and planning of one serving step in one call
+ * (gist.science summary, "Phase En-ligne": the retrieved facts' segment is
+ * what gets re-rotated and injected; "Résultats", Latence: the per-request
+ * path stays short).  Writes exactly what fs_retrieve_topk writes (ids,
+ * scores, num_tokens) and the plan that fs_plan_inject would write from
+ * those ids with the same user, block_table, max_blocks, start_pos and
+ * num_blocks; the selection's last kernel composes the plan itself, so
+ * fs_inject_planned can follow at once.  Device stores only.
+ *
+ *   arguments as fs_retrieve_topk's, then as fs_plan_inject's (block_table
+ *   device int32 [batch][max_blocks], start_pos device int32 [batch], plan
+ *   caller-owned device memory of fs_inject_plan_size(batch) bytes, 16-byte
+ *   aligned).  k = 0 writes num_tokens (when given) and no plan.
+ * Device-checked: FS_ERR_USER (ids -1, length 0), FS_ERR_START_POS,
+ * FS_ERR_BLOCK_SHORT, FS_ERR_BLOCK_ID (the request's plan length is then 0;
+ * its ids are still written).  Errors: FS_E_ARG, FS_E_RANGE,
+ * FS_E_BLOCKTABLE, FS_E_UNSUPPORTED, FS_E_HIP.
+ */
+FS_API fs_status fs_retrieve_plan(const fs_store* store, int32_t batch, const int32_t* user,
+                                  const float* query, int32_t k, int32_t* ids, double* scores,
+                                  int32_t* num_tokens, const int32_t* block_table, int32_t max_blocks,
+                                  const int32_t* start_pos, int32_t num_blocks, void* plan,
+                                  size_t plan_bytes, void* stream);
+
+/*
  * fs_fetch_async — host-DRAM offload (gist.science summary, "Résultats":
  * the KV store can be offloaded to host DRAM at a small TTFT cost).
  * Pinned stores only.  Gathers the selected facts' K and V rows of layers

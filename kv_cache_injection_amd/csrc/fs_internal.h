@@ -107,6 +107,13 @@ struct RetrieveLaunch {
     double* scores;
     int32_t* num_tokens;
     hipStream_t stream;
+    // plan set (fs_retrieve_plan): the final selection also writes the inject
+    // plan of the selected ids into it, checked against these
+    void* plan = nullptr;
+    const int32_t* block_table = nullptr;
+    int32_t max_blocks = 0;
+    const int32_t* start_pos = nullptr;
+    int32_t num_blocks = 0;
 };
 hipError_t fsi_launch_retrieve(const RetrieveLaunch& a);
 

@@ -350,10 +350,11 @@ fs_status fs_destroy_store(fs_store* store) {
     return FS_OK;
 }
 
-fs_status fs_retrieve_topk(const fs_store* store, int32_t batch, const int32_t* user,
-                           const float* query, int32_t k, int32_t* ids, double* scores,
-                           int32_t* num_tokens, void* stream) {
-    g_msg[0] = 0;
+namespace {
+
+// the host checks of fs_retrieve_topk and fs_retrieve_plan
+fs_status check_retrieve(const fs_store* store, int32_t batch, const int32_t* user, const float* query, int32_t k,
+                         const int32_t* ids, const double* scores, const int32_t* num_tokens) {
     if (!store) return fail(FS_E_ARG, "null store");
     const fs_store_desc& d = store->desc;
     if (batch < 1 || batch > d.max_batch)
@@ -366,6 +367,16 @@ fs_status fs_retrieve_topk(const fs_store* store, int32_t batch, const int32_t* 
     if (ids && !aligned(ids, 4)) return fail(FS_E_ARG, "ids not 4-byte aligned");
     if (scores && !aligned(scores, 8)) return fail(FS_E_ARG, "scores not 8-byte aligned");
     if (num_tokens && !aligned(num_tokens, 4)) return fail(FS_E_ARG, "num_tokens not 4-byte aligned");
+    return FS_OK;
+}
+
+}  // namespace
+
+fs_status fs_retrieve_topk(const fs_store* store, int32_t batch, const int32_t* user,
+                           const float* query, int32_t k, int32_t* ids, double* scores,
+                           int32_t* num_tokens, void* stream) {
+    g_msg[0] = 0;
+    if (fs_status c = check_retrieve(store, batch, user, query, k, ids, scores, num_tokens)) return c;
     if (k == 0 && !num_tokens) return FS_OK;
     RetrieveLaunch a{store, batch, user, query, k, ids, scores, num_tokens,
                      reinterpret_cast<hipStream_t>(stream)};
@@ -505,6 +516,34 @@ fs_status fs_plan_inject(const fs_store* store, int32_t batch, const int32_t* us
     a.plan_out = plan;
     hipError_t e = fsi_launch_inject(a);
     if (e != hipSuccess) return hip_fail(e, "plan launch");
+    return FS_OK;
+}
+
+fs_status fs_retrieve_plan(const fs_store* store, int32_t batch, const int32_t* user, const float* query, int32_t k,
+                           int32_t* ids, double* scores, int32_t* num_tokens, const int32_t* block_table,
+                           int32_t max_blocks, const int32_t* start_pos, int32_t num_blocks, void* plan,
+                           size_t plan_bytes, void* stream) {
+    g_msg[0] = 0;
+    if (fs_status c = check_retrieve(store, batch, user, query, k, ids, scores, num_tokens)) return c;
+    if (fs_status c = check_plan(store, batch, k, plan, plan_bytes)) return c;
+    if (!block_table || !start_pos) return fail(FS_E_ARG, "null pointer argument");
+    if (!aligned(block_table, 4) || !aligned(start_pos, 4))
+        return fail(FS_E_ARG, "int32 argument not 4-byte aligned");
+    if (max_blocks < 1) return fail(FS_E_BLOCKTABLE, "max_blocks %d < 1", max_blocks);
+    if (num_blocks < 1) return fail(FS_E_BLOCKTABLE, "num_blocks %d < 1", num_blocks);
+    if (k == 0 && !num_tokens) return FS_OK;
+    RetrieveLaunch a{store, batch, user, query, k, ids, scores, num_tokens,
+                     reinterpret_cast<hipStream_t>(stream)};
+    if (k > 0) {
+        // k = 0 plans nothing, as fs_plan_inject
+        a.plan = plan;
+        a.block_table = block_table;
+        a.max_blocks = max_blocks;
+        a.start_pos = start_pos;
+        a.num_blocks = num_blocks;
+    }
+    hipError_t e = fsi_launch_retrieve(a);
+    if (e != hipSuccess) return hip_fail(e, "retrieve launch");
     return FS_OK;
 }
 

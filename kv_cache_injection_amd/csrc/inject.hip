@@ -35,6 +35,7 @@
 
 #include "fs_device.h"
 #include "fs_internal.h"
+#include "fs_plan.h"
 
 namespace {
 
@@ -180,16 +181,6 @@ __device__ uint32_t plan_request(const int32_t* user, const int32_t* ids, int k,
     return bits;
 }
 
-__device__ __forceinline__ int find_fact(const int32_t* off, int nf, int t) {
-    // largest j < nf with off[j] <= t (off is non-decreasing, off[0] = 0)
-    int lo = 0, hi = nf - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
 // Validation of one composed request: start position, block-table coverage
 // and entries, and for pinned stores that every staging slot holds these ids.
 __device__ uint32_t check_request(const PlanArgs& a, int b, int L) {
@@ -197,26 +188,8 @@ __device__ uint32_t check_request(const PlanArgs& a, int b, int L) {
     uint32_t bits = 0;
     const int s = a.start_pos[b];
     const int32_t* bt = a.block_table + int64_t(b) * a.max_blocks;
-    if (s < 0 || int64_t(s) + L > int64_t(INT32_MAX)) {
-        bits |= FS_ERR_START_POS;
-    } else if (L > 0) {
-        const int first = s >> a.log2_block;
-        const int last = (s + L - 1) >> a.log2_block;
-        if (last >= a.max_blocks) {
-            bits |= FS_ERR_BLOCK_SHORT;
-        } else {
-            // four entries per lane in flight at a time (indices clamped to
-            // the range, so the loads need no branch and no wait between them)
-            for (int j0 = first + lane; j0 <= last; j0 += 256) {
-                int e[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) e[q] = bt[min(j0 + 64 * q, last)];
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (j0 + 64 * q <= last && (e[q] < 0 || e[q] >= a.num_blocks)) bits |= FS_ERR_BLOCK_ID;
-            }
-        }
-    }
+    bits |= fsp::check_segment(s, L, a.max_blocks, a.num_blocks, a.log2_block, lane, 64,
+                               [&](int j) { return bt[j]; });
     if (a.stage_ids) {
         for (int l = a.layer_begin; l < a.layer_end; ++l) {
             const int slot = l % a.staging_layers;
@@ -253,30 +226,15 @@ __global__ __launch_bounds__(kPlanThreads) void fs_plan_kernel(PlanArgs a) {
             s_len = bits ? 0 : L;
             s_nf = nf;
             a.out.req[b] = PlanReq{bits ? 0 : L, a.start_pos[b]};
-            if (b == 0) {
-                PlanHeader h{};
-                h.key = a.key;
-                h.magic = kPlanMagic;
-                h.tag = a.tag;
-                h.batch = a.batch;
-                h.k = a.k;
-                h.seg_tokens = a.seg_tokens;
-                h.num_blocks = a.num_blocks;
-                *a.out.hdr = h;
-            }
+            if (b == 0) fsp::write_header(a.out.hdr, a.key, a.tag, a.batch, a.k, a.seg_tokens, a.num_blocks);
         }
     }
     __syncthreads();
     const int L = s_len, nf = s_nf;
     const int s = a.start_pos[b];
     const int32_t* bt = a.block_table + int64_t(b) * a.max_blocks;
-    const int bs_mask = (1 << a.log2_block) - 1;
-    PlanTok* tok = a.out.tok + int64_t(b) * a.seg_tokens;
-    for (int t = threadIdx.x; t < L; t += blockDim.x) {
-        const int j = find_fact(off, nf, t);
-        const int p = s + t;
-        tok[t] = PlanTok{row0[j] + (t - off[j]), (int64_t(bt[p >> a.log2_block]) << a.log2_block) | (p & bs_mask)};
-    }
+    fsp::write_tokens(a.out.tok + int64_t(b) * a.seg_tokens, off, row0, nf, L, s, a.log2_block, threadIdx.x,
+                      blockDim.x, [&](int j) { return bt[j]; });
 }
 
 struct FlatArgs {
@@ -664,11 +622,11 @@ __global__ __launch_bounds__(kThreads) void fs_fetch_kernel(FetchArgs a) {
     for (int l = l0; l < l1; ++l) {
         for (int tt = t0; tt < tend; tt += 2) {
             const bool two = tt + 1 < tend;
-            const int ja = find_fact(off, nf, tt);
+            const int ja = fsp::find_fact(off, nf, tt);
             const int64_t rowa = row0[ja] + (tt - off[ja]);
             int64_t rowb = rowa;
             if (two) {
-                const int jb = find_fact(off, nf, tt + 1);
+                const int jb = fsp::find_fact(off, nf, tt + 1);
                 rowb = row0[jb] + (tt + 1 - off[jb]);
             }
             const int64_t sa = (int64_t(l % a.staging_layers) * a.max_batch + b) * a.stage_tokens + tt;

@@ -41,6 +41,7 @@
 #include <hip/hip_runtime.h>
 
 #include "fs_internal.h"
+#include "fs_plan.h"
 
 namespace {
 
@@ -273,12 +274,127 @@ struct TopkArgs {
     int32_t chunk;
     int32_t nchunks;
     int32_t* out_counts;
+    // planning (the final selection of fs_retrieve_plan; never in chunk
+    // mode): the inject plan of the selected ids, as the plan kernel
+    // composes it from them; plan.hdr is null when not planning
+    PlanView plan;
+    uint64_t plan_key;
+    uint32_t plan_tag;
+    int32_t batch, seg_tokens, num_blocks, max_blocks, log2_block;
+    const int32_t* block_table;   // [batch][max_blocks]
+    const int32_t* start_pos;     // [batch]
+    const int64_t* fact_begin;
 };
+
+// A value every lane of the block shares, loaded through the scalar unit
+// (the data is not written while the kernel runs): its wait does not hold
+// back the vector loads issued around it.
+template <class T>
+__device__ __forceinline__ T scalar_load(const T* p) { return *(const __attribute__((address_space(4))) T*)p; }
+
+// block-table entries of a planning request fetched when its selection
+// starts (from the block its start position falls in)
+constexpr int kPlanWin = 256;
+
+__device__ __forceinline__ int wave_or_u(uint32_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v |= __shfl_xor(v, m, 64);
+    return static_cast<int>(v);
+}
+
+// The planning tail of fs_retrieve_plan: request b's inject plan from its kk
+// selected ids (base + cand_idx[j], rank order), with the segment, checks,
+// error bits and token map the plan kernel derives from the same ids.  Every
+// id is a live fact of the request's user by construction, so only a bad
+// user, the start position and the block table can reject the request.
+// known: the selection left each rank's segment offset and first arena row
+// in off / row0 and the segment length in *s_len.  win_e is this thread's
+// block-table entry win_first + tid (tid < kPlanWin), fetched at the start.
+template <int kT>
+__device__ void plan_selected(const TopkArgs& a, int b, int kk, int64_t base, const int32_t* cand_idx, bool known,
+                              bool bad_user, int s0, int win_first, int win_e, int32_t* off, int64_t* row0,
+                              int32_t* win, int* s_len, int* s_bits) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    if (!known && tid < 64) {
+        // one dependent round: the selected facts' lengths and first rows
+        int carry = 0;
+        for (int c0 = 0; c0 < kk; c0 += 64) {
+            const int j = c0 + lane;
+            const int64_t id = j < kk ? base + cand_idx[j] : 0;
+            const int len = j < kk ? a.fact_len[id] : 0;
+            const int64_t r0 = j < kk ? a.fact_begin[id] : 0;
+            int incl = len;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += y;
+            }
+            if (j < kk) {
+                off[j] = carry + incl - len;
+                row0[j] = r0;
+            }
+            carry += __shfl(incl, 63, 64);
+        }
+        if (tid == 0) *s_len = carry;
+    }
+    const int nwin = max(0, min(kPlanWin, a.max_blocks - win_first));
+    if (tid < kPlanWin) win[tid] = win_e;
+    if (tid == 0) *s_bits = 0;
+    __syncthreads();
+    const int L = *s_len;
+    const int32_t* bt = a.block_table + int64_t(b) * a.max_blocks;
+    // The block-table entries come from the window when all the segment's
+    // blocks fall inside it (the usual case), else from the table.  The
+    // choice is uniform and each path has one kind of load: a per-token
+    // choice between two loads becomes one flat load of a selected pointer,
+    // which waits on the vector-memory counter.
+    const int64_t last_pos = int64_t(s0) + L - 1;
+    const bool in_win = s0 >= 0 && L > 0 && last_pos <= int64_t(INT32_MAX) &&
+                        (static_cast<int>(last_pos >> a.log2_block) - win_first) < nwin;
+    auto from_win = [&](int j) { return win[j - win_first]; };
+    auto from_table = [&](int j) { return bt[j]; };
+    uint32_t bits = in_win ? fsp::check_segment(s0, L, a.max_blocks, a.num_blocks, a.log2_block, tid, kT, from_win)
+                           : fsp::check_segment(s0, L, a.max_blocks, a.num_blocks, a.log2_block, tid, kT, from_table);
+    if (bad_user) bits |= FS_ERR_USER;
+    bits = wave_or_u(bits);
+    if (lane == 0 && bits) atomicOr(s_bits, static_cast<int>(bits));
+    __syncthreads();
+    bits = static_cast<uint32_t>(*s_bits);
+    if (tid == 0) {
+        if (bits) atomicOr(a.err, bits);
+        a.plan.req[b] = PlanReq{bits ? 0 : L, s0};
+        if (b == 0) fsp::write_header(a.plan.hdr, a.plan_key, a.plan_tag, a.batch, a.k, a.seg_tokens, a.num_blocks);
+    }
+    if (bits) return;
+    // the token map: G threads per fact, each over every G-th token of it
+    // (no search for a token's fact; a thread's lookups are independent)
+    PlanTok* tok = a.plan.tok + int64_t(b) * a.seg_tokens;
+    const int mask = (1 << a.log2_block) - 1;
+    const int G = kk > 0 && kk < kT ? kT / kk : 1;
+    const int sub = tid % G;
+    auto write_map = [&](auto entry) {
+        for (int j = tid / G; j < kk; j += kT / G) {
+            const int o = off[j];
+            const int n = (j + 1 < kk ? off[j + 1] : L) - o;
+            const int64_t r = row0[j];
+#pragma unroll 4
+            for (int t = sub; t < n; t += G) {
+                const int p = s0 + o + t;
+                tok[o + t] = PlanTok{r + t, (int64_t(entry(p >> a.log2_block)) << a.log2_block) | (p & mask)};
+            }
+        }
+    };
+    if (in_win) write_map(from_win);
+    else write_map(from_table);
+}
 
 // kT threads: 256 for stores of up to kTopkSmallN scores per request (a
 // small block starts sooner beside a running inject and syncs faster),
 // 1024 above.
-template <int kT>
+// kPlan: the launch plans (a.plan set); the plain selection is built
+// without any of the planning code.
+template <int kT, bool kPlan>
 __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
     constexpr int kTopkThreads = kT;
     constexpr int kTopkWaves = kT / 64;
@@ -299,6 +415,10 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
     const int wave = tid >> 6;
     const int k = a.k;
     const bool mapped = a.counts != nullptr;
+    // planning: the request's start position (and, in candidate mode, which
+    // reads no user otherwise, its user) in the first round of loads
+    const int s0 = kPlan ? scalar_load(a.start_pos + b) : 0;
+    const int pu = kPlan && mapped ? scalar_load(a.user + b) : 0;
     const int u = mapped ? 0 : a.user[b];
     const bool bad_user = !mapped && (u < 0 || u >= a.num_users);
     const int64_t ubase = (mapped || bad_user) ? 0 : a.user_begin[u];
@@ -319,6 +439,32 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
     // the id a candidate is ranked and reported by
     auto cand_id = [&](int i) -> int32_t { return mapped ? imap[i] : i; };
 
+    // planning: the user's validity and the request's block-table window,
+    // fetched now, beside the scores
+    constexpr bool planning = kPlan;
+    // candidates of the threshold bin (score key, id, fact length; first
+    // arena row when planning, for the one-wave sort's at most 64)
+    __shared__ uint64_t s_ck[kCandMax];
+    __shared__ int32_t s_ci[kCandMax];
+    __shared__ int32_t s_cl[kCandMax];
+    __shared__ int64_t s_cr[64];
+    __shared__ int32_t s_win[kPlanWin];
+    __shared__ int s_plen, s_pbits;
+    // the plan's per-rank segment offsets and first rows reuse the candidate
+    // keys and ids, which are dead once the ranks are known
+    static_assert(sizeof(int32_t) * fsi::kMaxK <= sizeof(s_ci) && sizeof(int64_t) * fsi::kMaxK <= sizeof(s_ck),
+                  "plan arrays fit the candidate arrays");
+    int32_t* const s_poff = s_ci;
+    int64_t* const s_prow = reinterpret_cast<int64_t*>(s_ck);
+    int win_first = 0, win_e = 0;
+    bool plan_bad_user = false;
+    if (planning) {
+        win_first = s0 > 0 ? (s0 >> a.log2_block) : 0;
+        const int j = win_first + tid;
+        win_e = tid < kPlanWin && j < a.max_blocks ? a.block_table[int64_t(b) * a.max_blocks + j] : 0;
+        plan_bad_user = mapped ? (pu < 0 || pu >= a.num_users) : bad_user;
+    }
+
     if (bad_user && tid == 0 && cidx == 0) atomicOr(a.err, FS_ERR_USER);
     if (chunked && kk == 0) return;
     if (kk == 0) {
@@ -327,18 +473,19 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
             if (a.out_scores) a.out_scores[int64_t(b) * k + j] = -__builtin_huge_val();
         }
         if (a.num_tokens && tid == 0) a.num_tokens[b] = 0;
+        if (planning)
+            plan_selected<kT>(a, b, 0, base, cand_idx, false, plan_bad_user, s0, win_first, win_e, s_poff, s_prow,
+                              s_win, &s_plen, &s_pbits);
         return;
     }
 
     const double* sc = a.scores + int64_t(b) * a.stride + c0;
 
     bool tokens_known = false;           // the fast path sums the lengths itself
+    bool plan_known = false;             // the fast path lays the plan's segment itself
 
     // ---- first try: threshold bin, then rank the candidates ---------------
     __shared__ int s_bin[kBins];
-    __shared__ uint64_t s_ck[kCandMax];
-    __shared__ int32_t s_ci[kCandMax];
-    __shared__ int32_t s_cl[kCandMax];   // candidate's fact length
     __shared__ double s_wlo[kTopkWaves], s_whi[kTopkWaves];
     __shared__ int s_wbad[kTopkWaves], s_wsum[kTopkWaves];
     __shared__ int s_t, s_C, s_nc;
@@ -350,13 +497,17 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
         // a candidate's length loaded only once it is found costs a round
         // trip per candidate a thread holds
         int32_t lv[kKeep];
+        // and, when planning, their first arena rows
+        int64_t rv[kKeep];
         const bool pre_len = !mapped && a.fact_len;
+        const bool pre_row = pre_len && planning;
         const int tail0 = tid + kKeep * kTopkThreads;
 #pragma unroll
         for (int j = 0; j < kKeep; ++j) {
             const int i = tid + j * kTopkThreads;
             xv[j] = i < n ? sc[i] : 0.0;
             lv[j] = pre_len && i < n ? a.fact_len[base + i] : 0;
+            rv[j] = pre_row && i < n ? a.fact_begin[base + i] : 0;
         }
         double lo = __builtin_huge_val(), hi = -__builtin_huge_val();
         int bad = 0;
@@ -444,34 +595,37 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
             __syncthreads();
             const int t = s_t, C = s_C;
             if (C <= kCandMax) {
-                // len < 0: the length is loaded here
-                auto gather = [&](double x, int i, int32_t len) {
+                // len < 0: the length (and, planning, the first row) is loaded here
+                auto gather = [&](double x, int i, int32_t len, int64_t r0) {
                     if (value_bin(x, lo, scale) >= t) {
                         const int slot = atomicAdd(&s_nc, 1);
                         const int32_t id = cand_id(i);
                         s_ck[slot] = order_key(x);
                         s_ci[slot] = id;
                         s_cl[slot] = len >= 0 ? len : (a.fact_len ? a.fact_len[base + id] : 0);
+                        if (planning && slot < 64) s_cr[slot] = len >= 0 ? r0 : a.fact_begin[base + id];
                     }
                 };
 #pragma unroll
                 for (int j = 0; j < kKeep; ++j)
-                    if (tid + j * kTopkThreads < n) gather(xv[j], tid + j * kTopkThreads, pre_len ? lv[j] : -1);
-                for (int i = tail0; i < n; i += kTopkThreads) gather(sc[i], i, -1);
+                    if (tid + j * kTopkThreads < n)
+                        gather(xv[j], tid + j * kTopkThreads, pre_len ? lv[j] : -1, rv[j]);
+                for (int i = tail0; i < n; i += kTopkThreads) gather(sc[i], i, -1, 0);
                 __syncthreads();
                 if (C <= 64) {
                     // one wave sorts the candidates in registers (bitonic,
                     // best first): a lane per candidate, the padding lanes
                     // worse than any candidate
                     if (wave == 0) {
+                        // each lane carries its candidate's slot
                         uint64_t key = lane < C ? s_ck[lane] : 0;
                         int32_t idx = lane < C ? s_ci[lane] : INT32_MAX;
-                        int32_t len = lane < C ? s_cl[lane] : 0;
+                        int32_t slot = lane;
                         for (int kw = 2; kw <= 64; kw <<= 1) {
                             for (int jw = kw >> 1; jw > 0; jw >>= 1) {
                                 const uint64_t ok = __shfl_xor(key, jw, 64);
                                 const int32_t oi = __shfl_xor(idx, jw, 64);
-                                const int32_t ol = __shfl_xor(len, jw, 64);
+                                const int32_t os = __shfl_xor(slot, jw, 64);
                                 // the lower lane of a pair keeps the better one in a
                                 // best-first run, the worse one in a worst-first run
                                 const bool lower = (lane & jw) == 0;
@@ -480,22 +634,35 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
                                 if (other_better == (lower == best_first)) {
                                     key = ok;
                                     idx = oi;
-                                    len = ol;
+                                    slot = os;
                                 }
                             }
                         }
-                        const int tok = lane < kk ? len : 0;
-                        int sum = tok;
+                        const int tok = lane < kk ? s_cl[slot] : 0;
+                        int incl = tok;
 #pragma unroll
-                        for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+                        for (int o = 1; o < 64; o <<= 1) {
+                            const int y = __shfl_up(incl, o, 64);
+                            if (lane >= o) incl += y;
+                        }
+                        const int sum = __shfl(incl, 63, 64);
                         if (lane < kk) {
                             cand_key[lane] = key;
                             cand_idx[lane] = idx;
+                            if (planning) {
+                                // rank lane's segment offset and first row
+                                s_poff[lane] = incl - tok;
+                                s_prow[lane] = s_cr[slot];
+                            }
                         }
-                        if (lane == 0) s_tokens = sum;
+                        if (lane == 0) {
+                            s_tokens = sum;
+                            s_plen = sum;
+                        }
                     }
                     __syncthreads();
                     tokens_known = true;
+                    plan_known = true;
                     goto outputs;
                 }
                 int my_tokens = 0;
@@ -731,6 +898,9 @@ outputs:
         }
         if (tid == 0) a.num_tokens[b] = s_tokens;
     }
+    if (planning)
+        plan_selected<kT>(a, b, kk, base, cand_idx, plan_known, plan_bad_user, s0, win_first, win_e, s_poff, s_prow,
+                          s_win, &s_plen, &s_pbits);
 }
 
 }  // namespace
@@ -740,10 +910,14 @@ namespace {
 
 // One block per request; n_max bounds the scores any request of the launch has.
 void launch_topk(int64_t n_max, dim3 grid, size_t lds, hipStream_t stream, const TopkArgs& a) {
-    if (n_max <= kTopkSmallN)
-        fs_topk_kernel<256><<<grid, 256, lds, stream>>>(a);
-    else
-        fs_topk_kernel<1024><<<grid, 1024, lds, stream>>>(a);
+    const bool plan = a.plan.hdr != nullptr;
+    if (n_max <= kTopkSmallN) {
+        if (plan) fs_topk_kernel<256, true><<<grid, 256, lds, stream>>>(a);
+        else fs_topk_kernel<256, false><<<grid, 256, lds, stream>>>(a);
+    } else {
+        if (plan) fs_topk_kernel<1024, true><<<grid, 1024, lds, stream>>>(a);
+        else fs_topk_kernel<1024, false><<<grid, 1024, lds, stream>>>(a);
+    }
 }
 
 }  // namespace
@@ -752,7 +926,7 @@ hipError_t fsi_launch_retrieve(const RetrieveLaunch& r) {
     const fs_store* st = r.st;
     const fs_store_desc& d = st->desc;
     if (r.k > 0 && st->max_user_facts > 0) {
-        ScoreArgs sa;
+        ScoreArgs sa{};
         sa.emb = reinterpret_cast<const float4*>(st->emb);
         sa.e4 = d.embed_dim / 4;
         sa.user_begin = st->d_user_begin;
@@ -781,11 +955,25 @@ hipError_t fsi_launch_retrieve(const RetrieveLaunch& r) {
     ta.out_scores = r.scores;
     ta.num_tokens = r.num_tokens;
     ta.err = st->d_err;
+    if (r.plan) {
+        ta.plan = fsi_plan_view(st, r.batch, r.plan);
+        ta.plan_key = fsi_plan_key(st->tag, r.batch, r.k, st->seg_tokens, r.num_blocks);
+        ta.plan_tag = st->tag;
+        ta.batch = r.batch;
+        ta.seg_tokens = st->seg_tokens;
+        ta.num_blocks = r.num_blocks;
+        ta.max_blocks = r.max_blocks;
+        ta.log2_block = st->log2_block;
+        ta.block_table = r.block_table;
+        ta.start_pos = r.start_pos;
+        ta.fact_begin = st->d_fact_begin;
+    }
     if (st->topk_chunks > 0 && r.k > 0) {
         // large users: the top k of every chunk, one block each, then the top
         // k of those candidates by (score desc, fact id asc).  Every fact of
         // the true top k is among its own chunk's top k, so this is exact.
         TopkArgs t1 = ta;
+        t1.plan = PlanView{};
         t1.fact_len = nullptr;
         t1.num_tokens = nullptr;
         t1.ids = st->d_tk_ids;

@@ -50,7 +50,7 @@ FS_KV_PINNED_HOST = 1
 
 EXPORTS = ("fs_create_store", "fs_destroy_store", "fs_retrieve_topk", "fs_inject",
            "fs_inject_layers", "fs_inject_noalloc", "fs_inject_plan_size", "fs_plan_inject",
-           "fs_inject_planned", "fs_fetch_async", "fs_attend_prefill", "fs_attend_workspace_size", "fs_ingest_init",
+           "fs_inject_planned", "fs_retrieve_plan", "fs_fetch_async", "fs_attend_prefill", "fs_attend_workspace_size", "fs_ingest_init",
            "fs_ingest_facts", "fs_evict_fact", "fs_store_live", "fs_ivf_build",
            "fs_ivf_destroy", "fs_ivf_arrays", "fs_ivf_retrieve_topk", "fs_poll_errors", "fs_check_block_tables",
            "fs_strerror", "fs_last_error_message")
@@ -111,6 +111,7 @@ def _load() -> ctypes.CDLL:
         "fs_inject_noalloc": (i32, [P, i32, i32, P, P, i32, P, i32, P, P, P, i32, P]),
         "fs_inject_plan_size": (i32, [P, i32, ctypes.POINTER(ctypes.c_size_t)]),
         "fs_plan_inject": (i32, [P, i32, P, P, i32, P, i32, P, i32, P, ctypes.c_size_t, P]),
+        "fs_retrieve_plan": (i32, [P, i32, P, P, i32, P, P, P, P, i32, P, i32, P, ctypes.c_size_t, P]),
         "fs_inject_planned": (i32, [P, i32, i32, i32, i32, P, ctypes.c_size_t, P, P, i32, P]),
         "fs_fetch_async": (i32, [P, i32, P, P, i32, i32, i32, P]),
         "fs_attend_prefill": (i32, [P, i32, i32, i32, P, P, P, i32, P, i32, P, P, ctypes.c_float,
@@ -401,6 +402,33 @@ def prepare_inject_planned(store, layers, batch: int, k: int, plan: torch.Tensor
     args = (_handle(store), lb, le, int(batch), int(k), _ptr(plan, torch.uint8, name="plan"),
             ctypes.c_size_t(plan.numel()), caches.k, caches.v, caches.num_blocks, _stream(stream))
     return Prepared(_lib.fs_inject_planned, args, "fs_inject_planned", (store, plan, caches))
+
+
+def prepare_retrieve_plan(store, batch: int, user, query, k: int, ids, block_table, max_blocks: int,
+                          start_pos, num_blocks: int, plan: torch.Tensor, scores=None, num_tokens=None,
+                          stream=None) -> Prepared:
+    """fs_retrieve_plan: retrieve the top k of each request and write the
+    inject plan of the selected ids into ``plan``."""
+    d = store.desc if isinstance(store, Store) else None
+    E = d.embed_dim if d is not None else query.shape[-1]
+    args = (_handle(store), int(batch),
+            _ptr(user, torch.int32, shape=(batch,), name="user"),
+            _ptr(query, torch.float32, shape=(batch, E), name="query"), int(k),
+            _ptr(ids, torch.int32, shape=(batch, k), name="ids"),
+            _ptr(scores, torch.float64, shape=(batch, k), name="scores"),
+            _ptr(num_tokens, torch.int32, shape=(batch,), name="num_tokens"),
+            _ptr(block_table, torch.int32, shape=(batch, max_blocks), name="block_table"),
+            int(max_blocks),
+            _ptr(start_pos, torch.int32, shape=(batch,), name="start_pos"), int(num_blocks),
+            _ptr(plan, torch.uint8, name="plan"), ctypes.c_size_t(plan.numel()), _stream(stream))
+    return Prepared(_lib.fs_retrieve_plan, args, "fs_retrieve_plan",
+                    (store, user, query, ids, scores, num_tokens, block_table, start_pos, plan))
+
+
+def fs_retrieve_plan(store, batch: int, user, query, k: int, ids, block_table, max_blocks: int, start_pos,
+                     num_blocks: int, plan: torch.Tensor, scores=None, num_tokens=None, stream=None) -> None:
+    prepare_retrieve_plan(store, batch, user, query, k, ids, block_table, max_blocks, start_pos, num_blocks,
+                          plan, scores, num_tokens, stream)()
 
 
 def fs_plan_inject(store, batch: int, user, ids, k: int, block_table, max_blocks: int, start_pos,

@@ -160,5 +160,7 @@ def test_null_store_is_rejected_everywhere():
     assert L.fs_plan_inject(None, 1, FAKE, FAKE, 1, FAKE, 4, FAKE, 4, FAKE, 1 << 20, None) == fs.FS_E_ARG
     assert L.fs_inject_planned(None, 0, 1, 1, 1, FAKE, 1 << 20, arr, arr, 4, None) == fs.FS_E_ARG
     assert L.fs_inject_noalloc(None, 0, 1, FAKE, FAKE, 1, FAKE, 1, FAKE, arr, arr, 4, None) == fs.FS_E_ARG
+    assert L.fs_retrieve_plan(None, 1, FAKE, FAKE, 1, FAKE, None, None, FAKE, 4, FAKE, 4, FAKE, 1 << 20,
+                              None) == fs.FS_E_ARG
     assert L.fs_poll_errors(None, None, ctypes.byref(flags)) == fs.FS_E_ARG
     assert L.fs_destroy_store(None) == fs.FS_OK
