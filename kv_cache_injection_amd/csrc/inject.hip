@@ -54,7 +54,12 @@ constexpr int kPlanThreads = 1024;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 ld_stream(const FS_GLOBAL u32x4* p) { return __builtin_nontemporal_load(p); }
-__device__ __forceinline__ void st_stream(FS_GLOBAL u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+// A streaming store at device scope (sc1 nt).  Against the plain streaming
+// store (nt alone), a gather of 2 KB rows into 32 KB cache blocks at the
+// inject's size ran 2% faster: 67.4 against 68.9 us.
+__device__ __forceinline__ void st_stream(FS_GLOBAL u32x4* p, u32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1 nt" ::"v"(p), "v"(v) : "memory");
+}
 // a cache row store: streaming, or through the caches when the launch's
 // writes fit in the last-level cache (a compile-time choice: a branch per
 // store cost the streaming launch 3%)
