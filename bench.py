@@ -3,18 +3,22 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config llama] [--k 50]
 
 One step = one pass of the whole hot path over one batch of requests:
-fs_retrieve_topk (embedding scores + top-k + segment length) followed by one
-all-layer fs_inject (gather -> Chunked RoPE -> paged scatter into every layer's
-cache).  Inputs are resident in HBM before the timed region; every step uses
-a different (query, start position, block table) set, cycling through
---sets pre-drawn sets, so the selected facts change from step to step.
+fs_retrieve_plan (embedding scores, then a top-k whose block also composes
+and validates the segment and writes the inject plan) followed by one
+all-layer fs_inject_planned (gather -> Chunked RoPE -> paged scatter into
+every layer's cache, streaming from that plan).  Inputs are resident in HBM
+before the timed region; every step uses a different (query, start
+position, block table) set, cycling through --sets pre-drawn sets, so the
+selected facts change from step to step.
 
 Steps are issued as a serving loop with two lanes would: step i runs its
 retrieval and then its injection on stream i % 2, so step i+1's retrieval
 (latency-bound, a few MB) and the start of its injection overlap step i's
 injection (bandwidth-bound).  Retrievals share the store's scratch, so each
 waits on an event after the previous one; the lanes inject into separate
-cache pools.  request_latency_us.in_order runs the requests on one stream,
+cache pools.  two_calls times the same loop through fs_retrieve_topk and the
+fused fs_inject (plan kernel + row kernel); both loops run in the warm-up.
+request_latency_us.in_order runs the requests on one stream,
 strictly one after the other, as a single request is served:
 fs_retrieve_plan (scores, then top-k whose block also writes the inject
 plan) and fs_inject_planned (the row kernel); in_order_two_calls does the
@@ -64,7 +68,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=300)
-    p.add_argument("--warmup", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--config", default="llama",
                    choices=["tiny", "llama", "qwen", "concurrent", "large"])
     p.add_argument("--k", type=int, default=None)
@@ -173,17 +177,29 @@ def main():
               for i in range(total)]
         jc = [fs.prepare_inject_planned(ds.store, fs.FS_ALL_LAYERS, B, k, plans[i], cache_of(i),
                                         stream=stream_inj(i)) for i in range(total)]
-        return rc, ic, pc, jc
-    ret_p, inj_p, _, _ = prep(lambda i: lanes[i % 2], lambda i: lanes[i % 2],
-                              lambda i: caches if i % 2 == 0 else caches2)         # two lanes
+        # retrieval that also writes the step's plan
+        rp = [fs.prepare_retrieve_plan(ds.store, B, user, sets[i % len(sets)]["query"], k, ids[i],
+                                       sets[i % len(sets)]["block_table"], mb, sets[i % len(sets)]["start_pos"],
+                                       nb, plans[i], num_tokens=ntok[i], stream=stream_ret(i)) for i in range(total)]
+        return rc, ic, pc, jc, rp
+    ret_p, inj_p, _, injp_p, rp_p = prep(lambda i: lanes[i % 2], lambda i: lanes[i % 2],
+                                         lambda i: caches if i % 2 == 0 else caches2)   # two lanes
     cur = torch.cuda.current_stream()
-    ret_s, inj_s, plan_s, injp_s = prep(lambda i: cur, lambda i: cur)           # one stream, in order
-    # retrieval that also writes the step's plan (one stream)
-    rp_s = [fs.prepare_retrieve_plan(ds.store, B, user, sets[i % len(sets)]["query"], k, ids[i],
-                                     sets[i % len(sets)]["block_table"], mb, sets[i % len(sets)]["start_pos"],
-                                     nb, plans[i], num_tokens=ntok[i], stream=cur) for i in range(total)]
+    ret_s, inj_s, plan_s, injp_s, rp_s = prep(lambda i: cur, lambda i: cur)            # one stream, in order
 
     def step_pipelined(i):
+        # the planning retrieval writes the step's plan, and the row kernel
+        # streams from it
+        lane = lanes[i % 2]
+        if i > 0:
+            lane.wait_event(ret_done[i - 1])
+        rp_p[i]()
+        ret_done[i].record(lane)
+        injp_p[i]()
+
+    def step_pipelined_two_calls(i):
+        # the same lanes with fs_retrieve_topk and the fused fs_inject (plan
+        # kernel + row kernel)
         lane = lanes[i % 2]
         if i > 0:
             lane.wait_event(ret_done[i - 1])
@@ -197,6 +213,7 @@ def main():
 
     print(f"[bench] warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
+        step_pipelined_two_calls(i)
         step_pipelined(i)
     torch.cuda.synchronize()
     # timed region 1: the whole hot path for every step, each lane's
@@ -210,12 +227,22 @@ def main():
     if flags:
         raise RuntimeError(f"device error bits 0x{flags:x}")
     L = ntok.cpu().numpy().astype(np.int64)[args.warmup:]          # [steps, B]
+    # timed region 1c (beside value): the same two-lane loop through the
+    # two-call path
+    w0 = time.perf_counter()
+    for i in range(args.warmup, total):
+        step_pipelined_two_calls(i)
+    torch.cuda.synchronize()
+    w1 = time.perf_counter()
+    if not np.array_equal(ntok.cpu().numpy().astype(np.int64)[args.warmup:], L):
+        raise RuntimeError("the two pipelined loops selected different segments")
 
-    # every kernel regions 1b and 2 time has run before them: the pipelined
-    # steps ran the retrievals and fused injects; the plans, the injects from
-    # plans and the planning retrievals run here (a first launch pays
-    # one-time costs)
+    # every kernel regions 1b and 2 time has run before them (the pipelined
+    # warm-up ran each kind on the lanes); they run here once more on the
+    # timing stream (a first launch pays one-time costs)
     for i in range(min(total, max(args.warmup, 5))):
+        ret_s[i]()
+        inj_s[i]()
         plan_s[i]()
         injp_s[i]()
         rp_s[i]()
@@ -301,6 +328,7 @@ def main():
     in_order_two_us = (u2 - u1) / args.steps * 1e6
     value = float(step_bytes.sum() / wall / 1e9)
     ms_per_step = wall / args.steps * 1e3
+    wall_two = w1 - w0
     traffic = recorded_traffic(args.config, nl)
 
     copy = None
@@ -341,6 +369,10 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "ms_per_step_in_order": round(in_order_us * 1e-3, 5),
+        "two_calls": {"ms_per_step": round(wall_two / args.steps * 1e3, 5),
+                      "value": round(float(step_bytes.sum() / wall_two / 1e9), 2),
+                      "note": "the same two-lane loop through fs_retrieve_topk and the fused fs_inject "
+                              "(plan kernel + row kernel)"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -108,13 +108,17 @@ def test_pinned_layer_pipeline_two_batches_match_device_store():
     dev.close()
 
 
-def test_two_lane_steps_match_one_stream():
+@pytest.mark.parametrize("path", ["planned", "two_calls"])
+def test_two_lane_steps_match_one_stream(path):
     """The bench's serving loop: step i retrieves then injects on stream
     i % 2, each retrieval after the previous one (an event), the lanes writing
-    separate cache pools, so consecutive injects run side by side.  Every
+    separate cache pools, so consecutive injects run side by side.  planned:
+    fs_retrieve_plan writes each step's plan and fs_inject_planned streams
+    from it; two_calls: fs_retrieve_topk, then the fused fs_inject.  Every
     step's ids and cache pool must equal the same step run alone on one
-    stream (which the parity tests compare with the oracle), and one step is
-    checked against the oracle directly."""
+    stream through fs_retrieve_topk and fs_inject (which the parity tests
+    compare with the oracle), and one step is checked against the oracle
+    directly."""
     wl = synth.make_workload("llama", seed=1007)
     s = wl.shape
     layers = [0, 1, 2, 3]
@@ -132,16 +136,25 @@ def test_two_lane_steps_match_one_stream():
     ntok = [torch.zeros((B,), dtype=torch.int32, device="cuda") for _ in range(n)]
     scores = [torch.zeros((B, k), dtype=torch.float64, device="cuda") for _ in range(n)]
     pools = [synth.make_caches(wl, layers, "cuda") for _ in range(n)]
-    say("two lanes: 6 pipelined steps")
+    plans = [fs.new_inject_plan(ds.store, B) for _ in range(n)]
+    say(f"two lanes ({path}): 6 pipelined steps")
     for i, r in enumerate(sets):
         lane = lanes[i % 2]
         if i > 0:
             lane.wait_event(done[i - 1])
-        fs.fs_retrieve_topk(ds.store, B, r["user"], r["query"], k, ids[i], scores[i], ntok[i], stream=lane)
-        done[i].record(lane)
         kc, vc = pools[i]
-        fs.fs_inject(ds.store, fs.FS_ALL_LAYERS, B, r["user"], ids[i], k, r["block_table"], mb,
-                     r["start_pos"], kc, vc, kc[0].shape[0], stream=lane)
+        nb = kc[0].shape[0]
+        if path == "planned":
+            fs.fs_retrieve_plan(ds.store, B, r["user"], r["query"], k, ids[i], r["block_table"], mb,
+                                r["start_pos"], nb, plans[i], scores=scores[i], num_tokens=ntok[i], stream=lane)
+            done[i].record(lane)
+            fs.fs_inject_planned(ds.store, fs.FS_ALL_LAYERS, B, k, plans[i], fs.CacheTable(ds.store, kc, vc, nb),
+                                 stream=lane)
+        else:
+            fs.fs_retrieve_topk(ds.store, B, r["user"], r["query"], k, ids[i], scores[i], ntok[i], stream=lane)
+            done[i].record(lane)
+            fs.fs_inject(ds.store, fs.FS_ALL_LAYERS, B, r["user"], ids[i], k, r["block_table"], mb,
+                         r["start_pos"], kc, vc, nb, stream=lane)
     torch.cuda.synchronize()
     assert fs.fs_poll_errors(ds.store) == 0
     say("two lanes: the same steps one by one on one stream")
