@@ -877,7 +877,7 @@ def inject_source_digest() -> str:
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in ("inject.hip", "fs_internal.h", "fs_device.h"):
+    for f in ("inject.hip", "fs_internal.h", "fs_device.h", "fs_plan.h"):
         with open(os.path.join(ROOT, "kv_cache_injection_amd", "csrc", f)) as fh:
             text = fh.read()
         # string literals are kept whole; // and /* */ comments go
@@ -890,8 +890,8 @@ def inject_source_digest() -> str:
 def recorded_traffic(config: str, layers: int):
     """HBM bytes per inject launch from the committed rocprofv3 counter record
     (FETCH_SIZE and WRITE_SIZE, scaled by what the same counters read for a
-    plain 1 GiB copy), or None when the record is for another kernel build or
-    workload."""
+    device copy of one inject's bytes), or None when the record is for
+    another kernel build or workload."""
     path = os.path.join(ROOT, "profiles", "inject_llama_hbm_traffic.json")
     try:
         with open(path) as fh:
