@@ -380,9 +380,9 @@ __device__ __forceinline__ void fill_cs(double2* s_cs, const double* w_e, int st
 // they own, then the K row, then evaluate cos/sin(p * w_i) in fp64 into LDS
 // while the row is in flight; a lane's rotate-half partner (D/16 lanes away,
 // in the same head) arrives by a cross-lane move.  Per launch on the Llama
-// shape: 73 us, against 80 us for a block of 8 tokens x all heads x K and V
-// with a per-block plan and cos/sin table, 75 us for two vectors per lane,
-// and 66 us for the same bytes as a contiguous copy.
+// shape: 68.8 us, against 80 us for a block of 8 tokens x all heads x K and V
+// with a per-block plan and cos/sin table, and 73.8 us for the runtime's
+// device copy of the same bytes.
 template <int D, int kLg, bool kStaged, bool kCached>
 __global__ __launch_bounds__(kFlatThreads) void fs_row_kernel(FlatArgs a) {
     constexpr int kSplit = kLg > 8 ? kLg - 8 : 0;              // log2 workgroups per row
