@@ -74,6 +74,29 @@ __device__ __forceinline__ int value_bin(double x, double lo, double scale) {
     return bin < kBins - 1 ? bin : kBins - 1;
 }
 
+// The value of lane (lane ^ m) for m a power of two below 64, without an
+// LDS round trip where the lane pattern allows: m = 1 and 2 by DPP quad
+// permutes, 4, 8 and 16 by swizzles within 32 lanes, 32 by a bpermute.
+// Folds to one instruction when m is a constant.
+__device__ __forceinline__ int xor_lane(int v, int m) {
+    switch (m) {
+        case 1: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+        case 2: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+        case 4: return __builtin_amdgcn_ds_swizzle(v, 0x101F);
+        case 8: return __builtin_amdgcn_ds_swizzle(v, 0x201F);
+        case 16: return __builtin_amdgcn_ds_swizzle(v, 0x401F);
+        default: return __shfl_xor(v, m, 64);
+    }
+}
+__device__ __forceinline__ uint64_t xor_lane(uint64_t v, int m) {
+    const int lo = xor_lane(static_cast<int>(static_cast<uint32_t>(v)), m);
+    const int hi = xor_lane(static_cast<int>(v >> 32), m);
+    return (uint64_t(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+__device__ __forceinline__ double xor_lane(double v, int m) {
+    return __longlong_as_double(static_cast<long long>(xor_lane(static_cast<uint64_t>(__double_as_longlong(v)), m)));
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
@@ -426,6 +449,22 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
                                  : (bad_user ? 0 : (a.user_count ? a.user_count[u]
                                                                 : static_cast<int32_t>(a.user_begin[u + 1] - ubase)));
     const int32_t c0 = cidx * a.chunk;              // first score of this block's chunk
+    // scores i = tid + j*blockDim.x: the first kKeep of each thread stay in
+    // registers for the later passes (the rest, for large users, are
+    // re-read).  Their address depends only on the request, so they are
+    // loaded before anything else, beside the user -> range chain; entries
+    // past the request's count (inside the scratch row) are loaded and never
+    // used.
+    const double* sc = a.scores + int64_t(b) * a.stride + c0;
+    double xv[kKeep];
+    {
+        const int32_t in_row = a.stride - c0;
+#pragma unroll
+        for (int j = 0; j < kKeep; ++j) {
+            const int i = tid + j * kTopkThreads;
+            xv[j] = i < in_row ? sc[i] : 0.0;
+        }
+    }
     const int32_t n = chunked ? max(0, min(a.chunk, n_all - c0)) : n_all;
     const int64_t base = ubase + c0;
     const int kk = n < k ? n : k;
@@ -479,8 +518,6 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
         return;
     }
 
-    const double* sc = a.scores + int64_t(b) * a.stride + c0;
-
     bool tokens_known = false;           // the fast path sums the lengths itself
     bool plan_known = false;             // the fast path lays the plan's segment itself
 
@@ -490,12 +527,9 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
     __shared__ int s_wbad[kTopkWaves], s_wsum[kTopkWaves];
     __shared__ int s_t, s_C, s_nc;
     {
-        // scores i = tid + j*blockDim.x: the first kKeep stay in registers
-        // for the later passes, the rest (large users) are re-read
-        double xv[kKeep];
-        // and, for plain requests, their facts' lengths, fetched with them:
-        // a candidate's length loaded only once it is found costs a round
-        // trip per candidate a thread holds
+        // for plain requests, the kept scores' fact lengths, fetched once
+        // the range is known: a candidate's length loaded only once it is
+        // found costs a round trip per candidate a thread holds
         int32_t lv[kKeep];
         // and, when planning, their first arena rows
         int64_t rv[kKeep];
@@ -505,7 +539,6 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
 #pragma unroll
         for (int j = 0; j < kKeep; ++j) {
             const int i = tid + j * kTopkThreads;
-            xv[j] = i < n ? sc[i] : 0.0;
             lv[j] = pre_len && i < n ? a.fact_len[base + i] : 0;
             rv[j] = pre_row && i < n ? a.fact_begin[base + i] : 0;
         }
@@ -522,9 +555,9 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
         for (int i = tail0; i < n; i += kTopkThreads) see(sc[i]);
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) {
-            lo = fmin(lo, __shfl_xor(lo, m, 64));
-            hi = fmax(hi, __shfl_xor(hi, m, 64));
-            bad |= __shfl_xor(bad, m, 64);
+            lo = fmin(lo, xor_lane(lo, m));
+            hi = fmax(hi, xor_lane(hi, m));
+            bad |= xor_lane(bad, m);
         }
         if (lane == 0) {
             s_wlo[wave] = lo;
@@ -621,11 +654,13 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
                         uint64_t key = lane < C ? s_ck[lane] : 0;
                         int32_t idx = lane < C ? s_ci[lane] : INT32_MAX;
                         int32_t slot = lane;
+#pragma unroll
                         for (int kw = 2; kw <= 64; kw <<= 1) {
+#pragma unroll
                             for (int jw = kw >> 1; jw > 0; jw >>= 1) {
-                                const uint64_t ok = __shfl_xor(key, jw, 64);
-                                const int32_t oi = __shfl_xor(idx, jw, 64);
-                                const int32_t os = __shfl_xor(slot, jw, 64);
+                                const uint64_t ok = xor_lane(key, jw);
+                                const int32_t oi = xor_lane(idx, jw);
+                                const int32_t os = xor_lane(slot, jw);
                                 // the lower lane of a pair keeps the better one in a
                                 // best-first run, the worse one in a worst-first run
                                 const bool lower = (lane & jw) == 0;
