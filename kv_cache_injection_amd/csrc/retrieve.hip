@@ -49,6 +49,7 @@ constexpr int kScoreWaves = 4;
 constexpr int kScoreRowsPerWave = 2;
 constexpr int kScoreRowsPerBlock = kScoreWaves * kScoreRowsPerWave;
 constexpr int kScoreGroup = 8;       // queries of one user scored per block
+constexpr int kScoreChunks = 4;      // float4 chunks of a row a lane loads at once (E up to 1024)
 constexpr int kTopkSmallN = 4096;     // up to this many scores a 256-thread block selects
 constexpr int kBins = 2048;          // value bins of the threshold search
 constexpr int kCandMax = 2048;       // largest candidate set ranked directly
@@ -124,17 +125,22 @@ __device__ __forceinline__ void fma4(double& acc, const float4& e, const float4&
 }
 
 // Block (row tile, request b).  Requests of one user that follow each other
-// (within an aligned group of kScoreGroup) are scored together by the block
+// (within an aligned group of kGroup) are scored together by the block
 // of the first of them: its rows are read once for all their queries.  The
 // other blocks of the run exit at once.  Every score still accumulates the
 // same products in the same order, so it does not depend on the grouping.
+// kGroup = 1 (launches of one request) loads all of its two rows' chunks
+// before the first product, so the rows arrive in one round trip; kGroup =
+// kScoreGroup loops over the chunks two at a time, with fewer registers.
+// Both accumulate the same products in the same order.
+template <int kGroup>
 __global__ __launch_bounds__(256) void fs_score_kernel(ScoreArgs a) {
     const int b = blockIdx.y;
     const int u = a.user[b];
     if (u < 0 || u >= a.num_users) return;
-    if (b % kScoreGroup != 0 && a.user[b - 1] == u) return;   // scored by the run's first block
+    if (b % kGroup != 0 && a.user[b - 1] == u) return;   // scored by the run's first block
     int nq = 1;
-    while (nq < kScoreGroup && (b + nq) % kScoreGroup != 0 && b + nq < a.batch && a.user[b + nq] == u) ++nq;
+    while (nq < kGroup && (b + nq) % kGroup != 0 && b + nq < a.batch && a.user[b + nq] == u) ++nq;
     const int64_t base = a.user_begin[u];
     const int32_t n = a.user_count ? a.user_count[u] : static_cast<int32_t>(a.user_begin[u + 1] - base);
     const int32_t row0 = blockIdx.x * kScoreRowsPerBlock;
@@ -149,24 +155,49 @@ __global__ __launch_bounds__(256) void fs_score_kernel(ScoreArgs a) {
     // the queries are read straight from global memory (cached after the
     // first wave touches them), so their loads overlap the embedding loads
     const float4* qv = a.query + int64_t(b) * a.e4;
-    double acc[kScoreGroup][2];
+    double acc[kGroup][2];
 #pragma unroll
-    for (int q = 0; q < kScoreGroup; ++q) acc[q][0] = acc[q][1] = 0.0;
-#pragma unroll 2
-    for (int c = lane; c < a.e4; c += 64) {
-        const float4 ea = e0[c];
-        const float4 eb = e1[c];
+    for (int q = 0; q < kGroup; ++q) acc[q][0] = acc[q][1] = 0.0;
+    auto accumulate = [&](int c, const float4& ea, const float4& eb) {
 #pragma unroll
-        for (int q = 0; q < kScoreGroup; ++q) {
+        for (int q = 0; q < kGroup; ++q) {
             if (q < nq) {
                 const float4 qq = qv[int64_t(q) * a.e4 + c];
                 fma4(acc[q][0], ea, qq);
                 fma4(acc[q][1], eb, qq);
             }
         }
+    };
+    if (kGroup == 1 && a.e4 <= 64 * kScoreChunks) {
+        // every chunk of both rows is loaded before the first product; the
+        // products then run in column order as in the loop below
+        float4 ea[kScoreChunks], eb[kScoreChunks];
+#pragma unroll
+        for (int j = 0; j < kScoreChunks; ++j) {
+            const int c = lane + 64 * j;
+            ea[j] = c < a.e4 ? e0[c] : float4{};
+            eb[j] = c < a.e4 ? e1[c] : float4{};
+        }
+#pragma unroll
+        for (int j = 0; j < kScoreChunks; ++j)
+            if (lane + 64 * j < a.e4) accumulate(lane + 64 * j, ea[j], eb[j]);
+    } else {
+#pragma unroll 2
+        for (int c = lane; c < a.e4; c += 64) {
+            const float4 ea = e0[c];
+            const float4 eb = e1[c];
+#pragma unroll
+            for (int q = 0; q < kGroup; ++q) {
+                if (q < nq) {
+                    const float4 qq = qv[int64_t(q) * a.e4 + c];
+                    fma4(acc[q][0], ea, qq);
+                    fma4(acc[q][1], eb, qq);
+                }
+            }
+        }
     }
 #pragma unroll
-    for (int q = 0; q < kScoreGroup; ++q) {
+    for (int q = 0; q < kGroup; ++q) {
         if (q < nq) {
             const double s0 = wave_sum(acc[q][0]);
             const double s1 = wave_sum(acc[q][1]);
@@ -973,7 +1004,8 @@ hipError_t fsi_launch_retrieve(const RetrieveLaunch& r) {
         sa.scores = st->d_scores;
         sa.stride = st->max_user_facts;
         dim3 grid((st->max_user_facts + kScoreRowsPerBlock - 1) / kScoreRowsPerBlock, r.batch);
-        fs_score_kernel<<<grid, 256, 0, r.stream>>>(sa);
+        if (r.batch == 1) fs_score_kernel<1><<<grid, 256, 0, r.stream>>>(sa);
+        else fs_score_kernel<kScoreGroup><<<grid, 256, 0, r.stream>>>(sa);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1053,7 +1085,8 @@ hipError_t fsi_launch_ivf_probe(const IvfProbeLaunch& r) {
     sa.scores = ix->d_cscores;
     sa.stride = ix->nlist;
     dim3 g1((ix->nlist + kScoreRowsPerBlock - 1) / kScoreRowsPerBlock, r.batch);
-    fs_score_kernel<<<g1, 256, 0, r.stream>>>(sa);
+    if (r.batch == 1) fs_score_kernel<1><<<g1, 256, 0, r.stream>>>(sa);
+    else fs_score_kernel<kScoreGroup><<<g1, 256, 0, r.stream>>>(sa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
