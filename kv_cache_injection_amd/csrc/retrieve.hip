@@ -17,7 +17,7 @@
 //                batch of one user's requests scans the table once, not once
 //                per request.
 // top-k kernel   one block per request: 256 threads when no request of the
-//                launch has more than 4,096 scores (a small block starts
+//                launch has more than 2,048 scores (a small block starts
 //                sooner beside a running inject), 1,024 above.  Users above
 //                65,536 facts are selected in two phases: the top k of every
 //                16,384-score chunk (one block each), then the top k of those
@@ -50,7 +50,7 @@ constexpr int kScoreRowsPerWave = 2;
 constexpr int kScoreRowsPerBlock = kScoreWaves * kScoreRowsPerWave;
 constexpr int kScoreGroup = 8;       // queries of one user scored per block
 constexpr int kScoreChunks = 4;      // float4 chunks of a row a lane loads at once (E up to 1024)
-constexpr int kTopkSmallN = 4096;     // up to this many scores a 256-thread block selects
+constexpr int kTopkSmallN = 2048;     // up to this many scores a 256-thread block selects
 constexpr int kBins = 2048;          // value bins of the threshold search
 constexpr int kCandMax = 2048;       // largest candidate set ranked directly
 
@@ -452,7 +452,10 @@ template <int kT, bool kPlan>
 __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
     constexpr int kTopkThreads = kT;
     constexpr int kTopkWaves = kT / 64;
-    constexpr int kKeep = 4096 / kT;       // scores per thread kept in registers
+    // scores per thread kept in registers: all of a small block's requests
+    // (every kept slot costs unrolled code and registers, so no more), the
+    // first 4096 of a large block's
+    constexpr int kKeep = (kT == 256 ? kTopkSmallN : 4096) / kT;
     __shared__ int hist[256];
     __shared__ uint64_t cand_key[fsi::kMaxK];
     __shared__ int32_t cand_idx[fsi::kMaxK];
@@ -557,6 +560,7 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
     __shared__ double s_wlo[kTopkWaves], s_whi[kTopkWaves];
     __shared__ int s_wbad[kTopkWaves], s_wsum[kTopkWaves];
     __shared__ int s_t, s_C, s_nc;
+    __shared__ int s_wn[kTopkWaves];
     {
         // for plain requests, the kept scores' fact lengths, fetched once
         // the range is known: a candidate's length loaded only once it is
@@ -660,21 +664,49 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
             const int t = s_t, C = s_C;
             if (C <= kCandMax) {
                 // len < 0: the length (and, planning, the first row) is loaded here
-                auto gather = [&](double x, int i, int32_t len, int64_t r0) {
-                    if (value_bin(x, lo, scale) >= t) {
-                        const int slot = atomicAdd(&s_nc, 1);
-                        const int32_t id = cand_id(i);
-                        s_ck[slot] = order_key(x);
-                        s_ci[slot] = id;
-                        s_cl[slot] = len >= 0 ? len : (a.fact_len ? a.fact_len[base + id] : 0);
-                        if (planning && slot < 64) s_cr[slot] = len >= 0 ? r0 : a.fact_begin[base + id];
-                    }
+                auto put = [&](int slot, double x, int i, int32_t len, int64_t r0) {
+                    const int32_t id = cand_id(i);
+                    s_ck[slot] = order_key(x);
+                    s_ci[slot] = id;
+                    s_cl[slot] = len >= 0 ? len : (a.fact_len ? a.fact_len[base + id] : 0);
+                    if (planning && slot < 64) s_cr[slot] = len >= 0 ? r0 : a.fact_begin[base + id];
                 };
+                if (C <= 64 && n <= kKeep * kTopkThreads) {
+                    // few candidates, every score in registers: each wave
+                    // counts its candidates by ballot, and after one barrier
+                    // writes them at its offset in index order (no LDS
+                    // atomics)
+                    uint64_t cm[kKeep];
+                    int wn = 0;
 #pragma unroll
-                for (int j = 0; j < kKeep; ++j)
-                    if (tid + j * kTopkThreads < n)
-                        gather(xv[j], tid + j * kTopkThreads, pre_len ? lv[j] : -1, rv[j]);
-                for (int i = tail0; i < n; i += kTopkThreads) gather(sc[i], i, -1, 0);
+                    for (int j = 0; j < kKeep; ++j) {
+                        cm[j] = __builtin_amdgcn_ballot_w64(tid + j * kTopkThreads < n &&
+                                                            value_bin(xv[j], lo, scale) >= t);
+                        wn += __popcll(cm[j]);
+                    }
+                    if (lane == 0) s_wn[wave] = wn;
+                    __syncthreads();
+                    int at = 0;
+                    for (int w = 0; w < wave; ++w) at += s_wn[w];
+#pragma unroll
+                    for (int j = 0; j < kKeep; ++j) {
+                        if ((cm[j] >> lane) & 1ull) {
+                            const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(cm[j] >> 32),
+                                                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(cm[j]), 0));
+                            put(at + below, xv[j], tid + j * kTopkThreads, pre_len ? lv[j] : -1, rv[j]);
+                        }
+                        at += __popcll(cm[j]);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < kKeep; ++j)
+                        if (tid + j * kTopkThreads < n && value_bin(xv[j], lo, scale) >= t)
+                            put(atomicAdd(&s_nc, 1), xv[j], tid + j * kTopkThreads, pre_len ? lv[j] : -1, rv[j]);
+                    for (int i = tail0; i < n; i += kTopkThreads) {
+                        const double x = sc[i];
+                        if (value_bin(x, lo, scale) >= t) put(atomicAdd(&s_nc, 1), x, i, -1, 0);
+                    }
+                }
                 __syncthreads();
                 if (C <= 64) {
                     // one wave sorts the candidates in registers (bitonic,
