@@ -367,9 +367,59 @@ __device__ __forceinline__ int wave_or_u(uint32_t v) {
 template <int kT>
 __device__ void plan_selected(const TopkArgs& a, int b, int kk, int64_t base, const int32_t* cand_idx, bool known,
                               bool bad_user, int s0, int win_first, int win_e, int32_t* off, int64_t* row0,
-                              int32_t* win, int* s_len, int* s_bits) {
+                              int32_t* win, const uint64_t* win_bad, int* s_len, int* s_bits) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
+    const int nwin = max(0, min(kPlanWin, a.max_blocks - win_first));
+    if (known) {
+        // The selection laid the segment out (off, row0, *s_len) before its
+        // last barrier, and the block-table window and its bad-entry bits
+        // (win_bad, one bit per entry) are in LDS since the first one.  When
+        // the segment's blocks all fall inside the window, every thread takes
+        // the same decision from them, with no further barrier.
+        const int L = *s_len;
+        const int64_t last_pos = int64_t(s0) + L - 1;
+        const int last_blk = static_cast<int>(last_pos >> a.log2_block);
+        // (the start-position and empty cases take the general path below,
+        // which reports them exactly as the plan kernel does)
+        if (s0 >= 0 && L > 0 && int64_t(s0) + L <= int64_t(INT32_MAX) && last_blk - win_first < nwin) {
+            // entries first .. last of the segment are window entries
+            // 0 .. last_blk - win_first (the window starts at the first)
+            const int hi = last_blk - win_first;
+            uint32_t bits = bad_user ? FS_ERR_USER : 0u;
+            if (last_blk >= a.max_blocks) {
+                bits |= FS_ERR_BLOCK_SHORT;
+            } else {
+#pragma unroll
+                for (int w = 0; w < kPlanWin / 64; ++w) {
+                    uint64_t m = 64 * w <= hi ? win_bad[w] : 0ull;
+                    if (hi - 64 * w < 63) m &= (2ull << max(hi - 64 * w, 0)) - 1ull;
+                    if (m) bits |= FS_ERR_BLOCK_ID;
+                }
+            }
+            if (tid == 0) {
+                if (bits) atomicOr(a.err, bits);
+                a.plan.req[b] = PlanReq{bits ? 0 : L, s0};
+                if (b == 0) fsp::write_header(a.plan.hdr, a.plan_key, a.plan_tag, a.batch, a.k, a.seg_tokens, a.num_blocks);
+            }
+            if (bits) return;
+            PlanTok* tok = a.plan.tok + int64_t(b) * a.seg_tokens;
+            const int mask = (1 << a.log2_block) - 1;
+            const int G = kk > 0 && kk < kT ? kT / kk : 1;
+            const int sub = tid % G;
+            for (int j = tid / G; j < kk; j += kT / G) {
+                const int o = off[j];
+                const int n = (j + 1 < kk ? off[j + 1] : L) - o;
+                const int64_t r = row0[j];
+#pragma unroll 4
+                for (int t = sub; t < n; t += G) {
+                    const int p = s0 + o + t;
+                    tok[o + t] = PlanTok{r + t, (int64_t(win[(p >> a.log2_block) - win_first]) << a.log2_block) | (p & mask)};
+                }
+            }
+            return;
+        }
+    }
     if (!known && tid < 64) {
         // one dependent round: the selected facts' lengths and first rows
         int carry = 0;
@@ -392,7 +442,6 @@ __device__ void plan_selected(const TopkArgs& a, int b, int kk, int64_t base, co
         }
         if (tid == 0) *s_len = carry;
     }
-    const int nwin = max(0, min(kPlanWin, a.max_blocks - win_first));
     if (tid < kPlanWin) win[tid] = win_e;
     if (tid == 0) *s_bits = 0;
     __syncthreads();
@@ -522,6 +571,7 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
     __shared__ int32_t s_cl[kCandMax];
     __shared__ int64_t s_cr[64];
     __shared__ int32_t s_win[kPlanWin];
+    __shared__ uint64_t s_winbad[kPlanWin / 64];   // entries outside [0, num_blocks), one bit each
     __shared__ int s_plen, s_pbits;
     // the plan's per-rank segment offsets and first rows reuse the candidate
     // keys and ids, which are dead once the ranks are known
@@ -548,7 +598,7 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
         if (a.num_tokens && tid == 0) a.num_tokens[b] = 0;
         if (planning)
             plan_selected<kT>(a, b, 0, base, cand_idx, false, plan_bad_user, s0, win_first, win_e, s_poff, s_prow,
-                              s_win, &s_plen, &s_pbits);
+                              s_win, s_winbad, &s_plen, &s_pbits);
         return;
     }
 
@@ -598,6 +648,15 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
             s_wlo[wave] = lo;
             s_whi[wave] = hi;
             s_wbad[wave] = bad;
+        }
+        if (planning) {
+            // the block-table window, loaded at the start, and which of its
+            // entries name no cache block (entries past the table's row are
+            // the plan's row-length check, not marked)
+            if (tid < kPlanWin) s_win[tid] = win_e;
+            const bool off_pool = tid < kPlanWin && win_first + tid < a.max_blocks && (win_e < 0 || win_e >= a.num_blocks);
+            const uint64_t m = __builtin_amdgcn_ballot_w64(off_pool);
+            if (lane == 0 && wave < kPlanWin / 64) s_winbad[wave] = m;
         }
         for (int i = tid; i < kBins; i += blockDim.x) s_bin[i] = 0;
         if (tid == 0) {
@@ -998,7 +1057,7 @@ outputs:
     }
     if (planning)
         plan_selected<kT>(a, b, kk, base, cand_idx, plan_known, plan_bad_user, s0, win_first, win_e, s_poff, s_prow,
-                          s_win, &s_plen, &s_pbits);
+                          s_win, s_winbad, &s_plen, &s_pbits);
 }
 
 }  // namespace

@@ -175,19 +175,20 @@ def test_retrieve_plan_rejections_match_plan_inject():
     """Request 0 is served; request 1 names a user past the store, request 2
     starts at -1, request 3's table holds a block id past the cache, request
     4's table is too short for its segment, request 5 belongs to an empty
-    user.  Bits, plan lengths and the injection from the plan must equal
-    fs_plan_inject's; only request 0 is written."""
+    user, request 6's segment would run past the last int32 position.  Bits,
+    plan lengths and the injection from the plan must equal fs_plan_inject's;
+    only request 0 is written."""
     rng = np.random.default_rng(7)
     E = 32
     emb = rng.standard_normal((200, E)).astype(np.float32)
     ufb = np.array([0, 120, 120, 200], np.int64)        # user 1 is empty
     fl = rng.integers(1, 12, 200).astype(np.int32)
-    B, mb, nb, k = 6, 40, 512, 20
+    B, mb, nb, k = 7, 40, 512, 20
     st, keep = _small_store(emb, ufb, fl, H=2, D=64, bs=8, max_k=32, max_batch=B)
-    users = np.array([0, 5, 2, 0, 2, 1], np.int32)
-    q = np.ascontiguousarray(emb[[3, 4, 150, 9, 170, 5]], np.float32)
+    users = np.array([0, 5, 2, 0, 2, 1, 0], np.int32)
+    q = np.ascontiguousarray(emb[[3, 4, 150, 9, 170, 5, 11]], np.float32)
     bt = _tables(rng, B, mb, nb)
-    sp = np.array([13, 0, -1, 40, 200, 0], np.int32)
+    sp = np.array([13, 0, -1, 40, 200, 0, np.iinfo(np.int32).max - 3], np.int32)
     bt[3, 40 // 8] = nb                            # its first block: one past the cache
     # request 4: 200 + its segment (>= 20 tokens) needs more than 25 blocks of 8
     mb_short = 25
