@@ -100,7 +100,21 @@ __device__ __forceinline__ double xor_lane(double v, int m) {
 
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    for (int m = 32; m >= 1; m >>= 1) v += xor_lane(v, m);
+    return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (lane i gets v_0 + ... +
+// v_i), all lanes active: DPP shifts within each row of 16 lanes, then each
+// row's running total carried into the following rows by the row broadcasts
+// (no LDS round trip).
+__device__ __forceinline__ int wave_incl_sum(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1 and 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2 and 3
     return v;
 }
 
@@ -696,12 +710,7 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
                 cb[j] = s_bin[kBins - 1 - (kBPT * tid + j)];
                 local += cb[j];
             }
-            int incl = local;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int y = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += y;
-            }
+            const int incl = wave_incl_sum(local);
             if (lane == 63) s_wsum[wave] = incl;
             __syncthreads();
             int before = incl - local;
@@ -796,13 +805,8 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
                             }
                         }
                         const int tok = lane < kk ? s_cl[slot] : 0;
-                        int incl = tok;
-#pragma unroll
-                        for (int o = 1; o < 64; o <<= 1) {
-                            const int y = __shfl_up(incl, o, 64);
-                            if (lane >= o) incl += y;
-                        }
-                        const int sum = __shfl(incl, 63, 64);
+                        const int incl = wave_incl_sum(tok);
+                        const int sum = __builtin_amdgcn_readlane(incl, 63);
                         if (lane < kk) {
                             cand_key[lane] = key;
                             cand_idx[lane] = idx;
