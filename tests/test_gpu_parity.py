@@ -237,6 +237,56 @@ def test_retrieval_select_paths_with_ties(k):
     st.close()
 
 
+@pytest.mark.parametrize("sizes", [(2048, 37), (2047, 2048), (2049, 100), (4096, 5), (4097, 64)])
+@pytest.mark.parametrize("k", [50, 64, 65])
+def test_retrieval_at_selection_block_boundaries(sizes, k):
+    """Users at the edges of the selection block's register capacity: a
+    store whose largest user has at most 2,048 facts selects with 256
+    threads and 8 kept scores each (every score in registers at 2,048),
+    larger ones with 1,024 threads and 4 each (scores past 4,096 re-read).
+    k = 64 and 65 straddle the ballot gather and one-wave sort; ids,
+    scores and lengths must be the oracle's for every user."""
+    rng = np.random.default_rng(sum(sizes) + k)
+    E = 48
+    ufb = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    F = int(ufb[-1])
+    emb = rng.standard_normal((F, E)).astype(np.float32)
+    emb /= np.linalg.norm(emb, axis=1, keepdims=True)
+    fl = rng.integers(1, 9, F).astype(np.int32)
+    B = len(sizes)
+    st, _, _ = _small_store(emb, ufb, fl, max_k=128, max_batch=B)
+    users = np.arange(B, dtype=np.int32)
+    q = rng.standard_normal((B, E)).astype(np.float32)
+    q /= np.linalg.norm(q, axis=1, keepdims=True)
+    ids = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((B, k), dtype=torch.float64, device="cuda")
+    nt = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    say(f"selection boundaries {sizes} k={k}")
+    fs.fs_retrieve_topk(st, B, torch.from_numpy(users).cuda(), torch.from_numpy(q).cuda(), k, ids, sc, nt)
+    assert fs.fs_poll_errors(st) == 0
+    g, gs, gn = _host(ids), _host(sc), _host(nt)
+    for b in range(B):
+        o_ids, o_sc = oracle.retrieve(emb, ufb, b, q[b], k)
+        kk = min(k, sizes[b])
+        s_all = oracle.score(emb[ufb[b]:ufb[b + 1]], q[b])
+        assert oracle.decisive_gap(s_all, k) > CERT_GAP, "seed gives a near-tie"
+        assert np.array_equal(g[b].astype(np.int64), o_ids), (sizes, k, b)
+        assert np.all(np.abs(gs[b][:kk] - o_sc[:kk]) <= SCORE_ABS_TOL)
+        assert gn[b] == oracle.compose(o_ids, fl)[1]
+    # the planning selection takes the same paths: same ids and lengths
+    mb = 40
+    bt = torch.arange(B * mb, dtype=torch.int32, device="cuda").reshape(B, mb)
+    sp = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    plan = fs.new_inject_plan(st, B)
+    ids2 = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    nt2 = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    fs.fs_retrieve_plan(st, B, torch.from_numpy(users).cuda(), torch.from_numpy(q).cuda(), k, ids2, bt, mb, sp,
+                        B * mb, plan, num_tokens=nt2)
+    assert fs.fs_poll_errors(st) == 0
+    assert torch.equal(ids2, ids) and torch.equal(nt2, nt)
+    st.close()
+
+
 def test_retrieval_bad_user_sets_error():
     rng = np.random.default_rng(6)
     emb = rng.standard_normal((10, 16)).astype(np.float32)
