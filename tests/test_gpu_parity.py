@@ -444,7 +444,8 @@ def _random_shape(case: int):
 def test_random_layouts(case):
     """Seeded random shapes (k may exceed a user's fact count), both layers
     compared row by row with the oracle and every other byte with the
-    sentinel."""
+    sentinel; the planning path (fs_retrieve_plan + fs_inject_planned) must
+    then write the same bytes."""
     shape = _random_shape(case)
     wl = synth.make_workload(shape, seed=9100 + case)
     say(f"random layout {case}: H={shape.num_kv_heads} D={shape.head_dim} bs={shape.block_size} "
@@ -454,6 +455,21 @@ def test_random_layouts(case):
     o = check_retrieval(wl, _host(ids), _host(scores), _host(ntok), range(shape.batch), wl.k)
     check_injection(wl, ds, kc, vc, o, [0, 1])
     check_sentinel(kc, vc, written_mask(wl, o, kc[0].shape[0]), [0, 1])
+    # the planning path (the top-k block writes the plan, the row kernel
+    # streams from it) must write the same bytes and select the same ids
+    B, k, nb = shape.batch, wl.k, kc[0].shape[0]
+    kc2, vc2 = synth.make_caches(wl, [0, 1], "cuda")
+    ids2 = torch.full_like(ids, -7)
+    nt2 = torch.full_like(ntok, -7)
+    plan = fs.new_inject_plan(ds.store, B)
+    fs.fs_retrieve_plan(ds.store, B, req["user"], req["query"], k, ids2, req["block_table"],
+                        wl.block_table.shape[1], req["start_pos"], nb, plan, num_tokens=nt2)
+    fs.fs_inject_planned(ds.store, fs.FS_ALL_LAYERS, B, k, plan, fs.CacheTable(ds.store, kc2, vc2, nb))
+    assert fs.fs_poll_errors(ds.store) == 0
+    assert torch.equal(ids2, ids) and torch.equal(nt2, ntok)
+    for l in range(2):
+        assert torch.equal(kc2[l].view(torch.int16), kc[l].view(torch.int16)), f"planning path K layer {l}"
+        assert torch.equal(vc2[l].view(torch.int16), vc[l].view(torch.int16)), f"planning path V layer {l}"
     ds.close()
 
 
