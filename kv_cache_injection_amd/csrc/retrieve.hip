@@ -635,11 +635,22 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
         const bool pre_len = !mapped && a.fact_len;
         const bool pre_row = pre_len && planning;
         const int tail0 = tid + kKeep * kTopkThreads;
+        {
+            // unpredicated, unbranched loads (the index clamped into the
+            // user's range, n >= 1 here; with no lengths to fetch, a harmless
+            // read of the request's first score instead): in straight-line
+            // code the scores' wait below counts past these loads instead of
+            // waiting for them too
+            const int64_t last = base + n - 1;
+            const int32_t* len_at = pre_len ? a.fact_len : reinterpret_cast<const int32_t*>(sc);
+            const int64_t* row_at = pre_row ? a.fact_begin : reinterpret_cast<const int64_t*>(sc);
 #pragma unroll
-        for (int j = 0; j < kKeep; ++j) {
-            const int i = tid + j * kTopkThreads;
-            lv[j] = pre_len && i < n ? a.fact_len[base + i] : 0;
-            rv[j] = pre_row && i < n ? a.fact_begin[base + i] : 0;
+            for (int j = 0; j < kKeep; ++j) {
+                const int64_t f = min(base + tid + j * kTopkThreads, last);
+                lv[j] = len_at[pre_len ? f : 0];
+                if (kPlan) rv[j] = row_at[pre_row ? f : 0];
+                else rv[j] = 0;
+            }
         }
         double lo = __builtin_huge_val(), hi = -__builtin_huge_val();
         int bad = 0;
@@ -648,9 +659,17 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
             lo = fmin(lo, x);
             hi = fmax(hi, x);
         };
+        // the kept scores by selects, not branches: in straight-line code
+        // the wait for each score counts past the length loads issued after
+        // it, instead of waiting for every load in flight
 #pragma unroll
-        for (int j = 0; j < kKeep; ++j)
-            if (tid + j * kTopkThreads < n) see(xv[j]);
+        for (int j = 0; j < kKeep; ++j) {
+            const bool in = tid + j * kTopkThreads < n;
+            const double x = xv[j];
+            bad |= (in && !(fabs(x) < __builtin_huge_val())) ? 1 : 0;
+            lo = fmin(lo, in ? x : __builtin_huge_val());
+            hi = fmax(hi, in ? x : -__builtin_huge_val());
+        }
         for (int i = tail0; i < n; i += kTopkThreads) see(sc[i]);
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) {
@@ -756,14 +775,35 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
                     __syncthreads();
                     int at = 0;
                     for (int w = 0; w < wave; ++w) at += s_wn[w];
+                    if (pre_len && !mapped) {
+                        // the usual request: ids are score indices and the
+                        // lengths and rows are in registers, so each
+                        // candidate is a few LDS writes (the general writer
+                        // below carries the loads of the other cases, and its
+                        // instructions, run for every kept slot, cost the
+                        // phase a microsecond)
 #pragma unroll
-                    for (int j = 0; j < kKeep; ++j) {
-                        if ((cm[j] >> lane) & 1ull) {
-                            const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(cm[j] >> 32),
-                                                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(cm[j]), 0));
-                            put(at + below, xv[j], tid + j * kTopkThreads, pre_len ? lv[j] : -1, rv[j]);
+                        for (int j = 0; j < kKeep; ++j) {
+                            if ((cm[j] >> lane) & 1ull) {
+                                const int slot = at + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(cm[j] >> 32),
+                                                                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(cm[j]), 0));
+                                s_ck[slot] = order_key(xv[j]);
+                                s_ci[slot] = tid + j * kTopkThreads;
+                                s_cl[slot] = lv[j];
+                                if (planning) s_cr[slot] = rv[j];   // slot < 64: at most 64 candidates
+                            }
+                            at += __popcll(cm[j]);
                         }
-                        at += __popcll(cm[j]);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < kKeep; ++j) {
+                            if ((cm[j] >> lane) & 1ull) {
+                                const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(cm[j] >> 32),
+                                                                            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(cm[j]), 0));
+                                put(at + below, xv[j], tid + j * kTopkThreads, pre_len ? lv[j] : -1, rv[j]);
+                            }
+                            at += __popcll(cm[j]);
+                        }
                     }
                 } else {
 #pragma unroll
