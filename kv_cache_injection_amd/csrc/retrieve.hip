@@ -602,9 +602,9 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
         plan_bad_user = mapped ? (pu < 0 || pu >= a.num_users) : bad_user;
     }
 
-    if (bad_user && tid == 0 && cidx == 0) atomicOr(a.err, FS_ERR_USER);
+    if (__builtin_expect(bad_user, 0) && tid == 0 && cidx == 0) atomicOr(a.err, FS_ERR_USER);
     if (chunked && kk == 0) return;
-    if (kk == 0) {
+    if (__builtin_expect(kk == 0, 0)) {
         for (int j = tid; j < k; j += blockDim.x) {
             a.ids[int64_t(b) * k + j] = -1;
             if (a.out_scores) a.out_scores[int64_t(b) * k + j] = -__builtin_huge_val();
@@ -704,7 +704,7 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
         }
         const double range = hi - lo;
         const double scale = (kBins - 0.5) / range;
-        if (!bad && range == 0.0 && !mapped) {
+        if (__builtin_expect(!bad && range == 0.0 && !mapped, 0)) {
             // every score is equal: the lowest kk indices win, in order
             for (int j = tid; j < kk; j += blockDim.x) {
                 cand_key[j] = order_key(lo);
@@ -713,7 +713,7 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
             __syncthreads();
             goto outputs;
         }
-        if (!bad && range < __builtin_huge_val() && scale < __builtin_huge_val()) {
+        if (__builtin_expect(!bad && range < __builtin_huge_val() && scale < __builtin_huge_val(), 1)) {
 #pragma unroll
             for (int j = 0; j < kKeep; ++j)
                 if (tid + j * kTopkThreads < n) atomicAdd(&s_bin[value_bin(xv[j], lo, scale)], 1);
@@ -749,7 +749,7 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
             }
             __syncthreads();
             const int t = s_t, C = s_C;
-            if (C <= kCandMax) {
+            if (__builtin_expect(C <= kCandMax, 1)) {
                 // len < 0: the length (and, planning, the first row) is loaded here
                 auto put = [&](int slot, double x, int i, int32_t len, int64_t r0) {
                     const int32_t id = cand_id(i);
@@ -758,7 +758,7 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
                     s_cl[slot] = len >= 0 ? len : (a.fact_len ? a.fact_len[base + id] : 0);
                     if (planning && slot < 64) s_cr[slot] = len >= 0 ? r0 : a.fact_begin[base + id];
                 };
-                if (C <= 64 && n <= kKeep * kTopkThreads) {
+                if (__builtin_expect(C <= 64 && n <= kKeep * kTopkThreads, 1)) {
                     // few candidates, every score in registers: each wave
                     // counts its candidates by ballot, and after one barrier
                     // writes them at its offset in index order (no LDS
@@ -775,7 +775,7 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
                     __syncthreads();
                     int at = 0;
                     for (int w = 0; w < wave; ++w) at += s_wn[w];
-                    if (pre_len && !mapped) {
+                    if (__builtin_expect(pre_len && !mapped, 1)) {
                         // the usual request: ids are score indices and the
                         // lengths and rows are in registers, so each
                         // candidate is a few LDS writes (the general writer
@@ -816,7 +816,7 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
                     }
                 }
                 __syncthreads();
-                if (C <= 64) {
+                if (__builtin_expect(C <= 64, 1)) {
                     // one wave sorts the candidates in registers (bitonic,
                     // best first): a lane per candidate, the padding lanes
                     // worse than any candidate
@@ -887,7 +887,7 @@ __global__ __launch_bounds__(kT) void fs_topk_kernel(TopkArgs a) {
         }
     }
 
-    if (mapped) {
+    if (__builtin_expect(mapped, 0)) {
         // exact fallback for candidate mode: the r-th winner is the best
         // candidate worse than the (r-1)-th on (score desc, fact id asc)
         __shared__ uint64_t s_rk[kTopkWaves];
