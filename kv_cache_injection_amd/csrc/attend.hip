@@ -429,6 +429,9 @@ __global__ __launch_bounds__(kThreads, 2) void fs_attend_kernel(AttendArgs a) {
         // is 0), so the wave skips it; so do waves without a real query
         if (wave_live && tbase <= wave_last) {
             // S^T for 4 sub-tiles of 16 positions: st[hs][sub][i] = S[jq][tbase + 16*sub + 4*grp + i]
+            // the compiler's own interleave of matrix instructions with LDS
+            // reads: 1-3% faster on every shape measured
+            __builtin_amdgcn_iglp_opt(1);
             f4 st[kHS][4];
 #pragma unroll
             for (int sub = 0; sub < 4; ++sub) {
